@@ -1,0 +1,191 @@
+/*
+ * lq.h -- C ABI of liblq.so: windowed INT8 recurrent-state decode for Gated
+ * DeltaNet (scalar gate) and Kimi Delta Attention (per-key-channel gate) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  The arXiv 2609.38166 abstract ("LeapQuant: Efficient
+ * Linear Attention with Accurate Recurrent State Quantization", section
+ * "Abstract (arXiv)" of the mlsanity.com paper page) describes per-window
+ * quantization of the linear-attention recurrent state: the state is stored
+ * in 8 bits and quantized only once at the end of a window of tokens; inside
+ * the window each output comes from the fixed low-bit state plus
+ * high-precision buffered updates; at quantization time the largest outlier
+ * rows and columns are kept as a few high-precision Compensator Tokens that
+ * share the real tokens' update path, and the residual is smoothed before
+ * quantization.  The bedrocknews.com review of the paper adds that the state
+ * goes from FP32 to INT8 and the compensators are kept in FP16/FP32.
+ *
+ * The recurrence (the pages name it but print no equation; this is the gated
+ * delta rule of the cited Gated DeltaNet / Kimi Linear works): per unit
+ * (one sequence x one value head) a d_v x d_k state S,
+ *     S_t = S_{t-1} Diag(g_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ * with g_t = alpha_t (one scalar per unit, gate_kind LQ_GATE_SCALAR) or
+ * g_t = a_t in (0,1]^{d_k} (gate_kind LQ_GATE_CHANNEL).  Quantizer (readings,
+ * the pages give no formula): line scores are squared L2 norms; the n_comp
+ * highest-scoring rows/columns become fp32 compensator lines; the residual R
+ * gets s_j = sqrt(max_i |R_ij|) per key channel and sigma_i =
+ * max_j |R_ij / s_j| / 127 per row; codes = clamp(rne(R_ij/(sigma_i s_j)),
+ * -127, 127).
+ *
+ * Conventions for every call:
+ *  - pointers named in a call are DEVICE pointers the caller owns (for
+ *    example torch tensors); `cfg`, `bytes`, `layout` and `flags` are host
+ *    pointers;
+ *  - `stream` is a hipStream_t (NULL = the default stream); every call except
+ *    lq_read_status is asynchronous on it, launches nothing when it returns
+ *    an error, and never allocates device memory; the library holds no
+ *    global mutable state, so distinct state blobs may be used concurrently;
+ *    calls on one blob must be ordered on one stream;
+ *  - device pointers must be 16-byte aligned, the state blob 256-byte
+ *    aligned (LQ_EINVAL otherwise);
+ *  - errors found on the device (a decode step on a full window, a
+ *    non-finite input) never abort: they set sticky flags in the blob, read
+ *    with lq_read_status.
+ *
+ * Layouts (row-major, fp32 unless noted; unit u = s * n_v_heads + h; value
+ * head h reads key head h / (n_v_heads / n_k_heads)):
+ *   q, k    [n_seq][n_k_heads][d_k]      v, o   [n_seq][n_v_heads][d_v]
+ *   beta    [n_seq][n_v_heads]           gate   [n_seq][n_v_heads] (scalar)
+ *                                               [n_seq][n_v_heads][d_k] (channel)
+ *   S0, S_out, S (fp32 state)            [n_seq][n_v_heads][d_v][d_k]
+ * q and k are used as given: the caller L2-normalizes them and folds any
+ * 1/sqrt(d_k) into q.
+ */
+#ifndef LQ_H
+#define LQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define LQ_OK 0
+#define LQ_EINVAL (-1)       /* NULL where not allowed, misaligned pointer, inconsistent sizes */
+#define LQ_EUNSUPPORTED (-2) /* a configuration outside the supported set below */
+#define LQ_EHIP (-3)         /* the HIP runtime reported an error (launch or copy) */
+
+/* gate kinds */
+#define LQ_GATE_SCALAR 0  /* Gated DeltaNet: one alpha per unit and token */
+#define LQ_GATE_CHANNEL 1 /* Kimi Delta Attention: one gate per key channel */
+
+/* sticky device flags (lq_read_status) */
+#define LQ_DEV_WINDOW_OVERFLOW 0x1u /* lq_decode_step found a full window: that unit's o is NaN, nothing appended */
+#define LQ_DEV_NONFINITE_INPUT 0x2u /* a decode input (q, k, v, beta, gate) was NaN or Inf */
+
+/*
+ * Problem description.  Supported: d_k == d_v in {64, 128};
+ * 1 <= window <= 128; 0 <= n_comp <= 16; n_seq, n_v_heads, n_k_heads >= 1;
+ * n_v_heads % n_k_heads == 0; gate_kind in {LQ_GATE_SCALAR, LQ_GATE_CHANNEL};
+ * the unit count n_seq * n_v_heads below 2^31.
+ */
+typedef struct lq_config {
+    int32_t n_seq;
+    int32_t n_v_heads;
+    int32_t n_k_heads;
+    int32_t d_k;
+    int32_t d_v;
+    int32_t window;   /* W: tokens per quantization window */
+    int32_t n_comp;   /* compensator lines kept per unit */
+    int32_t gate_kind;
+} lq_config;
+
+/*
+ * Byte offsets of the sections of the state blob (each 256-byte aligned).
+ * The blob is self-contained: copying it (with the lq_config) checkpoints
+ * the whole decode state.
+ *   status    uint32 sticky flags
+ *   fill      int32 [units]            tokens buffered in the current window
+ *   codes     int8  [units][d_v][d_k]  the INT8 state
+ *   sigma     fp32  [units][d_v]       per-row scales
+ *   smooth    fp32  [units][d_k]       per-key-channel smoothing factors
+ *   comp_idx  int32 [units][n_comp]    c < d_v: row c; c >= d_v: column c - d_v
+ *   comp_vec  fp32  [units][n_comp][max(d_k,d_v)]  row slot: the row (d_k);
+ *                                      column slot: the column (d_v)
+ *   buf_k     fp32  [n_seq][n_k_heads][window][d_k]  (shared by a key head's value heads)
+ *   buf_v     fp32  [units][window][d_v]
+ *   buf_beta  fp32  [units][window]
+ *   buf_gate  fp32  [units][window] (scalar) or [units][window][d_k] (channel)
+ */
+typedef struct lq_layout {
+    size_t total_bytes;
+    size_t status, fill, codes, sigma, smooth, comp_idx, comp_vec;
+    size_t buf_k, buf_v, buf_beta, buf_gate;
+} lq_layout;
+
+/* Size in bytes of the state blob for cfg.  Host only, no HIP call. */
+int32_t lq_state_bytes(const lq_config* cfg, size_t* bytes);
+
+/* Section offsets of the blob for cfg.  Host only, no HIP call. */
+int32_t lq_state_layout(const lq_config* cfg, lq_layout* layout);
+
+/*
+ * Quantize a start state into the blob: compensators, smoothing, scales and
+ * codes of S0 (the abstract's window-end quantization with an empty window),
+ * fill = 0, status = 0.  S0 may be NULL for the zero state.  Buffers are left
+ * as they are (never read while fill = 0).
+ */
+int32_t lq_state_init(const lq_config* cfg, void* state, const float* S0, void* stream);
+
+/*
+ * One decode token for every sequence.  Per unit: append (k, v, beta, gate)
+ * to the window buffer, then write o = S_j q where S_j is the stored
+ * window-start state advanced through the buffered tokens (the current one
+ * included): the abstract's "outputs from the fixed low-bit state together
+ * with high-precision buffered updates".  The INT8 codes, scales, smoothing
+ * and compensators are read, never written.  A unit whose window is already
+ * full (lq_window_flush was not called) gets o = NaN and sets
+ * LQ_DEV_WINDOW_OVERFLOW.
+ */
+int32_t lq_decode_step(const lq_config* cfg, void* state, const float* q, const float* k,
+                       const float* v, const float* beta, const float* gate, float* o,
+                       void* stream);
+
+/*
+ * Window-boundary requantization.  Every unit whose window is full
+ * (fill == window), and every unit of a sequence s with force_mask[s] != 0
+ * and fill > 0, is advanced through its buffered tokens in FP64, gets new
+ * compensators, smoothing, scales and codes, and fill = 0.  Other units are
+ * untouched.  force_mask: device uint8 [n_seq], or NULL.  Must be called
+ * between the decode step that fills a window and the next decode step.
+ */
+int32_t lq_window_flush(const lq_config* cfg, void* state, const uint8_t* force_mask,
+                        void* stream);
+
+/*
+ * Dequantized state into S_out (fp32): the window-start state
+ * Diag(sigma) Q Diag(s) + compensator lines, or, with include_buffer != 0,
+ * that state advanced through the buffered tokens (the state after the last
+ * decode step).  For inspection and checkpoint conversion.
+ */
+int32_t lq_dequant_state(const lq_config* cfg, const void* state, float* S_out,
+                         int32_t include_buffer, void* stream);
+
+/*
+ * The FP32-state comparison step: S (fp32, in place) advanced by one token
+ * and o = S_t q, with the same inputs and layouts as lq_decode_step.  This is
+ * the FP32 baseline the pages measure against (bedrocknews.com review: the
+ * baseline is FP32 inference of the same models).
+ */
+int32_t lq_fp32_decode_step(const lq_config* cfg, float* S, const float* q, const float* k,
+                            const float* v, const float* beta, const float* gate, float* o,
+                            void* stream);
+
+/*
+ * Synchronizes `stream`, then returns the blob's sticky flags in *flags.
+ * clear != 0 resets them to 0 afterwards (ordered on the stream).
+ */
+int32_t lq_read_status(const lq_config* cfg, void* state, uint32_t* flags, int32_t clear,
+                       void* stream);
+
+/* Static description of a return code. */
+const char* lq_strerror(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LQ_H */

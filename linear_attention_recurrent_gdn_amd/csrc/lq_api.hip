@@ -1,0 +1,182 @@
+// lq_api.hip -- the extern "C" entry points of liblq.so: argument checks,
+// blob layout, kernel launches.  Every check runs on the host before any HIP
+// call, so a rejected call launches nothing (and needs no GPU).
+
+#include <hip/hip_runtime.h>
+
+#include "lq_internal.h"
+
+using namespace lq;
+
+namespace {
+
+int32_t check_config(const lq_config* c) {
+    if (c == nullptr) return LQ_EINVAL;
+    if (c->n_seq < 1 || c->n_v_heads < 1 || c->n_k_heads < 1 || c->d_k < 1 || c->d_v < 1 ||
+        c->window < 1 || c->n_comp < 0)
+        return LQ_EINVAL;
+    if (c->n_v_heads % c->n_k_heads != 0) return LQ_EINVAL;
+    if (c->gate_kind != LQ_GATE_SCALAR && c->gate_kind != LQ_GATE_CHANNEL) return LQ_EINVAL;
+    if ((int64_t)c->n_seq * c->n_v_heads >= ((int64_t)1 << 31)) return LQ_EUNSUPPORTED;
+    if (c->d_k != c->d_v || (c->d_k != 64 && c->d_k != 128)) return LQ_EUNSUPPORTED;
+    if (c->window > 128 || c->n_comp > 16) return LQ_EUNSUPPORTED;
+    return LQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+Dims dims_of(const lq_config* c) {
+    Dims d;
+    d.n_units = c->n_seq * c->n_v_heads;
+    d.n_v_heads = c->n_v_heads;
+    d.n_k_heads = c->n_k_heads;
+    d.group = c->n_v_heads / c->n_k_heads;
+    d.window = c->window;
+    d.n_comp = c->n_comp;
+    return d;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? LQ_OK : LQ_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t lq_state_bytes(const lq_config* cfg, size_t* bytes) {
+    int32_t rc = check_config(cfg);
+    if (rc != LQ_OK) return rc;
+    if (bytes == nullptr) return LQ_EINVAL;
+    lq_layout L;
+    compute_layout(*cfg, L);
+    *bytes = L.total_bytes;
+    return LQ_OK;
+}
+
+int32_t lq_state_layout(const lq_config* cfg, lq_layout* layout) {
+    int32_t rc = check_config(cfg);
+    if (rc != LQ_OK) return rc;
+    if (layout == nullptr) return LQ_EINVAL;
+    compute_layout(*cfg, *layout);
+    return LQ_OK;
+}
+
+int32_t lq_state_init(const lq_config* cfg, void* state, const float* S0, void* stream) {
+    int32_t rc = check_config(cfg);
+    if (rc != LQ_OK) return rc;
+    if (state == nullptr || !aligned(state, kSectionAlign)) return LQ_EINVAL;
+    if (S0 != nullptr && !aligned(S0, 16)) return LQ_EINVAL;
+    lq_layout L;
+    compute_layout(*cfg, L);
+    MatArgs a{};
+    a.blob = blob_ptrs(state, L);
+    a.dm = dims_of(cfg);
+    a.S0 = S0;
+    return hip_status(launch_materialize(a, kModeInit, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+}
+
+int32_t lq_decode_step(const lq_config* cfg, void* state, const float* q, const float* k,
+                       const float* v, const float* beta, const float* gate, float* o,
+                       void* stream) {
+    int32_t rc = check_config(cfg);
+    if (rc != LQ_OK) return rc;
+    if (state == nullptr || q == nullptr || k == nullptr || v == nullptr || beta == nullptr ||
+        gate == nullptr || o == nullptr)
+        return LQ_EINVAL;
+    if (!aligned(state, kSectionAlign) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        !aligned(beta, 4) || !aligned(gate, cfg->gate_kind == LQ_GATE_CHANNEL ? 16 : 4) ||
+        !aligned(o, 16))
+        return LQ_EINVAL;
+    lq_layout L;
+    compute_layout(*cfg, L);
+    DecodeArgs a{};
+    a.blob = blob_ptrs(state, L);
+    a.dm = dims_of(cfg);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.gate = gate;
+    a.o = o;
+    return hip_status(launch_decode_int8(a, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+}
+
+int32_t lq_window_flush(const lq_config* cfg, void* state, const uint8_t* force_mask,
+                        void* stream) {
+    int32_t rc = check_config(cfg);
+    if (rc != LQ_OK) return rc;
+    if (state == nullptr || !aligned(state, kSectionAlign)) return LQ_EINVAL;
+    lq_layout L;
+    compute_layout(*cfg, L);
+    MatArgs a{};
+    a.blob = blob_ptrs(state, L);
+    a.dm = dims_of(cfg);
+    a.force = force_mask;
+    return hip_status(launch_materialize(a, kModeFlush, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+}
+
+int32_t lq_dequant_state(const lq_config* cfg, const void* state, float* S_out,
+                         int32_t include_buffer, void* stream) {
+    int32_t rc = check_config(cfg);
+    if (rc != LQ_OK) return rc;
+    if (state == nullptr || S_out == nullptr || !aligned(state, kSectionAlign) || !aligned(S_out, 16))
+        return LQ_EINVAL;
+    lq_layout L;
+    compute_layout(*cfg, L);
+    MatArgs a{};
+    a.blob = blob_ptrs(const_cast<void*>(state), L);
+    a.dm = dims_of(cfg);
+    a.S_out = S_out;
+    a.include_buffer = include_buffer != 0;
+    return hip_status(launch_materialize(a, kModeDequant, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+}
+
+int32_t lq_fp32_decode_step(const lq_config* cfg, float* S, const float* q, const float* k,
+                            const float* v, const float* beta, const float* gate, float* o,
+                            void* stream) {
+    int32_t rc = check_config(cfg);
+    if (rc != LQ_OK) return rc;
+    if (S == nullptr || q == nullptr || k == nullptr || v == nullptr || beta == nullptr ||
+        gate == nullptr || o == nullptr)
+        return LQ_EINVAL;
+    if (!aligned(S, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(beta, 4) ||
+        !aligned(gate, cfg->gate_kind == LQ_GATE_CHANNEL ? 16 : 4) || !aligned(o, 4))
+        return LQ_EINVAL;
+    Fp32DecodeArgs a{};
+    a.dm = dims_of(cfg);
+    a.S = S;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.gate = gate;
+    a.o = o;
+    return hip_status(launch_decode_fp32(a, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+}
+
+int32_t lq_read_status(const lq_config* cfg, void* state, uint32_t* flags, int32_t clear,
+                       void* stream) {
+    int32_t rc = check_config(cfg);
+    if (rc != LQ_OK) return rc;
+    if (state == nullptr || flags == nullptr || !aligned(state, kSectionAlign)) return LQ_EINVAL;
+    lq_layout L;
+    compute_layout(*cfg, L);
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t* dev = (uint32_t*)((char*)state + L.status);
+    if (hipMemcpyAsync(flags, dev, sizeof(uint32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+        return LQ_EHIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return LQ_EHIP;
+    if (clear) return hip_status(launch_clear_status(dev, st));
+    return LQ_OK;
+}
+
+const char* lq_strerror(int32_t code) {
+    switch (code) {
+        case LQ_OK: return "ok";
+        case LQ_EINVAL: return "invalid argument (null or misaligned pointer, or inconsistent sizes)";
+        case LQ_EUNSUPPORTED: return "unsupported configuration";
+        case LQ_EHIP: return "HIP runtime error";
+        default: return "unknown lq status code";
+    }
+}
+
+}  // extern "C"

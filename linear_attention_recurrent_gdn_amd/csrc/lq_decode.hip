@@ -1,0 +1,361 @@
+// lq_decode.hip -- per-token decode kernels for gfx950.
+//
+// decode_int8_kernel: one token of the windowed INT8 scheme.  The arXiv
+// 2609.38166 abstract ("Abstract (arXiv)" section, mlsanity.com paper page):
+// within a window, outputs are computed from the fixed low-bit state together
+// with high-precision buffered updates.  The bedrocknews.com review: the cost
+// is recomputing the buffered tokens' contributions, traded for far less
+// state traffic.  Per unit (sequence x value head), with the window-start
+// state S_hat = Diag(sigma) Q Diag(s) + sum_c v_c k_c^T and buffered tokens
+// 1..n (the current token is n):
+//     r = q;  acc = 0
+//     for i = n..1:  c = k_i . r;  acc += beta_i c v_i;  r = g_i * (r - beta_i c k_i)
+//     o = sigma * (Q (s * r)) + sum_c v_c (k_c . r) + acc
+// so r = A_1..A_n q and acc = sum_i beta_i v_i k_i^T A_{i+1}..A_n q, and o is
+// S_n q.  The INT8 tile, sigma, s and compensators are only read.
+//
+// Mapping: one wavefront per unit, four units per workgroup.  The 16 KiB
+// (d = 128) INT8 tile is requested with 16-byte coalesced loads before the
+// reverse pass so its latency hides behind the sequential chain; the chain's
+// d-length dot products reduce with DPP; buffer entries are loaded a batch
+// ahead of their use.  The tile product reads s*r from LDS, each lane
+// covering 16 columns of 16 rows, and reduces each row over 8 lanes with DPP.
+// The kernel is HBM-bound (about one flop per byte): no MFMA.
+//
+// decode_fp32_kernel: the FP32-state step the pages compare against (the
+// bedrocknews.com review: the baseline is FP32 inference).  The row form
+// x = g * S[i,:];  S[i,:] = x + beta (v_i - x.k) k;  o_i = x.q + beta (v_i - x.k)(k.q)
+// reads and writes each 512-byte row once.
+
+#include "lq_internal.h"
+
+namespace lq {
+
+namespace {
+
+template <int EPL>
+struct Vec {
+    float e[EPL];
+};
+
+template <int EPL>
+__device__ __forceinline__ Vec<EPL> load_vec(const float* p) {
+    Vec<EPL> r;
+    if constexpr (EPL == 2) {
+        float2 t = *reinterpret_cast<const float2*>(p);
+        r.e[0] = t.x;
+        r.e[1] = t.y;
+    } else {
+        r.e[0] = p[0];
+    }
+    return r;
+}
+
+template <int EPL>
+__device__ __forceinline__ void store_vec(float* p, const Vec<EPL>& v) {
+    if constexpr (EPL == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(v.e[0], v.e[1]);
+    } else {
+        p[0] = v.e[0];
+    }
+}
+
+__device__ __forceinline__ bool finite(float x) { return __builtin_isfinite(x); }
+
+// One buffered token as held in registers during the reverse pass.
+template <int EPL, int GE>
+struct Entry {
+    Vec<EPL> k, v;
+    Vec<GE> g;
+    float beta;
+};
+
+}  // namespace
+
+template <int D, bool KDA>
+__global__ __launch_bounds__(256) void decode_int8_kernel(DecodeArgs a) {
+    constexpr int EPL = D / kWave;   // state elements per lane along d
+    constexpr int GE = KDA ? EPL : 1;
+    constexpr int LPR = D / 16;      // lanes per code row (16 codes per 16-byte load)
+    constexpr int RPL = kWave / LPR; // code rows per wave-wide load
+    constexpr int NL = D / RPL;      // 16-byte loads per lane for the whole tile
+    constexpr int B = 4;             // buffer entries per prefetch batch
+
+    __shared__ float lds_x[4][D];
+    __shared__ float lds_o[4][D];
+
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int u = blockIdx.x * 4 + wave;
+    if (u >= a.dm.n_units) return;
+
+    const int W = a.dm.window;
+    const int nc = a.dm.n_comp;
+    const int s = u / a.dm.n_v_heads;
+    const int h = u - s * a.dm.n_v_heads;
+    const int kh = h / a.dm.group;
+    const size_t kvec = ((size_t)s * a.dm.n_k_heads + kh);  // key-head row of q, k
+
+    const int j = a.blob.fill[u];  // tokens already in the window
+    float* o = a.o + (size_t)u * D + lane * EPL;
+    if (j >= W) {
+        Vec<EPL> nanv;
+        for (int e = 0; e < EPL; ++e) nanv.e[e] = __builtin_nanf("");
+        store_vec(o, nanv);
+        if (lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_WINDOW_OVERFLOW);
+        return;
+    }
+
+    // ---- request the INT8 tile first: its latency overlaps the reverse pass
+    const uint4* tile = reinterpret_cast<const uint4*>(a.blob.codes + (size_t)u * D * D);
+    uint4 tw[NL];
+#pragma unroll
+    for (int t = 0; t < NL; ++t) tw[t] = tile[t * kWave + lane];
+    const Vec<EPL> sm = load_vec<EPL>(a.blob.smooth + (size_t)u * D + lane * EPL);
+    const Vec<EPL> sg = load_vec<EPL>(a.blob.sigma + (size_t)u * D + lane * EPL);
+
+    // ---- current token: read, check, append to the window buffer
+    const Vec<EPL> qv = load_vec<EPL>(a.q + kvec * D + lane * EPL);
+    Entry<EPL, GE> cur;
+    cur.k = load_vec<EPL>(a.k + kvec * D + lane * EPL);
+    cur.v = load_vec<EPL>(a.v + (size_t)u * D + lane * EPL);
+    cur.beta = a.beta[u];
+    if constexpr (KDA) {
+        cur.g = load_vec<GE>(a.gate + (size_t)u * D + lane * EPL);
+    } else {
+        cur.g.e[0] = a.gate[u];
+    }
+    bool ok = finite(cur.beta);
+    for (int e = 0; e < EPL; ++e) ok = ok && finite(qv.e[e]) && finite(cur.k.e[e]) && finite(cur.v.e[e]);
+    for (int e = 0; e < GE; ++e) ok = ok && finite(cur.g.e[e]);
+    if (__any(!ok) && lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_NONFINITE_INPUT);
+
+    float* bk = a.blob.buf_k + kvec * (size_t)W * D;
+    float* bv = a.blob.buf_v + (size_t)u * W * D;
+    float* bb = a.blob.buf_beta + (size_t)u * W;
+    float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
+    if (h % a.dm.group == 0) store_vec(bk + (size_t)j * D + lane * EPL, cur.k);
+    store_vec(bv + (size_t)j * D + lane * EPL, cur.v);
+    if constexpr (KDA) {
+        store_vec(bg + (size_t)j * D + lane * EPL, cur.g);
+    } else {
+        if (lane == 0) bg[j] = cur.g.e[0];
+    }
+    if (lane == 0) bb[j] = cur.beta;
+
+    // ---- reverse pass over the window: newest token first
+    Vec<EPL> r = qv;
+    Vec<EPL> acc;
+    for (int e = 0; e < EPL; ++e) acc.e[e] = 0.f;
+
+    auto step = [&](const Entry<EPL, GE>& en) {
+        float p = 0.f;
+        for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(en.k.e[e], r.e[e], p);
+        const float c = wave_sum(p);
+        const float bc = en.beta * c;
+        for (int e = 0; e < EPL; ++e) {
+            acc.e[e] = __builtin_fmaf(bc, en.v.e[e], acc.e[e]);
+            const float ge = KDA ? en.g.e[e] : en.g.e[0];
+            r.e[e] = ge * __builtin_fmaf(-bc, en.k.e[e], r.e[e]);
+        }
+    };
+    auto load_entry = [&](int i, Entry<EPL, GE>& en) {
+        en.k = load_vec<EPL>(bk + (size_t)i * D + lane * EPL);
+        en.v = load_vec<EPL>(bv + (size_t)i * D + lane * EPL);
+        en.beta = bb[i];
+        if constexpr (KDA) {
+            en.g = load_vec<GE>(bg + (size_t)i * D + lane * EPL);
+        } else {
+            en.g.e[0] = bg[i];
+        }
+    };
+
+    Entry<EPL, GE> ba[B], bn[B];
+    int i = j - 1;
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+        if (i - b >= 0) load_entry(i - b, ba[b]);
+    step(cur);
+    while (i >= 0) {
+        const int inext = i - B;
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+            if (inext - b >= 0) load_entry(inext - b, bn[b]);
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+            if (i - b >= 0) step(ba[b]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) ba[b] = bn[b];
+        i = inext;
+    }
+
+    // ---- compensator tokens: rows add (k_c . r) at their row, columns add v_c r[col]
+    Vec<EPL> rowadd;
+    for (int e = 0; e < EPL; ++e) rowadd.e[e] = 0.f;
+    for (int c = 0; c < nc; ++c) {
+        const int idx = a.blob.comp_idx[(size_t)u * nc + c];
+        const Vec<EPL> w = load_vec<EPL>(a.blob.comp_vec + ((size_t)u * nc + c) * D + lane * EPL);
+        if (idx < D) {
+            float p = 0.f;
+            for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(w.e[e], r.e[e], p);
+            const float dot = wave_sum(p);
+            for (int e = 0; e < EPL; ++e)
+                if (lane * EPL + e == idx) rowadd.e[e] += dot;
+        } else {
+            const int col = idx - D;
+            float rsel = r.e[0];
+            if constexpr (EPL == 2) rsel = (col & 1) ? r.e[1] : r.e[0];
+            const float rc = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsel), col / EPL));
+            for (int e = 0; e < EPL; ++e) acc.e[e] = __builtin_fmaf(w.e[e], rc, acc.e[e]);
+        }
+    }
+
+    // ---- INT8 tile times (s * r)
+    for (int e = 0; e < EPL; ++e) lds_x[wave][lane * EPL + e] = sm.e[e] * r.e[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int cg = lane % LPR;  // this lane's 16-column group
+    float xs[16];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float4 x4 = *reinterpret_cast<const float4*>(&lds_x[wave][cg * 16 + 4 * t]);
+        xs[4 * t + 0] = x4.x;
+        xs[4 * t + 1] = x4.y;
+        xs[4 * t + 2] = x4.z;
+        xs[4 * t + 3] = x4.w;
+    }
+    float part[NL];
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+        const uint32_t wd[4] = {tw[t].x, tw[t].y, tw[t].z, tw[t].w};
+        float p = 0.f;
+#pragma unroll
+        for (int wi = 0; wi < 4; ++wi) {
+#pragma unroll
+            for (int by = 0; by < 4; ++by) {
+                const int code = (int)(wd[wi] << (24 - 8 * by)) >> 24;
+                p = __builtin_fmaf((float)code, xs[4 * wi + by], p);
+            }
+        }
+        if constexpr (LPR == 8) part[t] = sum8(p);
+        else part[t] = sum4(p);
+    }
+#pragma unroll
+    for (int t = 0; t < NL; ++t)
+        if (t % LPR == cg) lds_o[wave][t * RPL + lane / LPR] = part[t];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    Vec<EPL> out;
+    for (int e = 0; e < EPL; ++e)
+        out.e[e] = __builtin_fmaf(sg.e[e], lds_o[wave][lane * EPL + e], rowadd.e[e] + acc.e[e]);
+    store_vec(o, out);
+    if (lane == 0) a.blob.fill[u] = j + 1;
+}
+
+template <int D, bool KDA>
+__global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
+    constexpr int LPR = D / 8;        // lanes per state row, 8 floats per lane
+    constexpr int RPP = kWave / LPR;  // rows per wave pass
+    constexpr int ROWS = D / 4;       // rows per wave (four waves per unit)
+    constexpr int NP = ROWS / RPP;    // passes
+
+    const int u = blockIdx.x;
+    if (u >= a.dm.n_units) return;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int cg = lane % LPR;
+    const int rsub = lane / LPR;
+    const int s = u / a.dm.n_v_heads;
+    const int h = u - s * a.dm.n_v_heads;
+    const int kh = h / a.dm.group;
+    const size_t kvec = ((size_t)s * a.dm.n_k_heads + kh);
+
+    float* S = a.S + (size_t)u * D * D;
+    float4 sv[NP][2];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int row = wave * ROWS + p * RPP + rsub;
+        const float4* src = reinterpret_cast<const float4*>(S + (size_t)row * D + cg * 8);
+        sv[p][0] = src[0];
+        sv[p][1] = src[1];
+    }
+    auto ld8 = [&](const float* p, float (&x)[8]) {
+        float4 a0 = reinterpret_cast<const float4*>(p)[0];
+        float4 a1 = reinterpret_cast<const float4*>(p)[1];
+        x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
+        x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
+    };
+    float kk[8], qq[8], gg[8];
+    ld8(a.k + kvec * D + cg * 8, kk);
+    ld8(a.q + kvec * D + cg * 8, qq);
+    if constexpr (KDA) {
+        ld8(a.gate + (size_t)u * D + cg * 8, gg);
+    } else {
+        const float al = a.gate[u];
+        for (int e = 0; e < 8; ++e) gg[e] = al;
+    }
+    const float beta = a.beta[u];
+    float vrow[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) vrow[p] = a.v[(size_t)u * D + wave * ROWS + p * RPP + rsub];
+
+    float kq = 0.f;
+    for (int e = 0; e < 8; ++e) kq = __builtin_fmaf(kk[e], qq[e], kq);
+    kq = (LPR == 16) ? sum16(kq) : sum8(kq);
+
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int row = wave * ROWS + p * RPP + rsub;
+        float x[8] = {sv[p][0].x, sv[p][0].y, sv[p][0].z, sv[p][0].w,
+                      sv[p][1].x, sv[p][1].y, sv[p][1].z, sv[p][1].w};
+        float dk = 0.f, dq = 0.f;
+        for (int e = 0; e < 8; ++e) {
+            x[e] *= gg[e];
+            dk = __builtin_fmaf(x[e], kk[e], dk);
+            dq = __builtin_fmaf(x[e], qq[e], dq);
+        }
+        if constexpr (LPR == 16) {
+            dk = sum16(dk);
+            dq = sum16(dq);
+        } else {
+            dk = sum8(dk);
+            dq = sum8(dq);
+        }
+        const float c = beta * (vrow[p] - dk);
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(c, kk[e], x[e]);
+        float4* dst = reinterpret_cast<float4*>(S + (size_t)row * D + cg * 8);
+        dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+        dst[1] = make_float4(x[4], x[5], x[6], x[7]);
+        if (cg == 0) a.o[(size_t)u * D + row] = __builtin_fmaf(c, kq, dq);
+    }
+}
+
+hipError_t launch_decode_int8(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
+    const dim3 grid((a.dm.n_units + 3) / 4), block(256);
+    if (d == 128) {
+        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_int8_kernel<128, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_int8_kernel<128, false>), grid, block, 0, st, a);
+    } else {
+        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_int8_kernel<64, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_int8_kernel<64, false>), grid, block, 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_fp32(const Fp32DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
+    const dim3 grid(a.dm.n_units), block(256);
+    if (d == 128) {
+        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_fp32_kernel<128, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_fp32_kernel<128, false>), grid, block, 0, st, a);
+    } else {
+        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_fp32_kernel<64, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_fp32_kernel<64, false>), grid, block, 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lq

@@ -131,6 +131,70 @@ def tokens(wl: Workload, t0: int, n: int, phase: int = PHASE_DECODE, layer: int 
     return {key: np.stack([tk[key] for tk in toks]) for key in toks[0]} if toks else None
 
 
+def prefill_stream(wl: Workload, unit: int, layer: int = 0) -> Dict[str, np.ndarray]:
+    """Prefill tokens of one unit: k [P, d], v [P, d], beta [P], gate [P] or [P, d].
+
+    Keyed per unit (k per (sequence, key head), so the value heads of one key
+    head share it), so any subset of units can be generated on its own.
+    Prefill needs no queries (no outputs are read).
+    """
+    if wl.projected:
+        raise ValueError("projected workloads prefill through projected_token()")
+    P, d = wl.prefill, wl.d
+    s, h = divmod(unit, wl.n_v_heads)
+    key_id = s * wl.n_k_heads + h // wl.group
+    k = _l2_normalise(_rng(wl, layer, PHASE_PREFILL, key_id, "k").standard_normal((P, d), np.float32))
+    rv = _rng(wl, layer, PHASE_PREFILL, unit, "v")
+    v = (rv.standard_t(3, size=(P, d)).astype(np.float32) if wl.v_dist == "t3"
+         else rv.standard_normal((P, d), np.float32))
+    beta = _rng(wl, layer, PHASE_PREFILL, unit, "beta").uniform(0.0, 1.0, P).astype(np.float32)
+    gshape = (P,) if wl.gate == "scalar" else (P, d)
+    gate = _rng(wl, layer, PHASE_PREFILL, unit, "gate").uniform(wl.gate_lo, wl.gate_hi, gshape).astype(
+        np.float32)
+    return {"k": k, "v": v, "beta": beta, "gate": gate}
+
+
+def prefill_streams(wl: Workload, units, layer: int = 0) -> Dict[str, np.ndarray]:
+    """Token-major prefill inputs of several units: k [P, n, d], v [P, n, d], ..."""
+    per = [prefill_stream(wl, int(u), layer) for u in units]
+    return {key: np.ascontiguousarray(np.stack([p[key] for p in per], axis=1)) for key in per[0]}
+
+
+def surrogate_state(wl: Workload, units, layer: int = 0, scale: float = 0.5) -> np.ndarray:
+    """Gaussian stand-in start states [n, d, d] for units whose outputs are not checked."""
+    out = np.empty((len(units), wl.d, wl.d), np.float32)
+    for i, u in enumerate(units):
+        out[i] = _rng(wl, layer, PHASE_PREFILL, int(u), "hidden").standard_normal(
+            (wl.d, wl.d), np.float32) * np.float32(scale)
+    return out
+
+
+def torch_token(wl: Workload, gen, device, phase_scale: float = 1.0):
+    """One token of inputs drawn on the device with a torch Generator (same
+    distributions as ``token``; used where numpy generation would dominate)."""
+    import torch
+
+    S, H, KH, d = wl.n_seq, wl.n_v_heads, wl.n_k_heads, wl.d
+    f = torch.float32
+
+    def nrm(shape):
+        x = torch.randn(shape, generator=gen, device=device, dtype=f)
+        return x / x.norm(dim=-1, keepdim=True)
+
+    q, k = nrm((S, KH, d)), nrm((S, KH, d))
+    if wl.v_dist == "t3":
+        # Student-t(3) = N / sqrt(chi2_3 / 3)
+        z = torch.randn((S, H, d), generator=gen, device=device, dtype=f)
+        c = torch.randn((S, H, d, 3), generator=gen, device=device, dtype=f).pow(2).sum(-1)
+        v = z / torch.sqrt(c / 3.0)
+    else:
+        v = torch.randn((S, H, d), generator=gen, device=device, dtype=f)
+    beta = torch.rand((S, H), generator=gen, device=device, dtype=f)
+    gshape = (S, H) if wl.gate == "scalar" else (S, H, d)
+    gate = wl.gate_lo + (wl.gate_hi - wl.gate_lo) * torch.rand(gshape, generator=gen, device=device, dtype=f)
+    return {"q": q, "k": k, "v": v, "beta": beta, "gate": gate}
+
+
 def outlier_scale(wl: Workload, layer: int = 0):
     """Per-unit row and column multipliers for planting outlier lines.
 

@@ -1,0 +1,211 @@
+"""Teacher-forced comparison of the HIP path (through the C ABI) with the CPU
+oracle on one workload.
+
+Tolerances (the decode step's outputs are fp32; the oracle is fp64):
+  * outputs: relative L2 error of each decode call's outputs <= 1e-4;
+  * codes after each init / flush: identical, except 1-LSB differences where
+    the oracle's unrounded value lies within 2^-10 of a half-integer, in at
+    most 0.01% of that call's codes;
+  * compensator selection identical, unless the oracle's n_c-th and
+    (n_c+1)-th line scores are within 1e-6 relative (then the GPU's choice is
+    adopted and the oracle's quantizer re-run with it forced);
+  * compensator vectors <= 1e-4 relative L2; scales and smoothing <= 1e-6 relative;
+  * dequantized state (with and without the buffer) <= 1e-4 relative L2
+    against the oracle's dequantization of the GPU's own stored state.
+After each init and flush the oracle adopts the GPU's stored state, so a
+permitted code difference never compounds.
+
+Start states: the oracle runs the workload's prefill for every checked unit
+(fp64, rounded to fp32); units whose outputs are not checked (sampled runs at
+full size) get a seeded Gaussian stand-in so every launch still has the full
+shape.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+import linear_attention_recurrent_gdn_amd as lq
+import oracle as orc
+from linear_attention_recurrent_gdn_amd import inputs as I
+
+TOL_OUT = 1e-4
+TOL_STATE = 1e-4
+TOL_COMP = 1e-4
+TOL_SCALE = 1e-6
+TIE_TAU = 2.0 ** -10
+FLIP_BUDGET = 1e-4  # fraction of a call's codes
+AMBIG = 1e-6
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    n = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / n) if n > 0 else float(np.linalg.norm(a - b))
+
+
+def config_of(wl: I.Workload) -> lq.Config:
+    return lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, wl.d, wl.d, wl.window, wl.n_comp,
+                     wl.gate_kind)
+
+
+@dataclasses.dataclass
+class Report:
+    name: str
+    max_out_err: float = 0.0
+    max_state_err: float = 0.0
+    flushes: int = 0
+    codes_checked: int = 0
+    code_flips: int = 0
+    ambiguous_selections: int = 0
+    decode_calls: int = 0
+
+
+def start_states(wl: I.Workload, checked: np.ndarray, layer: int = 0) -> np.ndarray:
+    """fp32 [U, d, d]: oracle prefill for checked units, stand-ins elsewhere."""
+    U, d = wl.n_units, wl.d
+    S0 = np.zeros((U, d, d), np.float32)
+    others = np.setdiff1d(np.arange(U), checked)
+    if len(others):
+        S0[others] = I.surrogate_state(wl, others, layer)
+    if wl.prefill > 0 and len(checked):
+        st = I.prefill_streams(wl, checked, layer)
+        S, _ = orc.recurrence(np.zeros((len(checked), d, d)), None, st["k"], st["v"], st["beta"],
+                              st["gate"], want_outputs=False)
+        S0[checked] = S.astype(np.float32)
+    sc = I.outlier_scale(wl, layer)
+    if sc is not None:
+        r, c = sc
+        S0 = (S0 * r[:, :, None] * c[:, None, :]).astype(np.float32)
+    return S0
+
+
+def blob_host(views, units) -> orc.Blob:
+    idx = torch.as_tensor(np.asarray(units), device=views["codes"].device, dtype=torch.long)
+    g = lambda key: views[key].index_select(0, idx).cpu().numpy()
+    return orc.Blob(g("codes"), g("sigma"), g("smooth"), g("comp_idx"), g("comp_vec"))
+
+
+def check_quantizer(S_ref: np.ndarray, gpu: orc.Blob, n_c: int, rep: Report, where: str):
+    """Compare the GPU's quantizer output with the oracle's on the same fp64 state."""
+    ob, x, scores = orc.qz(S_ref, n_c)
+    U = S_ref.shape[0]
+    if n_c > 0:
+        mism = np.where((ob.comp_idx != gpu.comp_idx).any(axis=1))[0]
+        if len(mism):
+            # near-ties in the line scores may go either way
+            srt = -np.sort(-scores, axis=1)
+            for u in mism:
+                hi, lo = srt[u, n_c - 1], srt[u, n_c] if srt.shape[1] > n_c else 0.0
+                assert hi - lo <= AMBIG * max(abs(hi), 1e-300), (
+                    f"{where}: unit {u} compensator choice {gpu.comp_idx[u]} vs oracle "
+                    f"{ob.comp_idx[u]} with a clear score gap ({hi} vs {lo})")
+            rep.ambiguous_selections += len(mism)
+            ob, x, scores = orc.qz(S_ref, n_c, force_sel=gpu.comp_idx)
+    dcode = gpu.codes.astype(np.int16) - ob.codes.astype(np.int16)
+    bad = np.argwhere(dcode != 0)
+    flips = 0
+    for (u, i, j) in bad:
+        xv = x[u, i, j]
+        near_half = abs(abs(xv - math.floor(xv)) - 0.5) <= TIE_TAU
+        assert abs(int(dcode[u, i, j])) == 1 and near_half, (
+            f"{where}: code mismatch at unit {u} ({i},{j}): gpu {gpu.codes[u, i, j]} oracle "
+            f"{ob.codes[u, i, j]} x={xv!r}")
+        flips += 1
+    n_codes = dcode.size
+    assert flips <= FLIP_BUDGET * n_codes, f"{where}: {flips} tie flips in {n_codes} codes"
+    rep.codes_checked += n_codes
+    rep.code_flips += flips
+    np.testing.assert_allclose(gpu.sigma, ob.sigma, rtol=TOL_SCALE, atol=0, err_msg=where)
+    np.testing.assert_allclose(gpu.smooth, ob.smooth, rtol=TOL_SCALE, atol=0, err_msg=where)
+    if n_c > 0:
+        for u in range(U):
+            e = rel_l2(gpu.comp_vec[u], ob.comp_vec[u])
+            assert e <= TOL_COMP, f"{where}: compensator vectors of unit {u} differ ({e})"
+
+
+def run(wl: I.Workload, n_tokens: Optional[int] = None, checked: Optional[Sequence[int]] = None,
+        layer: int = 0, dequant_every: int = 0, device="cuda") -> Report:
+    """Run ``n_tokens`` decode steps (plus flushes) on the GPU and the oracle."""
+    cfg = config_of(wl)
+    U, d, W, nc = wl.n_units, wl.d, wl.window, wl.n_comp
+    n_tokens = wl.decode if n_tokens is None else n_tokens
+    checked = np.arange(U) if checked is None else np.asarray(sorted(set(int(c) for c in checked)))
+    rep = Report(wl.name)
+    print(f"[parity] {wl.name}: units={U} checked={len(checked)} d={d} W={W} n_c={nc} "
+          f"tokens={n_tokens}", flush=True)
+
+    S0 = start_states(wl, checked, layer)
+    state = lq.new_state(cfg, device)
+    views = lq.state_views(cfg, state)
+    lq.lq_state_init(cfg, state, torch.from_numpy(S0).to(device))
+    torch.cuda.synchronize()
+    gb = blob_host(views, checked)
+    check_quantizer(S0[checked].astype(np.float64), gb, nc, rep, "init")
+    assert int(views["fill"].max()) == 0 and int(views["fill"].min()) == 0
+    S_hat = orc.dequant(gb)  # teacher-forced window-start state of the checked units
+
+    # forced partial flushes (staggered windows): host mirror of every unit's fill
+    fill = np.zeros(U, np.int64)
+    seq_of = np.arange(U) // wl.n_v_heads
+    sched = I.stagger_schedule(wl)
+    o_dev = torch.empty((wl.n_seq, wl.n_v_heads, d), dtype=torch.float32, device=device)
+    S_out = torch.empty((U, d, d), dtype=torch.float32, device=device)
+    frozen = None
+    for t in range(n_tokens):
+        tk = I.token(wl, t, I.PHASE_DECODE, layer)
+        dev = {k_: torch.from_numpy(v_).to(device) for k_, v_ in tk.items()}
+        if frozen is None:
+            frozen = {k_: views[k_].clone() for k_ in ("codes", "sigma", "smooth", "comp_idx", "comp_vec")}
+        lq.lq_decode_step(cfg, state, dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], o_dev)
+        o_gpu = o_dev.view(U, d).cpu().numpy()
+        pu = I.tokens_per_unit(wl, {k_: v_[None] for k_, v_ in tk.items()})
+        sel = lambda a: np.ascontiguousarray(a[:, checked])
+        S_hat, o_ref = orc.recurrence(S_hat, sel(pu["q"]), sel(pu["k"]), sel(pu["v"]), sel(pu["beta"]),
+                                      sel(pu["gate"]))
+        err = rel_l2(o_gpu[checked], o_ref[0])
+        assert err <= TOL_OUT, f"{wl.name}: decode token {t}: output rel-L2 {err}"
+        rep.max_out_err = max(rep.max_out_err, err)
+        rep.decode_calls += 1
+        fill += 1
+        # the stored low-bit state is read-only inside a window
+        for k_, v_ in frozen.items():
+            assert torch.equal(views[k_], v_), f"{wl.name}: decode step {t} modified {k_}"
+
+        if dequant_every and (t % dequant_every == dequant_every - 1):
+            lq.lq_dequant_state(cfg, state, S_out, include_buffer=True)
+            e1 = rel_l2(S_out.cpu().numpy()[checked], S_hat)
+            lq.lq_dequant_state(cfg, state, S_out, include_buffer=False)
+            e0 = rel_l2(S_out.cpu().numpy()[checked], orc.dequant(blob_host(views, checked)))
+            assert max(e0, e1) <= TOL_STATE, f"{wl.name}: dequantized state at token {t}: {e0}, {e1}"
+            rep.max_state_err = max(rep.max_state_err, e0, e1)
+
+        force_seq = np.zeros(wl.n_seq, np.uint8)
+        if sched is not None:
+            force_seq[(sched == t)] = 1
+        due = (fill >= W) | ((force_seq[seq_of] != 0) & (fill > 0))
+        if due.any():
+            fm = torch.from_numpy(force_seq).to(device) if force_seq.any() else None
+            lq.lq_window_flush(cfg, state, fm)
+            torch.cuda.synchronize()
+            rep.flushes += 1
+            fill[due] = 0
+            assert torch.equal(views["fill"].cpu(), torch.from_numpy(fill.astype(np.int32))), \
+                f"{wl.name}: fill after flush at token {t}"
+            due_c = np.where(due[checked])[0]
+            if len(due_c):
+                gb = blob_host(views, checked[due_c])
+                check_quantizer(S_hat[due_c], gb, nc, rep, f"flush after token {t}")
+                S_hat[due_c] = orc.dequant(gb)
+            frozen = None
+    flags = lq.lq_read_status(cfg, state)
+    assert flags == 0, f"{wl.name}: device flags {flags:#x}"
+    print(f"[parity] {wl.name}: ok max_out_err={rep.max_out_err:.3g} flushes={rep.flushes} "
+          f"flips={rep.code_flips}/{rep.codes_checked} ambiguous={rep.ambiguous_selections}",
+          flush=True)
+    return rep

@@ -1,0 +1,191 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI, at
+sizes the oracle finishes in seconds (several workgroups with a ragged last
+one, several windows plus a partial one, forced partial flushes, GQA, both
+gate kinds, both head sizes, the limits of the supported range) and the
+device-side error flags.  Needs an MI355X."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import linear_attention_recurrent_gdn_amd as lq  # noqa: E402
+import oracle as orc  # noqa: E402
+from linear_attention_recurrent_gdn_amd import inputs as I  # noqa: E402
+from tests import parity  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+W = I.WORKLOADS
+
+
+def small(base, **kw):
+    return W[base].scaled(**kw)
+
+
+CASES = {
+    # the whole tiny configuration: 1 unit, d=64, 256 tokens, W=64, 2 compensators
+    "tiny_gdn_full": (W["tiny_gdn"], dict(dequant_every=50)),
+    # 15 units (four per workgroup -> ragged last group), outlier lines, 2.3 windows
+    "gdn_small": (small("gdn_decode", name="gdn_small", n_seq=3, n_v_heads=5, n_k_heads=5,
+                        prefill=96, decode=150), dict(dequant_every=37)),
+    # KDA, heavy-tailed values, W=128 with one full window and a partial one
+    "kda_small": (small("kda_decode", name="kda_small", n_seq=2, n_v_heads=3, n_k_heads=3,
+                        prefill=48, decode=170), dict(dequant_every=41)),
+    # GQA: two value heads per key head share the key buffer
+    "gqa_small": (small("gdn_decode", name="gqa_small", n_seq=3, n_v_heads=4, n_k_heads=2,
+                        prefill=40, decode=40, window=16, n_comp=3, outlier_rows=0,
+                        outlier_cols=0), dict(dequant_every=13)),
+    # staggered windows: forced partial flushes at per-sequence offsets
+    "stagger_small": (small("gdn_serving", name="stagger_small", n_seq=8, n_v_heads=2,
+                            n_k_heads=2, prefill=32, decode=50, window=16), dict()),
+    # d = 64 with the channel gate
+    "kda_d64": (small("kda_decode", name="kda_d64", n_seq=2, n_v_heads=5, n_k_heads=5, d=64,
+                      prefill=40, decode=70, window=32, n_comp=2), dict(dequant_every=23)),
+    # window of one token and no compensators: a flush after every token
+    "w1_nc0": (small("gdn_decode", name="w1_nc0", n_seq=2, n_v_heads=3, n_k_heads=3,
+                     prefill=20, decode=12, window=1, n_comp=0, outlier_rows=0,
+                     outlier_cols=0), dict()),
+    # the largest supported window and compensator count
+    "max_limits": (small("gdn_decode", name="max_limits", n_seq=1, n_v_heads=5, n_k_heads=5,
+                         prefill=64, decode=140, window=128, n_comp=16), dict(dequant_every=70)),
+    # zero start state (no prefill) with the channel gate at d=128
+    "kda_zero_start": (small("kda_decode", name="kda_zero_start", n_seq=1, n_v_heads=2,
+                             n_k_heads=2, prefill=0, decode=20, window=8, n_comp=4), dict()),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_parity_small(name):
+    wl, kw = CASES[name]
+    rep = parity.run(wl, **kw)
+    assert rep.decode_calls == wl.decode
+    assert rep.code_flips <= parity.FLIP_BUDGET * max(rep.codes_checked, 1)
+
+
+def _cfg(wl):
+    return parity.config_of(wl)
+
+
+def test_window_overflow_sets_flag_and_nan():
+    wl = small("gdn_decode", name="overflow", n_seq=1, n_v_heads=2, n_k_heads=2, window=2, n_comp=1)
+    cfg = _cfg(wl)
+    st = lq.new_state(cfg)
+    lq.lq_state_init(cfg, st, None)
+    tk = {k: torch.from_numpy(v).cuda() for k, v in I.token(wl, 0).items()}
+    o = torch.empty(wl.n_units * wl.d, device="cuda")
+    for _ in range(2):
+        lq.lq_decode_step(cfg, st, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+    assert lq.lq_read_status(cfg, st) == 0 and torch.isfinite(o).all()
+    lq.lq_decode_step(cfg, st, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)  # window full
+    assert lq.lq_read_status(cfg, st, clear=True) == lq.LQ_DEV_WINDOW_OVERFLOW
+    assert torch.isnan(o).all()
+    assert lq.state_views(cfg, st)["fill"].tolist() == [2, 2]  # nothing appended
+    assert lq.lq_read_status(cfg, st) == 0
+    lq.lq_window_flush(cfg, st, None)
+    lq.lq_decode_step(cfg, st, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+    assert lq.lq_read_status(cfg, st) == 0 and torch.isfinite(o).all()
+
+
+def test_nonfinite_input_sets_flag():
+    wl = small("gdn_decode", name="nonfinite", n_seq=1, n_v_heads=1, n_k_heads=1, window=4, n_comp=1)
+    cfg = _cfg(wl)
+    st = lq.new_state(cfg)
+    lq.lq_state_init(cfg, st, None)
+    tk = {k: torch.from_numpy(v).cuda() for k, v in I.token(wl, 0).items()}
+    tk["v"][0, 0, 5] = float("nan")
+    o = torch.empty(wl.n_units * wl.d, device="cuda")
+    lq.lq_decode_step(cfg, st, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+    assert lq.lq_read_status(cfg, st, clear=True) == lq.LQ_DEV_NONFINITE_INPUT
+
+
+def test_forced_flush_of_empty_window_is_a_no_op():
+    wl = small("gdn_decode", name="noop", n_seq=2, n_v_heads=2, n_k_heads=2, window=4, n_comp=2,
+               prefill=0)
+    cfg = _cfg(wl)
+    st = lq.new_state(cfg)
+    lq.lq_state_init(cfg, st, torch.randn(wl.n_units, wl.d, wl.d, device="cuda"))
+    before = st.clone()
+    lq.lq_window_flush(cfg, st, torch.ones(wl.n_seq, dtype=torch.uint8, device="cuda"))
+    lq.lq_window_flush(cfg, st, None)
+    torch.cuda.synchronize()
+    assert torch.equal(before, st)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_state_kernel_matches_oracle(gate, d):
+    # the FP32-state comparison kernel against the oracle's plain recurrence
+    base = "gdn_decode" if gate == "scalar" else "kda_decode"
+    wl = small(base, name=f"fp32_{gate}_{d}", n_seq=3, n_v_heads=4, n_k_heads=2, d=d, prefill=0,
+               outlier_rows=0, outlier_cols=0)
+    cfg = _cfg(wl)
+    U = wl.n_units
+    rng = np.random.default_rng(9)
+    S0 = rng.standard_normal((U, d, d)).astype(np.float32)
+    S = torch.from_numpy(S0).cuda()
+    S_ref = S0.astype(np.float64)
+    o = torch.empty(U * d, device="cuda")
+    for t in range(40):
+        tk = I.token(wl, t)
+        dev = {k: torch.from_numpy(v).cuda() for k, v in tk.items()}
+        lq.lq_fp32_decode_step(cfg, S, dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], o)
+        pu = I.tokens_per_unit(wl, {k: v[None] for k, v in tk.items()})
+        S_ref, o_ref = orc.recurrence(S_ref, pu["q"], pu["k"], pu["v"], pu["beta"], pu["gate"])
+        assert parity.rel_l2(o.view(U, d).cpu().numpy(), o_ref[0]) <= 1e-5, t
+    assert parity.rel_l2(S.cpu().numpy(), S_ref) <= 1e-5
+
+
+def test_results_do_not_depend_on_batch_position():
+    # one unit alone, and the same unit placed in the middle of a batch with
+    # different neighbours, produce bitwise identical outputs and state
+    wl1 = small("gdn_decode", name="solo", n_seq=1, n_v_heads=1, n_k_heads=1, window=8, n_comp=2,
+                prefill=0)
+    wlb = small("gdn_decode", name="batch", n_seq=3, n_v_heads=3, n_k_heads=3, window=8, n_comp=2,
+                prefill=0)
+    pos = 4
+    rng = np.random.default_rng(3)
+    S_b = rng.standard_normal((wlb.n_units, 128, 128)).astype(np.float32)
+    outs = {}
+    for wl, S0 in ((wl1, S_b[pos:pos + 1]), (wlb, S_b)):
+        cfg = _cfg(wl)
+        st = lq.new_state(cfg)
+        lq.lq_state_init(cfg, st, torch.from_numpy(S0).cuda())
+        o = torch.empty(wl.n_units * wl.d, device="cuda")
+        res = []
+        for t in range(20):
+            tb = I.token(wlb, t)
+            if wl is wl1:
+                tb = {"q": tb["q"][1:2, 1:2], "k": tb["k"][1:2, 1:2], "v": tb["v"][1:2, 1:2],
+                      "beta": tb["beta"][1:2, 1:2], "gate": tb["gate"][1:2, 1:2]}
+            dev = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in tb.items()}
+            lq.lq_decode_step(cfg, st, dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], o)
+            res.append(o.view(wl.n_units, -1)[0 if wl is wl1 else pos].clone())
+            if (t + 1) % 8 == 0:
+                lq.lq_window_flush(cfg, st, None)
+        v = lq.state_views(cfg, st)
+        outs[wl.name] = (torch.stack(res), v["codes"][0 if wl is wl1 else pos].clone())
+    assert torch.equal(outs["solo"][0], outs["batch"][0])
+    assert torch.equal(outs["solo"][1], outs["batch"][1])
+
+
+def test_repeatable_bitwise():
+    wl = small("kda_decode", name="repeat", n_seq=2, n_v_heads=3, n_k_heads=3, window=8, n_comp=3,
+               prefill=0)
+    cfg = _cfg(wl)
+    S0 = torch.randn(wl.n_units, wl.d, wl.d, device="cuda", generator=torch.Generator("cuda").manual_seed(1))
+    runs = []
+    for _ in range(2):
+        st = lq.new_state(cfg)
+        lq.lq_state_init(cfg, st, S0)
+        o = torch.empty(wl.n_units * wl.d, device="cuda")
+        acc = []
+        for t in range(12):
+            dev = {k: torch.from_numpy(v).cuda() for k, v in I.token(wl, t).items()}
+            lq.lq_decode_step(cfg, st, dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], o)
+            acc.append(o.clone())
+            if (t + 1) % 8 == 0:
+                lq.lq_window_flush(cfg, st, None)
+        runs.append((torch.stack(acc), {k: v.clone() for k, v in lq.state_views(cfg, st).items()}))
+    assert torch.equal(runs[0][0], runs[1][0])
+    for key in ("fill", "codes", "sigma", "smooth", "comp_idx", "comp_vec"):
+        assert torch.equal(runs[0][1][key], runs[1][1][key]), key
