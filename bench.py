@@ -1,0 +1,354 @@
+#!/usr/bin/env python
+"""Decode benchmark of the windowed INT8 recurrent-state path on one MI355X.
+
+One step = one decode token for every (sequence, head) unit of every layer
+(lq_decode_step), plus the window-boundary requantization (lq_window_flush)
+for every unit whose window filled on that token.  Inputs are synthetic,
+seeded, and resident in HBM before the timed region starts.  The same steps
+are then timed on the FP32-state comparison kernel.
+
+Prints one JSON line:
+  value            unit-tokens/s (seq·head·tokens/s) of the INT8 path over the timed steps
+  roofline         the decode kernel's algorithmic bytes per launch / its average
+                   launch time (HIP events around every launch), against 8 TB/s
+  fp32_state       the FP32-state kernel on the same steps, and the speedup
+  cpu_baseline     the CPU oracle (FP64, definitional windowed form) on a bounded
+                   sample of the same workload, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "seq·head·tokens/s decode; HBM GB/s vs peak; speedup vs FP32-state kernel"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed decode tokens (default: the workload's)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed tokens first (default: one window)")
+    ap.add_argument("--workload", default="gdn_decode",
+                    help="tiny_gdn | gdn_decode | kda_decode | gdn_serving | hybrid_stack")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-fp32", action="store_true", help="skip the FP32-state comparison loop")
+    ap.add_argument("--no-launch-events", action="store_true",
+                    help="no per-launch events inside the timed loop (roofline omitted)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic byte model (what the method must move, per unit and token)
+# ---------------------------------------------------------------------------
+
+def entry_bytes(wl) -> int:
+    g = wl.d if wl.gate == "channel" else 1
+    return 4 * (wl.d // wl.group + wl.d + 1 + g)
+
+
+def decode_bytes(wl, j: int) -> int:
+    """Bytes one unit moves in one decode step with j tokens already buffered."""
+    d, nc = wl.d, wl.n_comp
+    g = d if wl.gate == "channel" else 1
+    E = entry_bytes(wl)
+    tile = d * d + 4 * (2 * d) + nc * (4 * d + 4)
+    inputs = 4 * (2 * d // wl.group + d + 1 + g)
+    return tile + j * E + inputs + E + 4 * d + 8
+
+
+def flush_bytes(wl, n: int) -> int:
+    """Bytes one unit moves in one flush over n buffered tokens (read and rewrite the stored state)."""
+    d, nc = wl.d, wl.n_comp
+    stored = d * d + 4 * 2 * d + nc * (4 * d + 4)
+    return 2 * stored + n * entry_bytes(wl) + 8
+
+
+# ---------------------------------------------------------------------------
+# inputs on the device
+# ---------------------------------------------------------------------------
+
+def device_tokens(wl, n_tok, layer, gen, dev, weights=None):
+    import torch
+
+    from linear_attention_recurrent_gdn_amd import inputs as I
+
+    out = []
+    for _ in range(n_tok):
+        if wl.projected:
+            h = torch.randn((wl.n_seq, wl.hidden), generator=gen, device=dev).to(torch.bfloat16)
+            out.append(projected(wl, weights, h))
+        else:
+            out.append(I.torch_token(wl, gen, dev))
+    return out
+
+
+def projection_weights(wl, gen, dev):
+    import torch
+
+    std = 1.0 / wl.hidden ** 0.5
+    KH, H, d = wl.n_k_heads, wl.n_v_heads, wl.d
+    return {name: (torch.randn((n, wl.hidden), generator=gen, device=dev) * std).to(torch.bfloat16)
+            for name, n in (("wq", KH * d), ("wk", KH * d), ("wv", H * d), ("wa", H), ("wb", H))}
+
+
+def projected(wl, w, h):
+    """q, k, v, beta, alpha from a bf16 hidden state (input synthesis, not the timed path)."""
+    import torch
+
+    S, KH, H, d = wl.n_seq, wl.n_k_heads, wl.n_v_heads, wl.d
+    p = lambda name: (h @ w[name].t().contiguous()).float()
+    q = p("wq").view(S, KH, d)
+    k = p("wk").view(S, KH, d)
+    return {"q": (q / q.norm(dim=-1, keepdim=True)).contiguous(),
+            "k": (k / k.norm(dim=-1, keepdim=True)).contiguous(),
+            "v": p("wv").view(S, H, d).contiguous(),
+            "beta": torch.sigmoid(p("wb")).contiguous(),
+            "gate": (0.9 + 0.1 * torch.sigmoid(p("wa"))).contiguous()}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl, n_tok, target_s):
+    import numpy as np
+
+    import oracle as orc
+    from linear_attention_recurrent_gdn_amd import inputs as I
+
+    src = wl.scaled(projected=False) if wl.projected else wl
+
+    def sample(units, n):
+        st = I.prefill_streams(src, units, n=n, phase=I.PHASE_DECODE, with_queries=True)
+        S0 = I.surrogate_state(src, units).astype(np.float64)
+        return S0, st
+
+    # calibrate on a few units, then size the sample for about target_s seconds
+    cal_units = list(range(min(2 * orc.num_threads(), wl.n_units)))
+    cal_tok = min(n_tok, 2 * wl.window)
+    S0, st = sample(cal_units, cal_tok)
+    t0 = time.perf_counter()
+    orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp)
+    rate = len(cal_units) * cal_tok / max(time.perf_counter() - t0, 1e-6)
+    n_units = int(max(1, min(wl.n_units, rate * target_s / n_tok)))
+    units = np.linspace(0, wl.n_units - 1, n_units).astype(int)
+    S0, st = sample(units, n_tok)
+    t0 = time.perf_counter()
+    orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp)
+    dt = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except Exception:
+        pass
+    return {
+        "value": n_units * n_tok / dt,
+        "unit": "seq·head·tokens/s",
+        "cores": orc.num_threads(),
+        "kind": "oracle",
+        "sample": (f"{n_units} of {wl.n_units} units x {n_tok} decode tokens (flushes included), "
+                   f"FP64 definitional windowed form, {dt:.1f} s; input generation excluded; "
+                   f"host CPU: {cpu_model}"),
+    }
+
+
+# ---------------------------------------------------------------------------
+# measured HBM traffic (rocprofv3 --pmc), valid only for the kernel it was taken on
+# ---------------------------------------------------------------------------
+
+def kernel_sha() -> str:
+    p = os.path.join(ROOT, "linear_attention_recurrent_gdn_amd", "csrc", "lq_decode.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    p = os.path.join(ROOT, "profiles", f"decode_int8_{workload}_traffic.json")
+    try:
+        rec = json.load(open(p))
+    except Exception:
+        return None
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); units shard across GPUs with no exchange, "
+              f"so the per-GPU figure is the N=1 line.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import linear_attention_recurrent_gdn_amd as lq
+    from linear_attention_recurrent_gdn_amd import inputs as I
+
+    lq.load_library()
+    wl = I.WORKLOADS[args.workload]
+    W, U, L, d = wl.window, wl.n_units, wl.layers, wl.d
+    steps = wl.decode if args.steps is None else args.steps
+    warmup = W if args.warmup is None else args.warmup
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(dev).manual_seed(1000 + wl.seed)
+    cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind)
+    stream = torch.cuda.current_stream()
+
+    # ---- start states: FP32 prefill through the FP32-state kernel (input synthesis)
+    weights = [projection_weights(wl, gen, dev) for _ in range(L)] if wl.projected else [None] * L
+    S_fp32, states = [], []
+    o = torch.empty((wl.n_seq, wl.n_v_heads, d), device=dev)
+    for layer in range(L):
+        S = torch.zeros((U, d, d), device=dev)
+        for tk in device_tokens(wl, wl.prefill, layer, gen, dev, weights[layer]):
+            lq.lq_fp32_decode_step(cfg, S, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+        sc = I.outlier_scale(wl, layer)
+        if sc is not None:
+            r, c = (torch.from_numpy(x).to(dev) for x in sc)
+            S *= r[:, :, None] * c[:, None, :]
+        st = lq.new_state(cfg, dev)
+        lq.lq_state_init(cfg, st, S)
+        states.append(st)
+        S_fp32.append(S)
+    n_tok = warmup + steps
+    toks = [device_tokens(wl, n_tok, layer, gen, dev, weights[layer]) for layer in range(L)]
+    torch.cuda.synchronize()
+
+    sched = I.stagger_schedule(wl)
+    fill = np.zeros(wl.n_seq, np.int64)
+    force_dev = torch.zeros(wl.n_seq, dtype=torch.uint8, device=dev)
+    decode_events, flush_events, decode_js = [], [], []
+
+    def int8_step(t, timed):
+        events = timed and not args.no_launch_events
+        for layer in range(L):
+            tk = toks[layer][t]
+            if events:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            lq.lq_decode_step(cfg, states[layer], tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+            if events:
+                b.record(stream)
+                decode_events.append((a, b))
+                decode_js.append(fill.copy())
+        fill[:] += 1
+        forced = (sched == t) if (sched is not None and t < warmup) else np.zeros(wl.n_seq, bool)
+        due = (fill >= W) | (forced & (fill > 0))
+        if due.any():
+            fm = None
+            if forced.any():
+                force_dev.copy_(torch.from_numpy(forced.astype(np.uint8)))
+                fm = force_dev
+            for layer in range(L):
+                if events:
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                lq.lq_window_flush(cfg, states[layer], fm)
+                if events:
+                    b.record(stream)
+                    flush_events.append((a, b, int(due.sum()) * wl.n_v_heads, fill[due].copy()))
+            fill[due] = 0
+
+    for t in range(warmup):
+        int8_step(t, False)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(warmup, n_tok):
+        int8_step(t, True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    int8_ms = e0.elapsed_time(e1)
+    flags = [lq.lq_read_status(cfg, st) for st in states]
+    if any(flags):
+        raise RuntimeError(f"device flags set during the run: {flags}")
+
+    result = {
+        "metric": METRIC,
+        "value": U * L * steps / (int8_ms * 1e-3),
+        "unit": "seq·head·tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": int8_ms / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "state_dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "layers": L, "n_seq": wl.n_seq, "n_v_heads": wl.n_v_heads, "n_k_heads": wl.n_k_heads,
+            "d_k": d, "d_v": d, "gate": wl.gate, "window": W, "n_comp": wl.n_comp,
+            "prefill": wl.prefill, "units": U * L,
+        },
+    }
+
+    if decode_events:
+        durs = np.array([a.elapsed_time(b) for a, b in decode_events]) * 1e-3  # s
+        byts = np.array([sum(decode_bytes(wl, int(j)) * wl.n_v_heads for j in js) for js in decode_js],
+                        dtype=np.float64)
+        achieved = byts.mean() / durs.mean() / 1e9
+        result["roofline"] = {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": measured_traffic(wl.name),
+            "kernel": "decode_int8_kernel",
+            "avg_launch_us": durs.mean() * 1e6,
+            "alg_bytes_per_launch": byts.mean(),
+        }
+        if flush_events:
+            fd = np.array([a.elapsed_time(b) for a, b, _, _ in flush_events]) * 1e-3
+            result["flush"] = {"launches": len(flush_events), "avg_launch_us": fd.mean() * 1e6,
+                               "units_flushed_per_launch": float(np.mean([n for _, _, n, _ in flush_events]))}
+
+    if not args.no_fp32:
+        for t in range(warmup):
+            for layer in range(L):
+                tk = toks[layer][t]
+                lq.lq_fp32_decode_step(cfg, S_fp32[layer], tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for t in range(warmup, n_tok):
+            for layer in range(L):
+                tk = toks[layer][t]
+                lq.lq_fp32_decode_step(cfg, S_fp32[layer], tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        fp32_ms = f0.elapsed_time(f1)
+        fp32_bytes = U * L * (8 * d * d + 4 * (2 * d // wl.group + 2 * d + 1 + (d if wl.gate == "channel" else 1)))
+        result["fp32_state"] = {
+            "value": U * L * steps / (fp32_ms * 1e-3),
+            "ms_per_step": fp32_ms / steps,
+            "alg_GBps": fp32_bytes / (fp32_ms / steps * 1e-3) / 1e9,
+            "speedup_int8_vs_fp32": fp32_ms / int8_ms,
+        }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

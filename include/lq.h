@@ -109,11 +109,14 @@ typedef struct lq_config {
  *   buf_v     fp32  [units][window][d_v]
  *   buf_beta  fp32  [units][window]
  *   buf_gate  fp32  [units][window] (scalar) or [units][window][d_k] (channel)
+ *   work      int32 [1 + units]        scratch of lq_window_flush: count, then the
+ *                                      units whose window is due
  */
 typedef struct lq_layout {
     size_t total_bytes;
     size_t status, fill, codes, sigma, smooth, comp_idx, comp_vec;
     size_t buf_k, buf_v, buf_beta, buf_gate;
+    size_t work;
 } lq_layout;
 
 /* Size in bytes of the state blob for cfg.  Host only, no HIP call. */

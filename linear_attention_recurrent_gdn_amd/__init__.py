@@ -44,7 +44,7 @@ class _CConfig(ctypes.Structure):
 
 
 _LAYOUT_FIELDS = ("total_bytes", "status", "fill", "codes", "sigma", "smooth", "comp_idx",
-                  "comp_vec", "buf_k", "buf_v", "buf_beta", "buf_gate")
+                  "comp_vec", "buf_k", "buf_v", "buf_beta", "buf_gate", "work")
 
 
 class _CLayout(ctypes.Structure):
@@ -79,7 +79,7 @@ def load_library(path: Optional[str] = None):
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("LQ_LIB_PATH") or LIB_PATH
     if not os.path.exists(p):
         raise ImportError(
             f"{p} is missing: build it first (python -m linear_attention_recurrent_gdn_amd._build)")
@@ -289,4 +289,5 @@ def state_views(cfg: Config, state) -> Dict[str, "object"]:
         "buf_v": view(L["buf_v"], U * W * cfg.d_v, torch.float32, (U, W, cfg.d_v)),
         "buf_beta": view(L["buf_beta"], U * W, torch.float32, (U, W)),
         "buf_gate": view(L["buf_gate"], U * W * g, torch.float32, (U, W) if g == 1 else (U, W, g)),
+        "work": view(L["work"], U + 1, torch.int32, (U + 1,)),
     }

@@ -14,13 +14,17 @@
 // so r = A_1..A_n q and acc = sum_i beta_i v_i k_i^T A_{i+1}..A_n q, and o is
 // S_n q.  The INT8 tile, sigma, s and compensators are only read.
 //
-// Mapping: one wavefront per unit, four units per workgroup.  The 16 KiB
-// (d = 128) INT8 tile is requested with 16-byte coalesced loads before the
-// reverse pass so its latency hides behind the sequential chain; the chain's
-// d-length dot products reduce with DPP; buffer entries are loaded a batch
-// ahead of their use.  The tile product reads s*r from LDS, each lane
-// covering 16 columns of 16 rows, and reduces each row over 8 lanes with DPP.
-// The kernel is HBM-bound (about one flop per byte): no MFMA.
+// Mapping: one workgroup of four wavefronts per unit.  Each wavefront
+// requests its quarter of the INT8 tile (4 KiB at d = 128) with 16-byte
+// coalesced loads at kernel start.  Wavefront 0 runs the reverse pass: the
+// buffered tokens stream through a register ring refilled a fixed number of
+// tokens ahead (so the wait counts are exact and memory latency is paid once
+// per ring, not per token), the d-length dot products reduce with DPP, and
+// with a scalar gate the running gate product stays off the dependent chain.
+// After one barrier every wavefront multiplies its tile rows by s*r (read from
+// LDS, each lane covering 16 columns, rows reduced over 8 lanes with DPP) and
+// writes its rows of o.  The kernel is HBM-bound (about one flop per byte):
+// no MFMA.
 //
 // decode_fp32_kernel: the FP32-state step the pages compare against (the
 // bedrocknews.com review: the baseline is FP32 inference).  The row form
@@ -72,23 +76,23 @@ struct Entry {
 
 }  // namespace
 
-template <int D, bool KDA>
+template <int D, bool KDA, int P>
 __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeArgs a) {
-    constexpr int EPL = D / kWave;   // state elements per lane along d
+    constexpr int EPL = D / kWave;   // state elements per lane in the chain wave
     constexpr int GE = KDA ? EPL : 1;
+    constexpr int RW = D / 4;        // tile rows per wave
     constexpr int LPR = D / 16;      // lanes per code row (16 codes per 16-byte load)
-    constexpr int RPL = kWave / LPR; // code rows per wave-wide load
-    constexpr int NL = D / RPL;      // 16-byte loads per lane for the whole tile
-    constexpr int B = 4;             // buffer entries per prefetch batch
+    constexpr int RPL = kWave / LPR; // code rows per wave-wide 16-byte load
+    constexpr int NLW = RW / RPL;    // 16-byte tile loads per lane
+    constexpr int NCP = 8;           // compensator slots held in registers
 
-    __shared__ float lds_x[4][D];
-    __shared__ float lds_o[4][D];
+    __shared__ float lds_x[D];       // s * r, r = A_1..A_n q (all waves read it)
+    __shared__ float lds_add[D];     // buffered-token and compensator terms of o
 
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    const int u = blockIdx.x * 4 + wave;
+    const int u = blockIdx.x;
     if (u >= a.dm.n_units) return;
-
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = lane_id();
     const int W = a.dm.window;
     const int nc = a.dm.n_comp;
     const int s = u / a.dm.n_v_heads;
@@ -96,164 +100,193 @@ __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeArgs a) {
     const int kh = h / a.dm.group;
     const size_t kvec = ((size_t)s * a.dm.n_k_heads + kh);  // key-head row of q, k
 
-    const int j = a.blob.fill[u];  // tokens already in the window
-    float* o = a.o + (size_t)u * D + lane * EPL;
+    // ---- every wave owns a quarter of the INT8 tile (RW rows) and writes those rows of o
+    const int cg = lane % LPR;  // this lane's 16-column group
+    const int row0 = wave * RW;
+    const uint4* tile = reinterpret_cast<const uint4*>(a.blob.codes + ((size_t)u * D + row0) * D);
+    const int my_row = row0 + min(cg, NLW - 1) * RPL + lane / LPR;  // row this lane writes (cg < NLW)
+    uint4 tw[NLW];
+    float sg_row;
+
+    // tokens already in the window (uniform: every branch below is scalar)
+    const int j = __builtin_amdgcn_readfirstlane(a.blob.fill[u]);
     if (j >= W) {
-        Vec<EPL> nanv;
-        for (int e = 0; e < EPL; ++e) nanv.e[e] = __builtin_nanf("");
-        store_vec(o, nanv);
-        if (lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_WINDOW_OVERFLOW);
+        if (cg < NLW) a.o[(size_t)u * D + my_row] = __builtin_nanf("");
+        if (wave == 0 && lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_WINDOW_OVERFLOW);
         return;
     }
 
-    // ---- request the INT8 tile first: its latency overlaps the reverse pass
-    const uint4* tile = reinterpret_cast<const uint4*>(a.blob.codes + (size_t)u * D * D);
-    uint4 tw[NL];
+    if (wave != 0) {
 #pragma unroll
-    for (int t = 0; t < NL; ++t) tw[t] = tile[t * kWave + lane];
-    const Vec<EPL> sm = load_vec<EPL>(a.blob.smooth + (size_t)u * D + lane * EPL);
-    const Vec<EPL> sg = load_vec<EPL>(a.blob.sigma + (size_t)u * D + lane * EPL);
-
-    // ---- current token: read, check, append to the window buffer
-    const Vec<EPL> qv = load_vec<EPL>(a.q + kvec * D + lane * EPL);
-    Entry<EPL, GE> cur;
-    cur.k = load_vec<EPL>(a.k + kvec * D + lane * EPL);
-    cur.v = load_vec<EPL>(a.v + (size_t)u * D + lane * EPL);
-    cur.beta = a.beta[u];
-    if constexpr (KDA) {
-        cur.g = load_vec<GE>(a.gate + (size_t)u * D + lane * EPL);
+        for (int t = 0; t < NLW; ++t) tw[t] = tile[t * kWave + lane];
+        sg_row = a.blob.sigma[(size_t)u * D + my_row];
     } else {
-        cur.g.e[0] = a.gate[u];
-    }
-    bool ok = finite(cur.beta);
-    for (int e = 0; e < EPL; ++e) ok = ok && finite(qv.e[e]) && finite(cur.k.e[e]) && finite(cur.v.e[e]);
-    for (int e = 0; e < GE; ++e) ok = ok && finite(cur.g.e[e]);
-    if (__any(!ok) && lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_NONFINITE_INPUT);
+        float* bk = a.blob.buf_k + kvec * (size_t)W * D;
+        float* bv = a.blob.buf_v + (size_t)u * W * D;
+        float* bb = a.blob.buf_beta + (size_t)u * W;
+        float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
 
-    float* bk = a.blob.buf_k + kvec * (size_t)W * D;
-    float* bv = a.blob.buf_v + (size_t)u * W * D;
-    float* bb = a.blob.buf_beta + (size_t)u * W;
-    float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
-    if (h % a.dm.group == 0) store_vec(bk + (size_t)j * D + lane * EPL, cur.k);
-    store_vec(bv + (size_t)j * D + lane * EPL, cur.v);
-    if constexpr (KDA) {
-        store_vec(bg + (size_t)j * D + lane * EPL, cur.g);
-    } else {
-        if (lane == 0) bg[j] = cur.g.e[0];
-    }
-    if (lane == 0) bb[j] = cur.beta;
-
-    // ---- reverse pass over the window: newest token first
-    Vec<EPL> r = qv;
-    Vec<EPL> acc;
-    for (int e = 0; e < EPL; ++e) acc.e[e] = 0.f;
-
-    auto step = [&](const Entry<EPL, GE>& en) {
-        float p = 0.f;
-        for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(en.k.e[e], r.e[e], p);
-        const float c = wave_sum(p);
-        const float bc = en.beta * c;
-        for (int e = 0; e < EPL; ++e) {
-            acc.e[e] = __builtin_fmaf(bc, en.v.e[e], acc.e[e]);
-            const float ge = KDA ? en.g.e[e] : en.g.e[0];
-            r.e[e] = ge * __builtin_fmaf(-bc, en.k.e[e], r.e[e]);
-        }
-    };
-    auto load_entry = [&](int i, Entry<EPL, GE>& en) {
-        en.k = load_vec<EPL>(bk + (size_t)i * D + lane * EPL);
-        en.v = load_vec<EPL>(bv + (size_t)i * D + lane * EPL);
-        en.beta = bb[i];
+        // loads in the order they are consumed (vector loads return in order):
+        // the current token, the newest P buffered tokens (a ring refilled P
+        // tokens ahead of use; indices below 0 are clamped to entry 0 and not
+        // used), beta and the scalar gate of the whole window (one per lane),
+        // smoothing and compensators
+        const Vec<EPL> qv = load_vec<EPL>(a.q + kvec * D + lane * EPL);
+        Entry<EPL, GE> cur;
+        cur.k = load_vec<EPL>(a.k + kvec * D + lane * EPL);
+        cur.v = load_vec<EPL>(a.v + (size_t)u * D + lane * EPL);
+        cur.beta = a.beta[u];
         if constexpr (KDA) {
-            en.g = load_vec<GE>(bg + (size_t)i * D + lane * EPL);
+            cur.g = load_vec<GE>(a.gate + (size_t)u * D + lane * EPL);
         } else {
-            en.g.e[0] = bg[i];
+            cur.g.e[0] = a.gate[u];
         }
-    };
+        auto load_entry = [&](int i, Entry<EPL, GE>& en) {
+            en.k = load_vec<EPL>(bk + (size_t)i * D + lane * EPL);
+            en.v = load_vec<EPL>(bv + (size_t)i * D + lane * EPL);
+            if constexpr (KDA) en.g = load_vec<GE>(bg + (size_t)i * D + lane * EPL);
+        };
+        Entry<EPL, GE> ring[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) load_entry(max(j - 1 - p, 0), ring[p]);
+        const float bwin0 = bb[min(lane, W - 1)];
+        const float bwin1 = bb[min(lane + kWave, W - 1)];
+        float awin0 = 0.f, awin1 = 0.f;
+        if constexpr (!KDA) {
+            awin0 = bg[min(lane, W - 1)];
+            awin1 = bg[min(lane + kWave, W - 1)];
+        }
+        // this wave's tile quarter comes after the data the reverse pass needs first
+#pragma unroll
+        for (int t = 0; t < NLW; ++t) tw[t] = tile[t * kWave + lane];
+        sg_row = a.blob.sigma[(size_t)u * D + my_row];
+        const Vec<EPL> sm = load_vec<EPL>(a.blob.smooth + (size_t)u * D + lane * EPL);
+        const int cidx = a.blob.comp_idx[(size_t)u * nc + min(lane, max(nc - 1, 0))];
+        Vec<EPL> cvec[NCP];
+#pragma unroll
+        for (int c = 0; c < NCP; ++c)
+            cvec[c] = load_vec<EPL>(a.blob.comp_vec + ((size_t)u * nc + min(c, max(nc - 1, 0))) * D + lane * EPL);
 
-    Entry<EPL, GE> ba[B], bn[B];
-    int i = j - 1;
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-        if (i - b >= 0) load_entry(i - b, ba[b]);
-    step(cur);
-    while (i >= 0) {
-        const int inext = i - B;
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-            if (inext - b >= 0) load_entry(inext - b, bn[b]);
-#pragma unroll
-        for (int b = 0; b < B; ++b)
-            if (i - b >= 0) step(ba[b]);
-#pragma unroll
-        for (int b = 0; b < B; ++b) ba[b] = bn[b];
-        i = inext;
-    }
+        // check the current token and append it to the window buffer
+        bool ok = finite(cur.beta);
+        for (int e = 0; e < EPL; ++e) ok = ok && finite(qv.e[e]) && finite(cur.k.e[e]) && finite(cur.v.e[e]);
+        for (int e = 0; e < GE; ++e) ok = ok && finite(cur.g.e[e]);
+        if (__any(!ok) && lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_NONFINITE_INPUT);
+        if (h % a.dm.group == 0) store_vec(bk + (size_t)j * D + lane * EPL, cur.k);
+        store_vec(bv + (size_t)j * D + lane * EPL, cur.v);
+        if constexpr (KDA) {
+            store_vec(bg + (size_t)j * D + lane * EPL, cur.g);
+        } else {
+            if (lane == 0) bg[j] = cur.g.e[0];
+        }
+        if (lane == 0) bb[j] = cur.beta;
 
-    // ---- compensator tokens: rows add (k_c . r) at their row, columns add v_c r[col]
-    Vec<EPL> rowadd;
-    for (int e = 0; e < EPL; ++e) rowadd.e[e] = 0.f;
-    for (int c = 0; c < nc; ++c) {
-        const int idx = a.blob.comp_idx[(size_t)u * nc + c];
-        const Vec<EPL> w = load_vec<EPL>(a.blob.comp_vec + ((size_t)u * nc + c) * D + lane * EPL);
-        if (idx < D) {
+        // reverse pass over the window, newest token first.  With a scalar
+        // gate the running gate product sc stays off the dependent chain:
+        // r_true = sc * r, so r -= (beta (k.r)) k and acc += beta sc (k.r) v.
+        Vec<EPL> r = qv;
+        Vec<EPL> acc;
+        for (int e = 0; e < EPL; ++e) acc.e[e] = 0.f;
+        float sc = 1.0f;
+        auto step = [&](const Entry<EPL, GE>& en, float beta, float alpha) {
             float p = 0.f;
-            for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(w.e[e], r.e[e], p);
-            const float dot = wave_sum(p);
-            for (int e = 0; e < EPL; ++e)
-                if (lane * EPL + e == idx) rowadd.e[e] += dot;
-        } else {
-            const int col = idx - D;
-            float rsel = r.e[0];
-            if constexpr (EPL == 2) rsel = (col & 1) ? r.e[1] : r.e[0];
-            const float rc = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsel), col / EPL));
-            for (int e = 0; e < EPL; ++e) acc.e[e] = __builtin_fmaf(w.e[e], rc, acc.e[e]);
+            for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(en.k.e[e], r.e[e], p);
+            const float red = wave_sum(p);
+            const float cr = beta * red;
+            if constexpr (KDA) {
+                for (int e = 0; e < EPL; ++e) {
+                    r.e[e] = en.g.e[e] * __builtin_fmaf(-cr, en.k.e[e], r.e[e]);
+                    acc.e[e] = __builtin_fmaf(cr, en.v.e[e], acc.e[e]);
+                }
+            } else {
+                for (int e = 0; e < EPL; ++e) r.e[e] = __builtin_fmaf(-cr, en.k.e[e], r.e[e]);
+                const float w = cr * sc;
+                for (int e = 0; e < EPL; ++e) acc.e[e] = __builtin_fmaf(w, en.v.e[e], acc.e[e]);
+                sc *= alpha;
+            }
+        };
+        step(cur, cur.beta, cur.g.e[0]);
+        for (int s0 = 0; s0 < j; s0 += P) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int i = j - 1 - (s0 + p);
+                if (i >= 0) {
+                    const float beta = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, i < kWave ? bwin0 : bwin1), i & (kWave - 1)));
+                    float alpha = 0.f;
+                    if constexpr (!KDA)
+                        alpha = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, i < kWave ? awin0 : awin1), i & (kWave - 1)));
+                    step(ring[p], beta, alpha);
+                }
+                load_entry(max(i - P, 0), ring[p]);
+            }
+        }
+        if constexpr (!KDA)
+            for (int e = 0; e < EPL; ++e) r.e[e] *= sc;
+
+        // compensator tokens: rows add (k_c . r) at their row, columns add v_c r[col]
+        auto comp = [&](int idx, const Vec<EPL>& w) {
+            if (idx < D) {
+                float p = 0.f;
+                for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(w.e[e], r.e[e], p);
+                const float dot = wave_sum(p);
+                for (int e = 0; e < EPL; ++e)
+                    if (lane * EPL + e == idx) acc.e[e] += dot;
+            } else {
+                const int col = idx - D;
+                float rsel = r.e[0];
+                if constexpr (EPL == 2) rsel = (col & 1) ? r.e[1] : r.e[0];
+                const float rc = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsel), col / EPL));
+                for (int e = 0; e < EPL; ++e) acc.e[e] = __builtin_fmaf(w.e[e], rc, acc.e[e]);
+            }
+        };
+#pragma unroll
+        for (int c = 0; c < NCP; ++c)
+            if (c < nc) comp(__builtin_amdgcn_readlane(cidx, c), cvec[c]);
+        for (int c = NCP; c < nc; ++c)
+            comp(__builtin_amdgcn_readlane(cidx, c),
+                 load_vec<EPL>(a.blob.comp_vec + ((size_t)u * nc + c) * D + lane * EPL));
+
+        for (int e = 0; e < EPL; ++e) {
+            lds_x[lane * EPL + e] = sm.e[e] * r.e[e];
+            lds_add[lane * EPL + e] = acc.e[e];
         }
     }
+    lds_barrier();
 
-    // ---- INT8 tile times (s * r)
-    for (int e = 0; e < EPL; ++e) lds_x[wave][lane * EPL + e] = sm.e[e] * r.e[e];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int cg = lane % LPR;  // this lane's 16-column group
+    // ---- every wave: its rows of Q (s * r), then o = sigma * that + the rest
     float xs[16];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        float4 x4 = *reinterpret_cast<const float4*>(&lds_x[wave][cg * 16 + 4 * t]);
+        float4 x4 = *reinterpret_cast<const float4*>(&lds_x[cg * 16 + 4 * t]);
         xs[4 * t + 0] = x4.x;
         xs[4 * t + 1] = x4.y;
         xs[4 * t + 2] = x4.z;
         xs[4 * t + 3] = x4.w;
     }
-    float part[NL];
+    float mine = 0.f;
 #pragma unroll
-    for (int t = 0; t < NL; ++t) {
+    for (int t = 0; t < NLW; ++t) {
         const uint32_t wd[4] = {tw[t].x, tw[t].y, tw[t].z, tw[t].w};
-        float p = 0.f;
+        float p0 = 0.f, p1 = 0.f;
 #pragma unroll
         for (int wi = 0; wi < 4; ++wi) {
 #pragma unroll
-            for (int by = 0; by < 4; ++by) {
-                const int code = (int)(wd[wi] << (24 - 8 * by)) >> 24;
-                p = __builtin_fmaf((float)code, xs[4 * wi + by], p);
+            for (int by = 0; by < 4; by += 2) {
+                p0 = __builtin_fmaf((float)((int)(wd[wi] << (24 - 8 * by)) >> 24), xs[4 * wi + by], p0);
+                p1 = __builtin_fmaf((float)((int)(wd[wi] << (16 - 8 * by)) >> 24), xs[4 * wi + by + 1], p1);
             }
         }
-        if constexpr (LPR == 8) part[t] = sum8(p);
-        else part[t] = sum4(p);
+        float p = p0 + p1;
+        if constexpr (LPR == 8) p = sum8(p);
+        else p = sum4(p);
+        if (t == cg) mine = p;
     }
-#pragma unroll
-    for (int t = 0; t < NL; ++t)
-        if (t % LPR == cg) lds_o[wave][t * RPL + lane / LPR] = part[t];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    Vec<EPL> out;
-    for (int e = 0; e < EPL; ++e)
-        out.e[e] = __builtin_fmaf(sg.e[e], lds_o[wave][lane * EPL + e], rowadd.e[e] + acc.e[e]);
-    store_vec(o, out);
-    if (lane == 0) a.blob.fill[u] = j + 1;
+    if (cg < NLW)
+        a.o[(size_t)u * D + my_row] = __builtin_fmaf(sg_row, mine, lds_add[my_row]);
+    if (wave == 0 && lane == 0) a.blob.fill[u] = j + 1;
 }
 
 template <int D, bool KDA>
@@ -334,14 +367,21 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
     }
 }
 
+#ifndef LQ_RING_GDN
+#define LQ_RING_GDN 8
+#endif
+#ifndef LQ_RING_KDA
+#define LQ_RING_KDA 8
+#endif
+
 hipError_t launch_decode_int8(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
-    const dim3 grid((a.dm.n_units + 3) / 4), block(256);
+    const dim3 grid(a.dm.n_units), block(256);
     if (d == 128) {
-        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_int8_kernel<128, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((decode_int8_kernel<128, false>), grid, block, 0, st, a);
+        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_int8_kernel<128, true, LQ_RING_KDA>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_int8_kernel<128, false, LQ_RING_GDN>), grid, block, 0, st, a);
     } else {
-        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_int8_kernel<64, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((decode_int8_kernel<64, false>), grid, block, 0, st, a);
+        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_int8_kernel<64, true, 16>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_int8_kernel<64, false, 16>), grid, block, 0, st, a);
     }
     return hipGetLastError();
 }

@@ -8,23 +8,39 @@
 // bedrocknews.com review: the biggest outlier rows and columns are pulled out
 // and kept in FP16/FP32, and the state goes from FP32 to INT8.
 //
-// One workgroup per unit, four threads per state row, each thread holding a
-// quarter row in FP64 registers:
+// Work list: a one-workgroup scan writes the units whose window is due (full,
+// or forced and non-empty) into the blob's work list; the materialize kernel
+// then runs on a fixed grid that walks that list, so a boundary that concerns
+// a few units does not launch a workgroup per unit.
+//
+// Materialize: one workgroup per unit at a time, each thread holding 2 rows x
+// 16 columns of the state in FP64 registers (a row is split over D/16
+// consecutive lanes):
 //   A  load: S = Diag(sigma) Q Diag(s) + compensator lines (flush, dequant) or
 //      the caller's FP32 start state (init);
-//   B  forward replay of the buffered tokens, row form
-//        x = g * S[i,:];  S[i,:] = x + beta (v_i - x.k) k
-//      in FP64 with the buffer staged through LDS a batch at a time (FP64 so
-//      that the rounding decisions below match an FP64 reference);
-//   C  quantizer, in the same pass (readings; the pages print no formula):
-//        line scores = squared L2 norms of rows and columns; the n_comp best
-//        lines (ties to the lower candidate index, rows before columns) go to
-//        fp32 compensator slots, rows taken whole, columns with the selected
-//        rows' entries zeroed; the residual R has those lines zeroed;
-//        s_j = sqrt(max_i |R_ij|) (1 if zero), sigma_i = max_j |R_ij/s_j|/127,
-//        both fp32; codes = clamp(rne(R_ij / (sigma_i s_j)), -127, 127).
-// Column reductions go lane-to-lane inside a wave (reduce-scatter over the
-// 16 rows a wave holds), then across waves through LDS in a fixed order, so
+//   B  forward replay of the buffered tokens in FP64 (FP64 so that the
+//      rounding decisions below match an FP64 reference), in a rescaled form
+//      that costs two FMAs per element and token:
+//        scalar gate  S = g T:  g' = g alpha;  d = T[i,:].k;
+//                     T[i,:] += beta (v_i - g' d) / g' * k
+//        channel gate S = T Diag(G):  G' = G * a;  d = T[i,:].(G' * k);
+//                     T[i,:] += beta (v_i - d) * (k / G')
+//      (a token-by-token restatement of x = g * S[i,:]; S[i,:] = x + beta
+//      (v_i - x.k) k).  g and G are folded into T before they can
+//      underflow.  The key (and for the channel gate its two scaled forms) is
+//      staged through LDS as FP64, a batch of tokens at a time, with a padded
+//      layout so the D/16 column chunks that a wavefront reads at once fall in
+//      different LDS banks;
+//   C  quantizer, in the same workgroup (readings; the pages print no
+//      formula): line scores = squared L2 norms of rows and columns; the
+//      n_comp best lines (ties to the lower candidate index, rows before
+//      columns) go to fp32 compensator slots, rows taken whole, columns with
+//      the selected rows' entries zeroed; the residual R has those lines
+//      zeroed; s_j = sqrt(max_i |R_ij|) (1 if zero), sigma_i =
+//      max_j |R_ij / s_j| / 127, both fp32; codes = clamp(rne(R_ij /
+//      (sigma_i s_j)), -127, 127).
+// Column reductions go lane-to-lane inside a wavefront (reduce-scatter over
+// its row pairs), then across wavefronts through LDS in a fixed order, so
 // results are deterministic.
 
 #include "lq_internal.h"
@@ -32,6 +48,9 @@
 namespace lq {
 
 namespace {
+
+constexpr double kRescaleBelow = 0x1p-200;   // fold the gate product into T below this
+constexpr double kMinChannelGate = 0x1p-45;  // per-token channel gate floor inside the flush
 
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
@@ -41,35 +60,36 @@ __device__ __forceinline__ double dpp_f64(double x) {
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-__device__ __forceinline__ double sum4_f64(double x) {
-    x += dpp_f64<kDppQuadXor1>(x);
+// Sum / max over groups of N consecutive lanes (N = 4 or 8), result in every lane.
+template <int N>
+__device__ __forceinline__ double group_sum(double x) {
+    if constexpr (N == 8) x += dpp_f64<kDppRowHalfMirror>(x);
     x += dpp_f64<kDppQuadXor2>(x);
+    x += dpp_f64<kDppQuadXor1>(x);
     return x;
 }
-
-__device__ __forceinline__ double max4_f64(double x) {
-    x = fmax(x, dpp_f64<kDppQuadXor1>(x));
+template <int N>
+__device__ __forceinline__ double group_max(double x) {
+    if constexpr (N == 8) x = fmax(x, dpp_f64<kDppRowHalfMirror>(x));
     x = fmax(x, dpp_f64<kDppQuadXor2>(x));
+    x = fmax(x, dpp_f64<kDppQuadXor1>(x));
     return x;
 }
 
 __device__ __forceinline__ double shfl_xor_f64(double x, int m) {
     const uint64_t b = __builtin_bit_cast(uint64_t, x);
-    const int lane = lane_id();
-    const int src = (lane ^ m) << 2;
+    const int src = (lane_id() ^ m) << 2;
     const int lo = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)b);
     const int hi = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(b >> 32));
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-// Reduce-scatter of a thread's CPT column values over the 16 lanes of a wave
-// that share its column quarter (lane bits 2..5).  Afterwards each lane holds
-// CPT/16 reduced values in v[0 .. CPT/16); their columns are
-// c0 + colbase + {0 .. CPT/16 - 1}, colbase returned.
-template <int CPT, int N, bool MAX>
-__device__ __forceinline__ void rs_stage(double (&v)[CPT], int lane, int m, int& colbase) {
+// One reduce-scatter stage over lane bit m: keep half of the N values, add
+// (or max) the partner's copy of that half.
+template <int N, bool MAX>
+__device__ __forceinline__ void rs_stage(double (&v)[16], int m, int& colbase) {
     constexpr int HALF = N / 2;
-    const bool upper = (lane & m) != 0;
+    const bool upper = (lane_id() & m) != 0;
 #pragma unroll
     for (int i = 0; i < HALF; ++i) {
         const double keep = upper ? v[HALF + i] : v[i];
@@ -80,325 +100,511 @@ __device__ __forceinline__ void rs_stage(double (&v)[CPT], int lane, int m, int&
     if (upper) colbase += HALF;
 }
 
-template <int CPT, bool MAX>
-__device__ __forceinline__ int reduce_scatter_cols(double (&v)[CPT]) {
-    const int lane = lane_id();
+// Reduce each of a thread's 16 column values over the row pairs of its
+// wavefront (the lanes that share its column chunk).  Afterwards each lane
+// holds 16 / (64 / CPR) reduced values in v[0..); their columns are
+// c0 + colbase + i.
+template <int CPR, bool MAX>
+__device__ __forceinline__ int reduce_rows_in_wave(double (&v)[16]) {
     int colbase = 0;
-    rs_stage<CPT, CPT, MAX>(v, lane, 4, colbase);
-    rs_stage<CPT, CPT / 2, MAX>(v, lane, 8, colbase);
-    rs_stage<CPT, CPT / 4, MAX>(v, lane, 16, colbase);
-    rs_stage<CPT, CPT / 8, MAX>(v, lane, 32, colbase);
+    if constexpr (CPR == 8) {  // row pairs on lane bits 3..5
+        rs_stage<16, MAX>(v, 8, colbase);
+        rs_stage<8, MAX>(v, 16, colbase);
+        rs_stage<4, MAX>(v, 32, colbase);
+    } else {  // CPR == 4: row pairs on lane bits 2..5
+        rs_stage<16, MAX>(v, 4, colbase);
+        rs_stage<8, MAX>(v, 8, colbase);
+        rs_stage<4, MAX>(v, 16, colbase);
+        rs_stage<2, MAX>(v, 32, colbase);
+    }
     return colbase;
+}
+
+__device__ __forceinline__ float pick4(const float4& f, int i) {
+    return i == 0 ? f.x : i == 1 ? f.y : i == 2 ? f.z : f.w;
 }
 
 }  // namespace
 
-template <int D, bool KDA, int MODE>
-__global__ __launch_bounds__(4 * D) void materialize_kernel(MatArgs a) {
-    constexpr int NT = 4 * D;
-    constexpr int CPT = D / 4;     // columns per thread
-    constexpr int NW = NT / kWave; // waves per workgroup
-    constexpr int EB = 16;         // buffered tokens staged per batch
-    constexpr int CPL = 2 * D / kWave;  // selection candidates per lane
-    static_assert(CPT % 16 == 0, "reduce-scatter needs 16 | CPT");
+// Units whose window is due, in ascending order, into the blob's work list.
+__global__ __launch_bounds__(1024) void due_scan_kernel(MatArgs a) {
+    __shared__ int wave_cnt[16];
+    __shared__ int base;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = lane_id();
+    if (tid == 0) base = 0;
+    __syncthreads();
+    for (int c0 = 0; c0 < a.dm.n_units; c0 += 1024) {
+        const int u = c0 + tid;
+        bool due = false;
+        if (u < a.dm.n_units) {
+            const int fill = a.blob.fill[u];
+            const int s = u / a.dm.n_v_heads;
+            due = fill >= a.dm.window || (a.force != nullptr && a.force[s] != 0 && fill > 0);
+        }
+        const uint64_t m = __ballot(due);
+        const int before =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (lane == 0) wave_cnt[wave] = __popcll(m);
+        __syncthreads();
+        int off = base;
+        for (int w = 0; w < wave; ++w) off += wave_cnt[w];
+        if (due) a.blob.work[1 + off + before] = u;
+        __syncthreads();
+        if (tid == 0) {
+            int t = 0;
+            for (int w = 0; w < 16; ++w) t += wave_cnt[w];
+            base += t;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) a.blob.work[0] = base;
+}
 
-    __shared__ double lds_k[EB][D];
+template <int D, bool KDA, int MODE>
+__global__ __launch_bounds__(D * D / 32) void materialize_kernel(MatArgs a) {
+    constexpr int CPR = D / 16;         // column chunks per row = threads per row pair
+    constexpr int NT = D * D / 32;      // threads
+    constexpr int NW = NT / kWave;      // wavefronts
+    constexpr int EB = 16;              // buffered tokens staged per batch
+    constexpr int KS = CPR * 18;        // padded FP64 length of one staged key (18 per 16-chunk)
+    constexpr int CPL = 2 * D / kWave;  // selection candidates per lane
+    constexpr int RPW = 64 / CPR;       // row pairs per wavefront
+    constexpr int NVAL = 16 / RPW;      // reduced column values per lane after reduce_rows_in_wave
+
+    __shared__ double lds_k[EB][KS];                        // key (scalar gate) or G' * key (channel gate)
+    __shared__ double lds_kd[KDA ? EB : 1][KDA ? KS : 1];  // key / G' (channel gate)
     __shared__ float lds_v[EB][D];
-    __shared__ float lds_g[KDA ? EB : 1][KDA ? D : 1];
+    __shared__ double lds_coef[EB][2];  // scalar gate: g', 1 / g'
     __shared__ float lds_b[EB];
-    __shared__ float lds_a[EB];
+    __shared__ int lds_resc[EB];        // scalar gate: fold g into T before this token
+    __shared__ double lds_G[KDA ? D : 1];     // channel gate: running G per column
+    __shared__ double lds_fold[KDA ? D : 1];  // channel gate: per-column fold factor of a batch
     __shared__ double lds_score[2 * D];
     __shared__ double lds_part[NW][D];
     __shared__ float lds_smooth[D];
     __shared__ int lds_slot[2 * D];  // slot + 1 of each selected candidate, 0 otherwise
     __shared__ int lds_chosen[16];
 
-    const int u = blockIdx.x;
     const int tid = threadIdx.x;
-    const int row = tid >> 2;
-    const int qd = tid & 3;
-    const int c0 = qd * CPT;
+    const int rp = tid / CPR;  // row pair
+    const int ch = tid % CPR;  // column chunk
+    const int r0 = 2 * rp;
+    const int c0 = ch * 16;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
     const int W = a.dm.window;
     const int nc = a.dm.n_comp;
-    const int s = u / a.dm.n_v_heads;
-    const int h = u - s * a.dm.n_v_heads;
-    const int kh = h / a.dm.group;
-    const size_t kvec = (size_t)s * a.dm.n_k_heads + kh;
 
-    int n_replay = 0;
-    if constexpr (MODE == kModeFlush) {
-        const int fill = a.blob.fill[u];
-        const bool forced = a.force != nullptr && a.force[s] != 0 && fill > 0;
-        if (!(fill >= W || forced)) return;  // not due: untouched (uniform per workgroup)
-        n_replay = fill < W ? fill : W;
-    } else if constexpr (MODE == kModeDequant) {
-        if (a.include_buffer) {
+    const int n_work = (MODE == kModeFlush) ? a.blob.work[0] : a.dm.n_units;
+    for (int wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
+        const int u = (MODE == kModeFlush) ? a.blob.work[1 + wi] : wi;
+        const int s = u / a.dm.n_v_heads;
+        const int h = u - s * a.dm.n_v_heads;
+        const int kh = h / a.dm.group;
+        const size_t kvec = (size_t)s * a.dm.n_k_heads + kh;
+
+        int n_replay = 0;
+        if (MODE == kModeFlush || (MODE == kModeDequant && a.include_buffer)) {
             const int fill = a.blob.fill[u];
             n_replay = fill < W ? fill : W;
         }
-    }
 
-    // ---------------- A: load the window-start state
-    double S[CPT];
-    if constexpr (MODE == kModeInit) {
-        if (a.S0 != nullptr) {
-            const float4* src = reinterpret_cast<const float4*>(a.S0 + ((size_t)u * D + row) * D + c0);
+        // ---------------- A: the window-start state, 2 rows x 16 columns per thread
+        double T[2][16];
+        if constexpr (MODE == kModeInit) {
 #pragma unroll
-            for (int t = 0; t < CPT / 4; ++t) {
-                const float4 f = src[t];
-                S[4 * t + 0] = f.x;
-                S[4 * t + 1] = f.y;
-                S[4 * t + 2] = f.z;
-                S[4 * t + 3] = f.w;
+            for (int rr = 0; rr < 2; ++rr) {
+                if (a.S0 != nullptr) {
+                    const float4* src =
+                        reinterpret_cast<const float4*>(a.S0 + ((size_t)u * D + r0 + rr) * D + c0);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float4 f = src[t];
+                        T[rr][4 * t + 0] = f.x;
+                        T[rr][4 * t + 1] = f.y;
+                        T[rr][4 * t + 2] = f.z;
+                        T[rr][4 * t + 3] = f.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) T[rr][c] = 0.0;
+                }
+            }
+        } else {
+            const float4* sp = reinterpret_cast<const float4*>(a.blob.smooth + (size_t)u * D + c0);
+            float4 s4[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s4[t] = sp[t];
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const double sgr = (double)a.blob.sigma[(size_t)u * D + r0 + rr];
+                const uint4 w = *reinterpret_cast<const uint4*>(a.blob.codes + ((size_t)u * D + r0 + rr) * D + c0);
+                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int b = 0; b < 16; ++b) {
+                    const int code = (int)(wd[b / 4] << (24 - 8 * (b % 4))) >> 24;
+                    T[rr][b] = sgr * (double)code * (double)pick4(s4[b / 4], b % 4);
+                }
+            }
+            for (int sl = 0; sl < nc; ++sl) {
+                const int idx = a.blob.comp_idx[(size_t)u * nc + sl];
+                const float* vec = a.blob.comp_vec + ((size_t)u * nc + sl) * D;
+                if (idx < D) {
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr)
+                        if (idx == r0 + rr) {
+#pragma unroll
+                            for (int c = 0; c < 16; ++c) T[rr][c] += (double)vec[c0 + c];
+                        }
+                } else {
+                    const int col = idx - D;
+                    if (col >= c0 && col < c0 + 16) {
+#pragma unroll
+                        for (int rr = 0; rr < 2; ++rr) {
+                            const double add = (double)vec[r0 + rr];
+#pragma unroll
+                            for (int c = 0; c < 16; ++c)
+                                if (c0 + c == col) T[rr][c] += add;
+                        }
+                    }
+                }
+            }
+        }
+
+        // ---------------- B: forward replay of the buffered tokens (FP64, rescaled)
+        const float* bk = a.blob.buf_k + kvec * (size_t)W * D;
+        const float* bv = a.blob.buf_v + (size_t)u * W * D;
+        const float* bb = a.blob.buf_beta + (size_t)u * W;
+        const float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
+        double gam = 1.0;  // scalar gate: running product g (uniform)
+        if constexpr (KDA) {
+            if (tid < D) lds_G[tid] = 1.0;
+        }
+        for (int i0 = 0; i0 < n_replay; i0 += EB) {
+            const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
+            __syncthreads();
+            if constexpr (KDA) {
+                // one thread per column walks the batch: fold G into T if it got
+                // small, then G' = G a and the key scaled both ways
+                if (tid < D) {
+                    const int c = tid;
+                    double G = lds_G[c];
+                    lds_fold[c] = (G < kRescaleBelow) ? G : 1.0;
+                    if (G < kRescaleBelow) G = 1.0;
+                    const int slot = (c / 16) * 18 + (c % 16);
+                    for (int e = 0; e < ne; ++e) {
+                        const double ag = fmax((double)bg[(size_t)(i0 + e) * D + c], kMinChannelGate);
+                        G *= ag;
+                        const double kc = (double)bk[(size_t)(i0 + e) * D + c];
+                        lds_k[e][slot] = G * kc;
+                        lds_kd[e][slot] = kc / G;
+                    }
+                    lds_G[c] = G;
+                }
+            } else {
+                for (int x = tid; x < ne * D; x += NT) {
+                    const int e = x / D, c = x - e * D;
+                    lds_k[e][(c / 16) * 18 + (c % 16)] = (double)bk[(size_t)(i0 + e) * D + c];
+                }
+                if (tid == 0) {
+                    double g = gam;
+                    for (int e = 0; e < ne; ++e) {
+                        const double al = (double)bg[i0 + e];
+                        const bool fold = g * al < kRescaleBelow;
+                        lds_resc[e] = fold ? 1 : 0;
+                        if (fold) g = 1.0;  // T takes the old product first
+                        g *= al;
+                        lds_coef[e][0] = g;
+                        lds_coef[e][1] = 1.0 / g;
+                    }
+                }
+            }
+            for (int x = tid; x < ne * D; x += NT) {
+                const int e = x / D, c = x - e * D;
+                lds_v[e][c] = bv[(size_t)(i0 + e) * D + c];
+            }
+            if (tid < ne) lds_b[tid] = bb[i0 + tid];
+            __syncthreads();
+            if constexpr (KDA) {
+                // fold this batch's per-column factors into T (rare)
+                bool any = false;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) any = any || (lds_fold[c0 + c] != 1.0);
+                if (any) {
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) {
+                        const double f = lds_fold[c0 + c];
+                        T[0][c] *= f;
+                        T[1][c] *= f;
+                    }
+                }
+            }
+            for (int e = 0; e < ne; ++e) {
+                double kk[16];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const double2 k2 = *reinterpret_cast<const double2*>(&lds_k[e][ch * 18 + 2 * t]);
+                    kk[2 * t] = k2.x;
+                    kk[2 * t + 1] = k2.y;
+                }
+                if constexpr (!KDA) {
+                    if (lds_resc[e]) {  // uniform: fold the gate product into T
+#pragma unroll
+                        for (int c = 0; c < 16; ++c) {
+                            T[0][c] *= gam;
+                            T[1][c] *= gam;
+                        }
+                    }
+                }
+                double d0a = 0.0, d0b = 0.0, d1a = 0.0, d1b = 0.0;
+#pragma unroll
+                for (int c = 0; c < 16; c += 2) {
+                    d0a = __builtin_fma(T[0][c], kk[c], d0a);
+                    d0b = __builtin_fma(T[0][c + 1], kk[c + 1], d0b);
+                    d1a = __builtin_fma(T[1][c], kk[c], d1a);
+                    d1b = __builtin_fma(T[1][c + 1], kk[c + 1], d1b);
+                }
+                const double d0 = group_sum<CPR>(d0a + d0b);
+                const double d1 = group_sum<CPR>(d1a + d1b);
+                const double be = (double)lds_b[e];
+                double k0, k1;
+                if constexpr (KDA) {
+                    k0 = be * ((double)lds_v[e][r0] - d0);
+                    k1 = be * ((double)lds_v[e][r0 + 1] - d1);
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const double2 k2 = *reinterpret_cast<const double2*>(&lds_kd[e][ch * 18 + 2 * t]);
+                        kk[2 * t] = k2.x;
+                        kk[2 * t + 1] = k2.y;
+                    }
+                } else {
+                    const double g = lds_coef[e][0], ig = lds_coef[e][1];
+                    gam = g;
+                    k0 = be * ((double)lds_v[e][r0] - g * d0) * ig;
+                    k1 = be * ((double)lds_v[e][r0 + 1] - g * d1) * ig;
+                }
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    T[0][c] = __builtin_fma(k0, kk[c], T[0][c]);
+                    T[1][c] = __builtin_fma(k1, kk[c], T[1][c]);
+                }
+            }
+        }
+        // back to S
+        if constexpr (KDA) {
+            __syncthreads();
+            if (n_replay > 0) {
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const double G = lds_G[c0 + c];
+                    T[0][c] *= G;
+                    T[1][c] *= G;
+                }
             }
         } else {
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) S[c] = 0.0;
-        }
-    } else {
-        const double sgr = (double)a.blob.sigma[(size_t)u * D + row];
-        const uint4* cp = reinterpret_cast<const uint4*>(a.blob.codes + ((size_t)u * D + row) * D + c0);
-        const float4* sp = reinterpret_cast<const float4*>(a.blob.smooth + (size_t)u * D + c0);
-#pragma unroll
-        for (int t = 0; t < CPT / 16; ++t) {
-            const uint4 w = cp[t];
-            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int b = 0; b < 16; ++b) {
-                const int code = (int)(wd[b / 4] << (24 - 8 * (b % 4))) >> 24;
-                const float4 s4 = sp[(16 * t + b) / 4];
-                const float sj = ((b % 4) == 0) ? s4.x : ((b % 4) == 1) ? s4.y : ((b % 4) == 2) ? s4.z : s4.w;
-                S[16 * t + b] = sgr * (double)code * (double)sj;
+            for (int c = 0; c < 16; ++c) {
+                T[0][c] *= gam;
+                T[1][c] *= gam;
             }
         }
-        for (int sl = 0; sl < nc; ++sl) {
-            const int idx = a.blob.comp_idx[(size_t)u * nc + sl];
-            const float* vec = a.blob.comp_vec + ((size_t)u * nc + sl) * D;
-            if (idx < D) {
-                if (idx == row) {
+
+        if constexpr (MODE == kModeDequant) {
 #pragma unroll
-                    for (int c = 0; c < CPT; ++c) S[c] += (double)vec[c0 + c];
-                }
-            } else {
-                const int col = idx - D;
-                if (col >= c0 && col < c0 + CPT) {
-                    const double add = (double)vec[row];
+            for (int rr = 0; rr < 2; ++rr) {
+                float4* dst = reinterpret_cast<float4*>(a.S_out + ((size_t)u * D + r0 + rr) * D + c0);
 #pragma unroll
-                    for (int c = 0; c < CPT; ++c)
-                        if (c0 + c == col) S[c] += add;
+                for (int t = 0; t < 4; ++t)
+                    dst[t] = make_float4((float)T[rr][4 * t], (float)T[rr][4 * t + 1], (float)T[rr][4 * t + 2],
+                                         (float)T[rr][4 * t + 3]);
+            }
+            __syncthreads();  // LDS is reused by the next unit
+            continue;
+        }
+
+        // ---------------- C1: line scores
+        {
+            double rs0 = 0.0, rs1 = 0.0;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                rs0 = __builtin_fma(T[0][c], T[0][c], rs0);
+                rs1 = __builtin_fma(T[1][c], T[1][c], rs1);
+            }
+            rs0 = group_sum<CPR>(rs0);
+            rs1 = group_sum<CPR>(rs1);
+            if (ch == 0) {
+                lds_score[r0] = rs0;
+                lds_score[r0 + 1] = rs1;
+            }
+            double sq[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) sq[c] = T[0][c] * T[0][c] + T[1][c] * T[1][c];
+            const int cb = reduce_rows_in_wave<CPR, false>(sq);
+#pragma unroll
+            for (int i = 0; i < NVAL; ++i) lds_part[wave][c0 + cb + i] = sq[i];
+            __syncthreads();
+            if (tid < D) {
+                double t = 0.0;
+                for (int w = 0; w < NW; ++w) t += lds_part[w][tid];
+                lds_score[D + tid] = t;
+            }
+            __syncthreads();
+        }
+
+        // ---------------- C2: top-n_comp selection (wavefront 0)
+        if (wave == 0) {
+            // scores are >= 0; a NaN score (non-finite input) ranks below every
+            // real one, and a lane with nothing left offers (-1, INT_MAX), which
+            // always loses, so every round picks one untaken candidate
+            double val[CPL];
+            bool taken[CPL];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const double sc = lds_score[lane * CPL + i];
+                val[i] = __builtin_isnan(sc) ? -0.5 : sc;
+                taken[i] = false;
+            }
+            for (int r = 0; r < nc; ++r) {
+                double bv_ = -1.0;
+                int bi = 0x7fffffff;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i)
+                    if (!taken[i] && val[i] > bv_) {
+                        bv_ = val[i];
+                        bi = lane * CPL + i;
+                    }
+                for (int m = 1; m < kWave; m <<= 1) {
+                    const double ov = shfl_xor_f64(bv_, m);
+                    const int oi = __shfl_xor(bi, m);
+                    if (ov > bv_ || (ov == bv_ && oi < bi)) {
+                        bv_ = ov;
+                        bi = oi;
+                    }
                 }
+#pragma unroll
+                for (int i = 0; i < CPL; ++i)
+                    if (bi == lane * CPL + i) taken[i] = true;
+                if (lane == 0) lds_chosen[r] = bi;
+            }
+            // slots in ascending candidate order (rows, then columns)
+            for (int x = lane; x < 2 * D; x += kWave) lds_slot[x] = 0;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane < nc) {
+                const int me = lds_chosen[lane];
+                int rank = 0;
+                for (int q2 = 0; q2 < nc; ++q2) rank += lds_chosen[q2] < me;
+                lds_slot[me] = rank + 1;
+                a.blob.comp_idx[(size_t)u * nc + rank] = me;
             }
         }
-    }
+        __syncthreads();
 
-    // ---------------- B: forward replay of the buffered tokens (FP64)
-    const float* bk = a.blob.buf_k + kvec * (size_t)W * D;
-    const float* bv = a.blob.buf_v + (size_t)u * W * D;
-    const float* bb = a.blob.buf_beta + (size_t)u * W;
-    const float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
-    for (int i0 = 0; i0 < n_replay; i0 += EB) {
-        const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
-        __syncthreads();
-        for (int x = tid; x < ne * D; x += NT) {
-            const int e = x / D, c = x - e * D;
-            lds_k[e][c] = (double)bk[(size_t)(i0 + e) * D + c];
-            lds_v[e][c] = bv[(size_t)(i0 + e) * D + c];
-            if constexpr (KDA) lds_g[e][c] = bg[(size_t)(i0 + e) * D + c];
-        }
-        if (tid < ne) {
-            lds_b[tid] = bb[i0 + tid];
-            if constexpr (!KDA) lds_a[tid] = bg[i0 + tid];
-        }
-        __syncthreads();
-        for (int e = 0; e < ne; ++e) {
-            double d = 0.0;
-            if constexpr (KDA) {
+        // ---------------- C3: extract compensator lines, zero them in the residual
+        {
+            float* cvb = a.blob.comp_vec + (size_t)u * nc * D;
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) {
-                    S[c] *= (double)lds_g[e][c0 + c];
-                    d = __builtin_fma(S[c], lds_k[e][c0 + c], d);
-                }
-            } else {
-                const double al = (double)lds_a[e];
+            for (int rr = 0; rr < 2; ++rr) {
+                const int rslot = lds_slot[r0 + rr];
+                if (rslot) {
+                    float4* dst = reinterpret_cast<float4*>(cvb + (size_t)(rslot - 1) * D + c0);
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) {
-                    S[c] *= al;
-                    d = __builtin_fma(S[c], lds_k[e][c0 + c], d);
+                    for (int t = 0; t < 4; ++t)
+                        dst[t] = make_float4((float)T[rr][4 * t], (float)T[rr][4 * t + 1], (float)T[rr][4 * t + 2],
+                                             (float)T[rr][4 * t + 3]);
                 }
             }
-            d = sum4_f64(d);
-            const double coef = (double)lds_b[e] * ((double)lds_v[e][row] - d);
+            const int rs0 = lds_slot[r0], rs1 = lds_slot[r0 + 1];
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) S[c] = __builtin_fma(coef, lds_k[e][c0 + c], S[c]);
-        }
-    }
-
-    if constexpr (MODE == kModeDequant) {
-        float4* dst = reinterpret_cast<float4*>(a.S_out + ((size_t)u * D + row) * D + c0);
-#pragma unroll
-        for (int t = 0; t < CPT / 4; ++t)
-            dst[t] = make_float4((float)S[4 * t], (float)S[4 * t + 1], (float)S[4 * t + 2], (float)S[4 * t + 3]);
-        return;
-    }
-
-    // ---------------- C1: line scores
-    {
-        double rs = 0.0;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) rs = __builtin_fma(S[c], S[c], rs);
-        rs = sum4_f64(rs);
-        if (qd == 0) lds_score[row] = rs;
-        double sq[CPT];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) sq[c] = S[c] * S[c];
-        const int cb = reduce_scatter_cols<CPT, false>(sq);
-#pragma unroll
-        for (int i = 0; i < CPT / 16; ++i) lds_part[wave][c0 + cb + i] = sq[i];
-        __syncthreads();
-        if (tid < D) {
-            double t = 0.0;
-            for (int w = 0; w < NW; ++w) t += lds_part[w][tid];
-            lds_score[D + tid] = t;
-        }
-        __syncthreads();
-    }
-
-    // ---------------- C2: top-n_comp selection (wave 0)
-    if (wave == 0) {
-        // scores are >= 0; a NaN score (non-finite input) ranks below every
-        // real one, and a lane with nothing left offers (-1, INT_MAX), which
-        // always loses, so every round picks one untaken candidate
-        double val[CPL];
-        bool taken[CPL];
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const double sc = lds_score[lane * CPL + i];
-            val[i] = __builtin_isnan(sc) ? -0.5 : sc;
-            taken[i] = false;
-        }
-        for (int r = 0; r < nc; ++r) {
-            double bv_ = -1.0;
-            int bi = 0x7fffffff;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i)
-                if (!taken[i] && val[i] > bv_) {
-                    bv_ = val[i];
-                    bi = lane * CPL + i;
+            for (int c = 0; c < 16; ++c) {
+                const int cs = lds_slot[D + c0 + c];
+                if (cs) {
+                    cvb[(size_t)(cs - 1) * D + r0] = rs0 ? 0.0f : (float)T[0][c];
+                    cvb[(size_t)(cs - 1) * D + r0 + 1] = rs1 ? 0.0f : (float)T[1][c];
+                    T[0][c] = 0.0;
+                    T[1][c] = 0.0;
                 }
-            for (int m = 1; m < kWave; m <<= 1) {
-                const double ov = shfl_xor_f64(bv_, m);
-                const int oi = __shfl_xor(bi, m);
-                if (ov > bv_ || (ov == bv_ && oi < bi)) {
-                    bv_ = ov;
-                    bi = oi;
+                if (rs0) T[0][c] = 0.0;
+                if (rs1) T[1][c] = 0.0;
+            }
+        }
+
+        // ---------------- C4: smoothing per key channel
+        {
+            double am[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) am[c] = fmax(fabs(T[0][c]), fabs(T[1][c]));
+            const int cb = reduce_rows_in_wave<CPR, true>(am);
+#pragma unroll
+            for (int i = 0; i < NVAL; ++i) lds_part[wave][c0 + cb + i] = am[i];
+            __syncthreads();
+            if (tid < D) {
+                double m = 0.0;
+                for (int w = 0; w < NW; ++w) m = fmax(m, lds_part[w][tid]);
+                const float sj = m > 0.0 ? (float)sqrt(m) : 1.0f;
+                lds_smooth[tid] = sj;
+                a.blob.smooth[(size_t)u * D + tid] = sj;
+            }
+            __syncthreads();
+        }
+
+        // ---------------- C5: per-row scale and codes
+        {
+            double sj[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) sj[c] = (double)lds_smooth[c0 + c];
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                double m = 0.0;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) m = fmax(m, fabs(T[rr][c] / sj[c]));
+                m = group_max<CPR>(m);
+                const float sg = (float)(m / 127.0);
+                if (ch == 0) a.blob.sigma[(size_t)u * D + r0 + rr] = sg;
+                uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    int code = 0;
+                    if (sg != 0.0f) {
+                        double x = rint(T[rr][c] / ((double)sg * sj[c]));
+                        x = fmin(fmax(x, -127.0), 127.0);
+                        code = (int)x;
+                    }
+                    packed[c / 4] |= ((uint32_t)code & 0xFFu) << (8 * (c % 4));
                 }
+                *reinterpret_cast<uint4*>(a.blob.codes + ((size_t)u * D + r0 + rr) * D + c0) =
+                    make_uint4(packed[0], packed[1], packed[2], packed[3]);
             }
-#pragma unroll
-            for (int i = 0; i < CPL; ++i)
-                if (bi == lane * CPL + i) taken[i] = true;
-            if (lane == 0) lds_chosen[r] = bi;
         }
-        // slots in ascending candidate order (rows, then columns)
-        for (int x = lane; x < 2 * D; x += kWave) lds_slot[x] = 0;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < nc) {
-            const int me = lds_chosen[lane];
-            int rank = 0;
-            for (int q2 = 0; q2 < nc; ++q2) rank += lds_chosen[q2] < me;
-            lds_slot[me] = rank + 1;
-            a.blob.comp_idx[(size_t)u * nc + rank] = me;
+        if (tid == 0) {
+            a.blob.fill[u] = 0;
+            if (MODE == kModeInit && u == 0) *a.blob.status = 0u;
         }
-    }
-    __syncthreads();
-
-    // ---------------- C3: extract compensator lines, zero them in the residual
-    {
-        const int rslot = lds_slot[row];
-        float* cvb = a.blob.comp_vec + (size_t)u * nc * D;
-        if (rslot) {
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) cvb[(size_t)(rslot - 1) * D + c0 + c] = (float)S[c];
-        }
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int cs = lds_slot[D + c0 + c];
-            if (cs) {
-                cvb[(size_t)(cs - 1) * D + row] = rslot ? 0.0f : (float)S[c];
-                S[c] = 0.0;
-            }
-            if (rslot) S[c] = 0.0;
-        }
-    }
-
-    // ---------------- C4: smoothing per key channel
-    {
-        double am[CPT];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) am[c] = fabs(S[c]);
-        const int cb = reduce_scatter_cols<CPT, true>(am);
-#pragma unroll
-        for (int i = 0; i < CPT / 16; ++i) lds_part[wave][c0 + cb + i] = am[i];
-        __syncthreads();
-        if (tid < D) {
-            double m = 0.0;
-            for (int w = 0; w < NW; ++w) m = fmax(m, lds_part[w][tid]);
-            const float sj = m > 0.0 ? (float)sqrt(m) : 1.0f;
-            lds_smooth[tid] = sj;
-            a.blob.smooth[(size_t)u * D + tid] = sj;
-        }
-        __syncthreads();
-    }
-
-    // ---------------- C5: per-row scale and codes
-    {
-        double sj[CPT];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) sj[c] = (double)lds_smooth[c0 + c];
-        double m = 0.0;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) m = fmax(m, fabs(S[c] / sj[c]));
-        m = max4_f64(m);
-        const float sg = (float)(m / 127.0);
-        if (qd == 0) a.blob.sigma[(size_t)u * D + row] = sg;
-        uint32_t packed[CPT / 4];
-#pragma unroll
-        for (int w = 0; w < CPT / 4; ++w) packed[w] = 0;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            int code = 0;
-            if (sg != 0.0f) {
-                double x = rint(S[c] / ((double)sg * sj[c]));
-                x = fmin(fmax(x, -127.0), 127.0);
-                code = (int)x;
-            }
-            packed[c / 4] |= ((uint32_t)code & 0xFFu) << (8 * (c % 4));
-        }
-        uint4* dst = reinterpret_cast<uint4*>(a.blob.codes + ((size_t)u * D + row) * D + c0);
-#pragma unroll
-        for (int t = 0; t < CPT / 16; ++t)
-            dst[t] = make_uint4(packed[4 * t], packed[4 * t + 1], packed[4 * t + 2], packed[4 * t + 3]);
-    }
-    if (tid == 0) {
-        a.blob.fill[u] = 0;
-        if (MODE == kModeInit && u == 0) *a.blob.status = 0u;
+        __syncthreads();  // LDS is reused by the next unit
     }
 }
 
 __global__ void clear_status_kernel(uint32_t* status) { *status = 0u; }
 
 hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, hipStream_t st) {
-    const dim3 grid(a.dm.n_units), block(4 * d);
+    // a fixed grid walks the units (init, dequant) or the work list (flush)
+    const int grid_cap = 2048;
+    const dim3 grid(a.dm.n_units < grid_cap ? a.dm.n_units : grid_cap), block(d * d / 32);
     const bool kda = gate_kind == LQ_GATE_CHANNEL;
+    if (mode == kModeFlush) {
+        hipLaunchKernelGGL(due_scan_kernel, dim3(1), dim3(1024), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
 #define LQ_MAT(D_, K_, M_) hipLaunchKernelGGL((materialize_kernel<D_, K_, M_>), grid, block, 0, st, a)
-#define LQ_MAT_MODE(D_, K_)                              \
-    do {                                                 \
-        if (mode == kModeInit) LQ_MAT(D_, K_, kModeInit);       \
+#define LQ_MAT_MODE(D_, K_)                                      \
+    do {                                                         \
+        if (mode == kModeInit) LQ_MAT(D_, K_, kModeInit);        \
         else if (mode == kModeFlush) LQ_MAT(D_, K_, kModeFlush); \
-        else LQ_MAT(D_, K_, kModeDequant);                \
+        else LQ_MAT(D_, K_, kModeDequant);                       \
     } while (0)
     if (d == 128) {
         if (kda) LQ_MAT_MODE(128, true);

@@ -39,6 +39,7 @@ inline void compute_layout(const lq_config& c, lq_layout& L) {
     L.buf_v = take(U * W * c.d_v * sizeof(float));
     L.buf_beta = take(U * W * sizeof(float));
     L.buf_gate = take(U * W * (c.gate_kind == LQ_GATE_CHANNEL ? c.d_k : 1) * sizeof(float));
+    L.work = take((U + 1) * sizeof(int32_t));
     L.total_bytes = off;
 }
 
@@ -55,6 +56,7 @@ struct BlobPtrs {
     float* buf_v;
     float* buf_beta;
     float* buf_gate;
+    int32_t* work;  // [0] = count, [1..] = units due at the window boundary
 };
 
 inline BlobPtrs blob_ptrs(void* base, const lq_layout& L) {
@@ -71,6 +73,7 @@ inline BlobPtrs blob_ptrs(void* base, const lq_layout& L) {
     p.buf_v = (float*)(b + L.buf_v);
     p.buf_beta = (float*)(b + L.buf_beta);
     p.buf_gate = (float*)(b + L.buf_gate);
+    p.work = (int32_t*)(b + L.work);
     return p;
 }
 
@@ -183,6 +186,16 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, i.e. waits for every outstanding store of the wave to be
+// acknowledged, which costs microseconds when the wave has just written the
+// window buffer; exchanges through LDS do not need that.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 }  // namespace lq
 #endif

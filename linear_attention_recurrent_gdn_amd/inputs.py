@@ -95,8 +95,9 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
-def _rng(wl: Workload, layer: int, phase: int, t: int, tensor: str) -> np.random.Generator:
-    ss = np.random.SeedSequence([wl.seed, layer, phase, t, _TENSOR_IDS[tensor]])
+def _rng(wl: Workload, layer: int, phase: int, t: int, tensor: str,
+         per_unit: bool = False) -> np.random.Generator:
+    ss = np.random.SeedSequence([wl.seed, layer, phase, int(per_unit), t, _TENSOR_IDS[tensor]])
     return np.random.Generator(np.random.PCG64(ss))
 
 
@@ -131,32 +132,44 @@ def tokens(wl: Workload, t0: int, n: int, phase: int = PHASE_DECODE, layer: int 
     return {key: np.stack([tk[key] for tk in toks]) for key in toks[0]} if toks else None
 
 
-def prefill_stream(wl: Workload, unit: int, layer: int = 0) -> Dict[str, np.ndarray]:
-    """Prefill tokens of one unit: k [P, d], v [P, d], beta [P], gate [P] or [P, d].
+def unit_stream(wl: Workload, unit: int, n: int, phase: int = PHASE_PREFILL, layer: int = 0,
+                with_queries: bool = False) -> Dict[str, np.ndarray]:
+    """``n`` tokens of one unit: k [n, d], v [n, d], beta [n], gate [n] or [n, d]
+    (and q [n, d] with ``with_queries``).
 
-    Keyed per unit (k per (sequence, key head), so the value heads of one key
-    head share it), so any subset of units can be generated on its own.
-    Prefill needs no queries (no outputs are read).
+    Keyed per unit (q and k per (sequence, key head), so the value heads of
+    one key head share them), so any subset of units can be generated on its
+    own.  Prefill needs no queries (no outputs are read).
     """
     if wl.projected:
-        raise ValueError("projected workloads prefill through projected_token()")
-    P, d = wl.prefill, wl.d
+        raise ValueError("projected workloads draw inputs through projected_token()")
+    d = wl.d
     s, h = divmod(unit, wl.n_v_heads)
     key_id = s * wl.n_k_heads + h // wl.group
-    k = _l2_normalise(_rng(wl, layer, PHASE_PREFILL, key_id, "k").standard_normal((P, d), np.float32))
-    rv = _rng(wl, layer, PHASE_PREFILL, unit, "v")
-    v = (rv.standard_t(3, size=(P, d)).astype(np.float32) if wl.v_dist == "t3"
-         else rv.standard_normal((P, d), np.float32))
-    beta = _rng(wl, layer, PHASE_PREFILL, unit, "beta").uniform(0.0, 1.0, P).astype(np.float32)
-    gshape = (P,) if wl.gate == "scalar" else (P, d)
-    gate = _rng(wl, layer, PHASE_PREFILL, unit, "gate").uniform(wl.gate_lo, wl.gate_hi, gshape).astype(
+    k = _l2_normalise(_rng(wl, layer, phase, key_id, "k", True).standard_normal((n, d), np.float32))
+    rv = _rng(wl, layer, phase, unit, "v", True)
+    v = (rv.standard_t(3, size=(n, d)).astype(np.float32) if wl.v_dist == "t3"
+         else rv.standard_normal((n, d), np.float32))
+    beta = _rng(wl, layer, phase, unit, "beta", True).uniform(0.0, 1.0, n).astype(np.float32)
+    gshape = (n,) if wl.gate == "scalar" else (n, d)
+    gate = _rng(wl, layer, phase, unit, "gate", True).uniform(wl.gate_lo, wl.gate_hi, gshape).astype(
         np.float32)
-    return {"k": k, "v": v, "beta": beta, "gate": gate}
+    out = {"k": k, "v": v, "beta": beta, "gate": gate}
+    if with_queries:
+        out["q"] = _l2_normalise(_rng(wl, layer, phase, key_id, "q", True).standard_normal((n, d), np.float32))
+    return out
 
 
-def prefill_streams(wl: Workload, units, layer: int = 0) -> Dict[str, np.ndarray]:
-    """Token-major prefill inputs of several units: k [P, n, d], v [P, n, d], ..."""
-    per = [prefill_stream(wl, int(u), layer) for u in units]
+def prefill_stream(wl: Workload, unit: int, layer: int = 0) -> Dict[str, np.ndarray]:
+    """The prefill tokens of one unit (see ``unit_stream``)."""
+    return unit_stream(wl, unit, wl.prefill, PHASE_PREFILL, layer)
+
+
+def prefill_streams(wl: Workload, units, layer: int = 0, n: Optional[int] = None,
+                    phase: int = PHASE_PREFILL, with_queries: bool = False) -> Dict[str, np.ndarray]:
+    """Token-major per-unit streams of several units: k [n, U', d], v [n, U', d], ..."""
+    n = wl.prefill if n is None else n
+    per = [unit_stream(wl, int(u), n, phase, layer, with_queries) for u in units]
     return {key: np.ascontiguousarray(np.stack([p[key] for p in per], axis=1)) for key in per[0]}
 
 
@@ -164,7 +177,7 @@ def surrogate_state(wl: Workload, units, layer: int = 0, scale: float = 0.5) -> 
     """Gaussian stand-in start states [n, d, d] for units whose outputs are not checked."""
     out = np.empty((len(units), wl.d, wl.d), np.float32)
     for i, u in enumerate(units):
-        out[i] = _rng(wl, layer, PHASE_PREFILL, int(u), "hidden").standard_normal(
+        out[i] = _rng(wl, layer, PHASE_PREFILL, int(u), "hidden", True).standard_normal(
             (wl.d, wl.d), np.float32) * np.float32(scale)
     return out
 

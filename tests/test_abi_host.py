@@ -53,7 +53,7 @@ def test_layout_sections_aligned_and_disjoint(lib):
             "status": 4, "fill": 4 * U, "codes": U * D * D, "sigma": 4 * U * D,
             "smooth": 4 * U * D, "comp_idx": 4 * U * nc, "comp_vec": 4 * U * nc * D,
             "buf_k": 4 * c.n_seq * c.n_k_heads * W * D, "buf_v": 4 * U * W * D,
-            "buf_beta": 4 * U * W, "buf_gate": 4 * U * W * g,
+            "buf_beta": 4 * U * W, "buf_gate": 4 * U * W * g, "work": 4 * (U + 1),
         }
         spans = sorted((L[k], L[k] + n, k) for k, n in sizes.items())
         for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
