@@ -4,13 +4,16 @@
 One step = one decode token for every (sequence, head) unit of every layer
 (lq_decode_step), plus the window-boundary requantization (lq_window_flush)
 for every unit whose window filled on that token.  Inputs are synthetic,
-seeded, and resident in HBM before the timed region starts.  The same steps
-are then timed on the FP32-state comparison kernel.
+seeded, and resident in HBM before the timed region starts.  The timed steps
+are captured as one HIP graph and replayed between HIP events, so the host's
+launch cost is not in the figure.  The same steps are then timed on the
+FP32-state comparison kernel.
 
 Prints one JSON line:
   value            unit-tokens/s (seq·head·tokens/s) of the INT8 path over the timed steps
   roofline         the decode kernel's algorithmic bytes per launch / its average
-                   launch time (HIP events around every launch), against 8 TB/s
+                   launch time (a graph of one window of decode launches, HIP events
+                   around the replay), against 8 TB/s
   fp32_state       the FP32-state kernel on the same steps, and the speedup
   cpu_baseline     the CPU oracle (FP64, definitional windowed form) on a bounded
                    sample of the same workload, on this host's cores
@@ -42,8 +45,6 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-fp32", action="store_true", help="skip the FP32-state comparison loop")
-    ap.add_argument("--no-launch-events", action="store_true",
-                    help="no per-launch events inside the timed loop (roofline omitted)")
     return ap.parse_args()
 
 
@@ -141,10 +142,13 @@ def cpu_baseline(wl, n_tok, target_s):
     orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp)
     rate = len(cal_units) * cal_tok / max(time.perf_counter() - t0, 1e-6)
     n_units = int(max(1, min(wl.n_units, rate * target_s / n_tok)))
+    # the whole workload may take well under target_s: repeat it to get a steady figure
+    reps = int(max(1, min(20, round(rate * target_s / (n_units * n_tok)))))
     units = np.linspace(0, wl.n_units - 1, n_units).astype(int)
     S0, st = sample(units, n_tok)
     t0 = time.perf_counter()
-    orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp)
+    for _ in range(reps):
+        orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp)
     dt = time.perf_counter() - t0
     cpu_model = ""
     try:
@@ -153,11 +157,11 @@ def cpu_baseline(wl, n_tok, target_s):
     except Exception:
         pass
     return {
-        "value": n_units * n_tok / dt,
+        "value": reps * n_units * n_tok / dt,
         "unit": "seq·head·tokens/s",
         "cores": orc.num_threads(),
         "kind": "oracle",
-        "sample": (f"{n_units} of {wl.n_units} units x {n_tok} decode tokens (flushes included), "
+        "sample": (f"{n_units} of {wl.n_units} units x {n_tok} decode tokens (flushes included) x {reps} passes, "
                    f"FP64 definitional windowed form, {dt:.1f} s; input generation excluded; "
                    f"host CPU: {cpu_model}"),
     }
@@ -233,20 +237,12 @@ def main():
     sched = I.stagger_schedule(wl)
     fill = np.zeros(wl.n_seq, np.int64)
     force_dev = torch.zeros(wl.n_seq, dtype=torch.uint8, device=dev)
-    decode_events, flush_events, decode_js = [], [], []
+    flush_calls = []
 
-    def int8_step(t, timed):
-        events = timed and not args.no_launch_events
+    def int8_step(t):
         for layer in range(L):
             tk = toks[layer][t]
-            if events:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
             lq.lq_decode_step(cfg, states[layer], tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
-            if events:
-                b.record(stream)
-                decode_events.append((a, b))
-                decode_js.append(fill.copy())
         fill[:] += 1
         forced = (sched == t) if (sched is not None and t < warmup) else np.zeros(wl.n_seq, bool)
         due = (fill >= W) | (forced & (fill > 0))
@@ -256,25 +252,29 @@ def main():
                 force_dev.copy_(torch.from_numpy(forced.astype(np.uint8)))
                 fm = force_dev
             for layer in range(L):
-                if events:
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
                 lq.lq_window_flush(cfg, states[layer], fm)
-                if events:
-                    b.record(stream)
-                    flush_events.append((a, b, int(due.sum()) * wl.n_v_heads, fill[due].copy()))
+            flush_calls.append(int(due.sum()) * wl.n_v_heads)
             fill[due] = 0
 
+    def timed_graph(body):
+        """Capture body() as one HIP graph, replay it once between events (ms)."""
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
     for t in range(warmup):
-        int8_step(t, False)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for t in range(warmup, n_tok):
-        int8_step(t, True)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    int8_ms = e0.elapsed_time(e1)
+        int8_step(t)
+    n_flush_warm = len(flush_calls)
+    # the timed steps run as one graph: kernels back to back, no host launch cost
+    int8_ms = timed_graph(lambda: [int8_step(t) for t in range(warmup, n_tok)])
     flags = [lq.lq_read_status(cfg, st) for st in states]
     if any(flags):
         raise RuntimeError(f"device flags set during the run: {flags}")
@@ -299,44 +299,54 @@ def main():
             "d_k": d, "d_v": d, "gate": wl.gate, "window": W, "n_comp": wl.n_comp,
             "prefill": wl.prefill, "units": U * L,
         },
+        "timing": "HIP graph replay of the timed steps, HIP events around the replay",
     }
 
-    if decode_events:
-        durs = np.array([a.elapsed_time(b) for a, b in decode_events]) * 1e-3  # s
-        byts = np.array([sum(decode_bytes(wl, int(j)) * wl.n_v_heads for j in js) for js in decode_js],
-                        dtype=np.float64)
-        achieved = byts.mean() / durs.mean() / 1e9
-        result["roofline"] = {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(wl.name),
-            "kernel": "decode_int8_kernel",
-            "avg_launch_us": durs.mean() * 1e6,
-            "alg_bytes_per_launch": byts.mean(),
-        }
-        if flush_events:
-            fd = np.array([a.elapsed_time(b) for a, b, _, _ in flush_events]) * 1e-3
-            result["flush"] = {"launches": len(flush_events), "avg_launch_us": fd.mean() * 1e6,
-                               "units_flushed_per_launch": float(np.mean([n for _, _, n, _ in flush_events]))}
+    # ---- the decode kernel alone over one whole window (every unit at j = 0 .. W-1),
+    # replayed as a graph: its average launch time against its algorithmic bytes
+    all_seq = torch.ones(wl.n_seq, dtype=torch.uint8, device=dev)
+    for layer in range(L):
+        lq.lq_window_flush(cfg, states[layer], all_seq)  # forced: every window restarts empty
+    win_tok = [t % n_tok for t in range(W)]
+    dec_ms = timed_graph(lambda: [lq.lq_decode_step(cfg, states[layer], toks[layer][t]["q"], toks[layer][t]["k"],
+                                                    toks[layer][t]["v"], toks[layer][t]["beta"],
+                                                    toks[layer][t]["gate"], o)
+                                  for t in win_tok for layer in range(L)])
+    n_launch = W * L
+    avg_launch_s = dec_ms * 1e-3 / n_launch
+    avg_bytes = float(np.mean([decode_bytes(wl, j) for j in range(W)])) * U
+    achieved = avg_bytes / avg_launch_s / 1e9
+    result["roofline"] = {
+        "bound": "hbm",
+        "achieved": achieved,
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": achieved / HBM_PEAK_GBS,
+        "traffic": measured_traffic(wl.name),
+        "kernel": "decode_int8_kernel",
+        "avg_launch_us": avg_launch_s * 1e6,
+        "alg_bytes_per_launch": avg_bytes,
+        "launches": n_launch,
+        "note": "one graph of one window of decode launches (j = 0..W-1), events around the replay",
+    }
+    # flush alone: one forced boundary of every unit after a full window
+    fl_ms = timed_graph(lambda: [lq.lq_window_flush(cfg, states[layer], None) for layer in range(L)])
+    result["flush"] = {
+        "avg_launch_us": fl_ms * 1e3 / L,
+        "units_per_launch": U,
+        "tokens_replayed": W,
+        "timed_steps_flushes": len(flush_calls) - n_flush_warm,
+    }
 
     if not args.no_fp32:
-        for t in range(warmup):
-            for layer in range(L):
-                tk = toks[layer][t]
-                lq.lq_fp32_decode_step(cfg, S_fp32[layer], tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
-        torch.cuda.synchronize()
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        f0.record(stream)
-        for t in range(warmup, n_tok):
-            for layer in range(L):
-                tk = toks[layer][t]
-                lq.lq_fp32_decode_step(cfg, S_fp32[layer], tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
-        f1.record(stream)
-        torch.cuda.synchronize()
-        fp32_ms = f0.elapsed_time(f1)
+        def fp32_steps(t_from, t_to):
+            for t in range(t_from, t_to):
+                for layer in range(L):
+                    tk = toks[layer][t]
+                    lq.lq_fp32_decode_step(cfg, S_fp32[layer], tk["q"], tk["k"], tk["v"], tk["beta"],
+                                           tk["gate"], o)
+        fp32_steps(0, warmup)
+        fp32_ms = timed_graph(lambda: fp32_steps(warmup, n_tok))
         fp32_bytes = U * L * (8 * d * d + 4 * (2 * d // wl.group + 2 * d + 1 + (d if wl.gate == "channel" else 1)))
         result["fp32_state"] = {
             "value": U * L * steps / (fp32_ms * 1e-3),

@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import ctypes
 import dataclasses
+import functools
 import os
 from typing import Dict, Optional
 
@@ -163,6 +164,7 @@ def _sizes(cfg: Config) -> Dict[str, int]:
 # entry points (names as in lq.h)
 # ---------------------------------------------------------------------------
 
+@functools.lru_cache(maxsize=256)
 def lq_state_bytes(cfg: Config) -> int:
     n = ctypes.c_size_t(0)
     _check("lq_state_bytes", load_library().lq_state_bytes(ctypes.byref(cfg.c()), ctypes.byref(n)))
