@@ -66,7 +66,34 @@ class Report:
     decode_calls: int = 0
 
 
-def start_states(wl: I.Workload, checked: np.ndarray, layer: int = 0) -> np.ndarray:
+class TokenSource:
+    """Decode and prefill inputs of one layer of a workload (numpy, library layouts)."""
+
+    def __init__(self, wl: I.Workload, layer: int = 0, device="cuda"):
+        self.wl, self.layer, self.device = wl, layer, device
+        self.weights = I.projection_weights(wl, layer) if wl.projected else None
+        if self.weights is not None:
+            self.weights = {k: torch.as_tensor(v, device=device).to(torch.bfloat16)
+                            for k, v in self.weights.items()}
+
+    def token(self, t: int, phase: int = I.PHASE_DECODE):
+        if self.wl.projected:
+            h = I.hidden_state(self.wl, self.layer, t, phase)
+            return I.projected_token(self.wl, self.weights, h, self.device)
+        return I.token(self.wl, t, phase, self.layer)
+
+    def prefill(self, units):
+        """Token-major prefill inputs of ``units`` (k, v, beta, gate; per-unit layout)."""
+        wl = self.wl
+        if not wl.projected:
+            return I.prefill_streams(wl, units, self.layer)
+        toks = [I.tokens_per_unit(wl, {k: v[None] for k, v in self.token(t, I.PHASE_PREFILL).items()})
+                for t in range(wl.prefill)]
+        return {key: np.ascontiguousarray(np.concatenate([tk[key] for tk in toks])[:, units])
+                for key in ("k", "v", "beta", "gate")}
+
+
+def start_states(wl: I.Workload, checked: np.ndarray, layer: int = 0, src: "TokenSource" = None) -> np.ndarray:
     """fp32 [U, d, d]: oracle prefill for checked units, stand-ins elsewhere."""
     U, d = wl.n_units, wl.d
     S0 = np.zeros((U, d, d), np.float32)
@@ -74,7 +101,7 @@ def start_states(wl: I.Workload, checked: np.ndarray, layer: int = 0) -> np.ndar
     if len(others):
         S0[others] = I.surrogate_state(wl, others, layer)
     if wl.prefill > 0 and len(checked):
-        st = I.prefill_streams(wl, checked, layer)
+        st = (src or TokenSource(wl, layer)).prefill(checked)
         S, _ = orc.recurrence(np.zeros((len(checked), d, d)), None, st["k"], st["v"], st["beta"],
                               st["gate"], want_outputs=False)
         S0[checked] = S.astype(np.float32)
@@ -140,7 +167,8 @@ def run(wl: I.Workload, n_tokens: Optional[int] = None, checked: Optional[Sequen
     print(f"[parity] {wl.name}: units={U} checked={len(checked)} d={d} W={W} n_c={nc} "
           f"tokens={n_tokens}", flush=True)
 
-    S0 = start_states(wl, checked, layer)
+    src = TokenSource(wl, layer, device)
+    S0 = start_states(wl, checked, layer, src)
     state = lq.new_state(cfg, device)
     views = lq.state_views(cfg, state)
     lq.lq_state_init(cfg, state, torch.from_numpy(S0).to(device))
@@ -156,19 +184,20 @@ def run(wl: I.Workload, n_tokens: Optional[int] = None, checked: Optional[Sequen
     sched = I.stagger_schedule(wl)
     o_dev = torch.empty((wl.n_seq, wl.n_v_heads, d), dtype=torch.float32, device=device)
     S_out = torch.empty((U, d, d), dtype=torch.float32, device=device)
+    chk_dev = torch.as_tensor(checked, device=device, dtype=torch.long)
     frozen = None
     for t in range(n_tokens):
-        tk = I.token(wl, t, I.PHASE_DECODE, layer)
+        tk = src.token(t)
         dev = {k_: torch.from_numpy(v_).to(device) for k_, v_ in tk.items()}
         if frozen is None:
             frozen = {k_: views[k_].clone() for k_ in ("codes", "sigma", "smooth", "comp_idx", "comp_vec")}
         lq.lq_decode_step(cfg, state, dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], o_dev)
-        o_gpu = o_dev.view(U, d).cpu().numpy()
+        o_chk = o_dev.view(U, d).index_select(0, chk_dev).cpu().numpy()
         pu = I.tokens_per_unit(wl, {k_: v_[None] for k_, v_ in tk.items()})
         sel = lambda a: np.ascontiguousarray(a[:, checked])
         S_hat, o_ref = orc.recurrence(S_hat, sel(pu["q"]), sel(pu["k"]), sel(pu["v"]), sel(pu["beta"]),
                                       sel(pu["gate"]))
-        err = rel_l2(o_gpu[checked], o_ref[0])
+        err = rel_l2(o_chk, o_ref[0])
         assert err <= TOL_OUT, f"{wl.name}: decode token {t}: output rel-L2 {err}"
         rep.max_out_err = max(rep.max_out_err, err)
         rep.decode_calls += 1
@@ -179,9 +208,9 @@ def run(wl: I.Workload, n_tokens: Optional[int] = None, checked: Optional[Sequen
 
         if dequant_every and (t % dequant_every == dequant_every - 1):
             lq.lq_dequant_state(cfg, state, S_out, include_buffer=True)
-            e1 = rel_l2(S_out.cpu().numpy()[checked], S_hat)
+            e1 = rel_l2(S_out.index_select(0, chk_dev).cpu().numpy(), S_hat)
             lq.lq_dequant_state(cfg, state, S_out, include_buffer=False)
-            e0 = rel_l2(S_out.cpu().numpy()[checked], orc.dequant(blob_host(views, checked)))
+            e0 = rel_l2(S_out.index_select(0, chk_dev).cpu().numpy(), orc.dequant(blob_host(views, checked)))
             assert max(e0, e1) <= TOL_STATE, f"{wl.name}: dequantized state at token {t}: {e0}, {e1}"
             rep.max_state_err = max(rep.max_state_err, e0, e1)
 
