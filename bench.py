@@ -21,7 +21,6 @@ Prints one JSON line:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -171,17 +170,14 @@ def cpu_baseline(wl, n_tok, target_s):
 # measured HBM traffic (rocprofv3 --pmc), valid only for the kernel it was taken on
 # ---------------------------------------------------------------------------
 
-def kernel_sha() -> str:
-    p = os.path.join(ROOT, "linear_attention_recurrent_gdn_amd", "csrc", "lq_decode.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
-
-
 def measured_traffic(workload):
     p = os.path.join(ROOT, "profiles", f"decode_int8_{workload}_traffic.json")
     try:
         rec = json.load(open(p))
     except Exception:
         return None
+    from linear_attention_recurrent_gdn_amd.profiling import kernel_sha
+
     if rec.get("kernel_sha") != kernel_sha():
         return None
     return rec.get("hbm_bytes_per_launch")

@@ -1,0 +1,189 @@
+"""Measurement helpers around rocprofv3 (no part of the decode path).
+
+Three commands:
+
+  window   --workload W
+      Runs, eagerly on cuda:0, one plain device-to-device copy of COPY_BYTES
+      (the calibration kernel for the memory counters), then one whole window
+      of decode launches (every unit at fill j = 0 .. W-1) on a freshly
+      initialised state.  Meant to run under ``rocprofv3 --pmc FETCH_SIZE``
+      and, in a second run, ``--pmc WRITE_SIZE``.
+
+  traffic  --workload W --fetch DIR --write DIR --out FILE
+      Reads the two counter_collection.csv files, scales the decode kernel's
+      per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) by the factor that makes the
+      copy read and write exactly COPY_BYTES, and writes the per-launch HBM
+      bytes averaged over the window, keyed by a hash of the decode kernel's
+      source (a changed kernel invalidates the figure).
+
+  stats    --csv FILE --cmd "..." --out FILE
+      Formats a ``rocprofv3 --stats`` kernel_stats.csv as a short text
+      summary headed by the command that produced it.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30
+DECODE_KERNEL = "decode_int8_kernel"
+COPY_KERNEL = "copyBuffer"
+
+
+def kernel_sha() -> str:
+    """Short hash of the decode kernel's source file."""
+    with open(os.path.join(HERE, "csrc", "lq_decode.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def run_window(workload: str) -> None:
+    import torch
+
+    import linear_attention_recurrent_gdn_amd as lq
+    from linear_attention_recurrent_gdn_amd import inputs as I
+
+    lq.load_library()
+    wl = I.WORKLOADS[workload]
+    U, d, W = wl.n_units, wl.d, wl.window
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(dev).manual_seed(2000 + wl.seed)
+    cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind)
+
+    src = torch.empty(COPY_BYTES // 4, device=dev).normal_(generator=gen)
+    dst = torch.empty_like(src)
+    state = lq.new_state(cfg, dev)
+    S0 = torch.randn((U, d, d), generator=gen, device=dev) * 0.5
+    lq.lq_state_init(cfg, state, S0)
+    del S0
+    if wl.projected:
+        from bench import projected, projection_weights  # input synthesis only
+
+        w = projection_weights(wl, gen, dev)
+        toks = [projected(wl, w, torch.randn((wl.n_seq, wl.hidden), generator=gen, device=dev)
+                          .to(torch.bfloat16)) for _ in range(W)]
+    else:
+        toks = [I.torch_token(wl, gen, dev) for _ in range(W)]
+    o = torch.empty((wl.n_seq, wl.n_v_heads, d), device=dev)
+    torch.cuda.synchronize()
+    print(f"[window] {workload}: copy of {COPY_BYTES} B", flush=True)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[window] {workload}: {W} decode launches over {U} units", flush=True)
+    for t in range(W):
+        tk = toks[t]
+        lq.lq_decode_step(cfg, state, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+    torch.cuda.synchronize()
+    flags = lq.lq_read_status(cfg, state)
+    print(f"[window] done, flags={flags:#x}", flush=True)
+    if flags:
+        sys.exit(1)
+
+
+def _counter_rows(path_or_dir: str, counter: str):
+    paths = [path_or_dir] if os.path.isfile(path_or_dir) else \
+        glob.glob(os.path.join(path_or_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no counter_collection.csv under {path_or_dir}")
+    rows = []
+    for p in paths:
+        with open(p) as f:
+            rows += [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+    return rows
+
+
+def _per_dispatch(rows, name_part):
+    by = {}
+    for r in rows:
+        if name_part in r["Kernel_Name"]:
+            key = int(r["Dispatch_Id"])
+            by[key] = by.get(key, 0.0) + float(r["Counter_Value"])
+    return [by[k] for k in sorted(by)]
+
+
+def traffic(workload: str, fetch_dir: str, write_dir: str, out: str, cmd: str) -> dict:
+    from linear_attention_recurrent_gdn_amd import inputs as I
+
+    wl = I.WORKLOADS[workload]
+    res = {}
+    for tag, counter, path in (("fetch", "FETCH_SIZE", fetch_dir), ("write", "WRITE_SIZE", write_dir)):
+        rows = _counter_rows(path, counter)
+        # the runtime's own small copies (status reads) use the same blit kernel:
+        # the calibration copy is the largest one
+        copy = max(_per_dispatch(rows, COPY_KERNEL), default=0.0)
+        dec = _per_dispatch(rows, DECODE_KERNEL)
+        if copy <= 0 or len(dec) != wl.window:
+            raise SystemExit(f"{counter}: expected a copy and {wl.window} decode dispatches, "
+                             f"found copy={copy} and {len(dec)}")
+        factor = (COPY_BYTES / 1024.0) / copy
+        res[tag] = {"copy_kib": copy, "factor": factor,
+                    "decode_kib_per_launch_raw": sum(dec) / len(dec),
+                    "decode_bytes_per_launch": factor * 1024.0 * sum(dec) / len(dec),
+                    "first_last_kib_raw": [dec[0], dec[-1]]}
+    rec = {
+        "kernel": DECODE_KERNEL,
+        "workload": workload,
+        "kernel_sha": kernel_sha(),
+        "launches": wl.window,
+        "hbm_bytes_per_launch": res["fetch"]["decode_bytes_per_launch"] + res["write"]["decode_bytes_per_launch"],
+        "fetch": res["fetch"],
+        "write": res["write"],
+        "calibration": f"one device copy of {COPY_BYTES} B read and written in the same run",
+        "command": cmd,
+    }
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
+def stats(csv_path: str, cmd: str, out: str) -> None:
+    with open(csv_path) as f:
+        rows = list(csv.DictReader(f))
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {cmd}", "#",
+             f"# {'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10} {'pct':>6}  kernel"]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 90:
+            name = name[:87] + "..."
+        lines.append(f"  {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e6:10.3f} "
+                     f"{float(r['Percentage']):6.2f}  {name}")
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("window")
+    a.add_argument("--workload", default="gdn_decode")
+    b = sub.add_parser("traffic")
+    b.add_argument("--workload", default="gdn_decode")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--out", required=True)
+    b.add_argument("--command", default="")
+    c = sub.add_parser("stats")
+    c.add_argument("--csv", required=True)
+    c.add_argument("--command", default="")
+    c.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+    if args.cmd == "window":
+        run_window(args.workload)
+    elif args.cmd == "traffic":
+        print(json.dumps(traffic(args.workload, args.fetch, args.write, args.out, args.command), indent=1))
+    else:
+        stats(args.csv, args.command, args.out)
+
+
+if __name__ == "__main__":
+    sys.path.insert(0, os.path.dirname(HERE))
+    main()
