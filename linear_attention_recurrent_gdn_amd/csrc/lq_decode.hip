@@ -231,14 +231,21 @@ __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeArgs a) {
                 float p = 0.f;
                 for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(w.e[e], r.e[e], p);
                 const float dot = wave_sum(p);
-                for (int e = 0; e < EPL; ++e)
-                    if (lane * EPL + e == idx) acc.e[e] += dot;
+                // a select per element: an indexed update here would make the
+                // compiler move acc to LDS addressed by the flat thread id, which
+                // costs every workgroup a read of the dispatch packet
+                for (int e = 0; e < EPL; ++e) acc.e[e] += (lane * EPL + e == idx) ? dot : 0.f;
             } else {
                 const int col = idx - D;
-                float rsel = r.e[0];
-                if constexpr (EPL == 2) rsel = (col & 1) ? r.e[1] : r.e[0];
-                const float rc = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rsel), col / EPL));
+                // read each element from the owning lane, then choose: selecting
+                // r.e[col % EPL] first would index a private array dynamically
+                float rc = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.e[0]), col / EPL));
+                if constexpr (EPL == 2) {
+                    const float rc1 = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r.e[1]), col / EPL));
+                    rc = (col & 1) ? rc1 : rc;
+                }
                 for (int e = 0; e < EPL; ++e) acc.e[e] = __builtin_fmaf(w.e[e], rc, acc.e[e]);
             }
         };
