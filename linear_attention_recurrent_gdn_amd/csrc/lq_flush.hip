@@ -124,6 +124,37 @@ __device__ __forceinline__ float pick4(const float4& f, int i) {
     return i == 0 ? f.x : i == 1 ? f.y : i == 2 ? f.z : f.w;
 }
 
+// One batch of buffered tokens as fetched by one thread of the materialize
+// kernel: F4 float4 of the batch's keys, values and channel gates (token-major,
+// D floats per token), and, for the first threads, one beta and scalar gate.
+template <int F4, bool KDA>
+struct Stage {
+    float4 k[F4], v[F4], g[KDA ? F4 : 1];
+    float b, al;
+};
+
+template <int D, int EB, int NT, int F4, bool KDA>
+__device__ __forceinline__ Stage<F4, KDA> fetch_stage(const float* bk, const float* bv, const float* bb,
+                                                     const float* bg, int i0, int n_replay, int tid) {
+    Stage<F4, KDA> st;
+    const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
+#pragma unroll
+    for (int f = 0; f < F4; ++f) {
+        const int x = 4 * (tid + f * NT);
+        const int e = min(x / D, ne - 1), c = x % D;
+        st.k[f] = *reinterpret_cast<const float4*>(bk + (size_t)(i0 + e) * D + c);
+        st.v[f] = *reinterpret_cast<const float4*>(bv + (size_t)(i0 + e) * D + c);
+        if constexpr (KDA) st.g[f] = *reinterpret_cast<const float4*>(bg + (size_t)(i0 + e) * D + c);
+    }
+    st.b = 0.f;
+    st.al = 1.f;
+    if (tid < EB) {
+        st.b = bb[i0 + min(tid, ne - 1)];
+        if constexpr (!KDA) st.al = bg[i0 + min(tid, ne - 1)];
+    }
+    return st;
+}
+
 }  // namespace
 
 // Units whose window is due, in ascending order, into the blob's work list.
@@ -167,15 +198,19 @@ __global__ __launch_bounds__(D * D / 32) void materialize_kernel(MatArgs a) {
     constexpr int CPR = D / 16;         // column chunks per row = threads per row pair
     constexpr int NT = D * D / 32;      // threads
     constexpr int NW = NT / kWave;      // wavefronts
-    constexpr int EB = 16;              // buffered tokens staged per batch
+    constexpr int EB = D == 128 ? 16 : 8;  // buffered tokens staged per batch (one float4 per thread)
     constexpr int KS = CPR * 18;        // padded FP64 length of one staged key (18 per 16-chunk)
     constexpr int CPL = 2 * D / kWave;  // selection candidates per lane
     constexpr int RPW = 64 / CPR;       // row pairs per wavefront
     constexpr int NVAL = 16 / RPW;      // reduced column values per lane after reduce_rows_in_wave
+    constexpr int F4 = EB * D / (4 * NT);  // float4 of a staged batch per thread
 
     __shared__ double lds_k[EB][KS];                        // key (scalar gate) or G' * key (channel gate)
     __shared__ double lds_kd[KDA ? EB : 1][KDA ? KS : 1];  // key / G' (channel gate)
     __shared__ float lds_v[EB][D];
+    __shared__ float lds_kraw[KDA ? EB : 1][KDA ? D : 1];  // channel gate: keys as fetched
+    __shared__ float lds_graw[KDA ? EB : 1][KDA ? D : 1];  // channel gate: gates as fetched
+    __shared__ float lds_al[KDA ? 1 : EB];                  // scalar gate: gates as fetched
     __shared__ double lds_coef[EB][2];  // scalar gate: g', 1 / g'
     __shared__ float lds_b[EB];
     __shared__ int lds_resc[EB];        // scalar gate: fold g into T before this token
@@ -184,6 +219,7 @@ __global__ __launch_bounds__(D * D / 32) void materialize_kernel(MatArgs a) {
     __shared__ double lds_score[2 * D];
     __shared__ double lds_part[NW][D];
     __shared__ float lds_smooth[D];
+    __shared__ double lds_ismooth[D];
     __shared__ int lds_slot[2 * D];  // slot + 1 of each selected candidate, 0 otherwise
     __shared__ int lds_chosen[16];
 
@@ -248,26 +284,41 @@ __global__ __launch_bounds__(D * D / 32) void materialize_kernel(MatArgs a) {
                     T[rr][b] = sgr * (double)code * (double)pick4(s4[b / 4], b % 4);
                 }
             }
-            for (int sl = 0; sl < nc; ++sl) {
-                const int idx = a.blob.comp_idx[(size_t)u * nc + sl];
-                const float* vec = a.blob.comp_vec + ((size_t)u * nc + sl) * D;
-                if (idx < D) {
+            // compensator lines, four slots at a time: every load of a group is
+            // issued before any is used (row slots use the 16 columns of this
+            // thread, column slots the entries of its two rows)
+            for (int sl0 = 0; sl0 < nc; sl0 += 4) {
+                int idx[4];
+                float4 rowv[4][4];
+                float colv[4][2];
 #pragma unroll
-                    for (int rr = 0; rr < 2; ++rr)
-                        if (idx == r0 + rr) {
+                for (int q = 0; q < 4; ++q) {
+                    const int sl = min(sl0 + q, nc - 1);
+                    idx[q] = a.blob.comp_idx[(size_t)u * nc + sl];
+                    const float* vec = a.blob.comp_vec + ((size_t)u * nc + sl) * D;
 #pragma unroll
-                            for (int c = 0; c < 16; ++c) T[rr][c] += (double)vec[c0 + c];
-                        }
-                } else {
-                    const int col = idx - D;
-                    if (col >= c0 && col < c0 + 16) {
+                    for (int t = 0; t < 4; ++t) rowv[q][t] = reinterpret_cast<const float4*>(vec + c0)[t];
+                    colv[q][0] = vec[r0];
+                    colv[q][1] = vec[r0 + 1];
+                }
 #pragma unroll
-                        for (int rr = 0; rr < 2; ++rr) {
-                            const double add = (double)vec[r0 + rr];
+                for (int q = 0; q < 4; ++q) {
+                    if (sl0 + q >= nc) break;
+                    if (idx[q] < D) {
 #pragma unroll
-                            for (int c = 0; c < 16; ++c)
-                                if (c0 + c == col) T[rr][c] += add;
-                        }
+                        for (int rr = 0; rr < 2; ++rr)
+                            if (idx[q] == r0 + rr) {
+#pragma unroll
+                                for (int c = 0; c < 16; ++c) T[rr][c] += (double)pick4(rowv[q][c / 4], c % 4);
+                            }
+                    } else {
+                        const int col = idx[q] - D;
+#pragma unroll
+                        for (int c = 0; c < 16; ++c)
+                            if (c0 + c == col) {
+                                T[0][c] += (double)colv[q][0];
+                                T[1][c] += (double)colv[q][1];
+                            }
                     }
                 }
             }
@@ -282,9 +333,38 @@ __global__ __launch_bounds__(D * D / 32) void materialize_kernel(MatArgs a) {
         if constexpr (KDA) {
             if (tid < D) lds_G[tid] = 1.0;
         }
+        // A batch's keys, values (and channel gates) are fetched into registers
+        // one batch ahead, F4 float4 per thread, every load independent of the
+        // others; tokens past the end of the window repeat the last one and are
+        // never used.
+        Stage<F4, KDA> pf{};
+        if (n_replay > 0) pf = fetch_stage<D, EB, NT, F4, KDA>(bk, bv, bb, bg, 0, n_replay, tid);
         for (int i0 = 0; i0 < n_replay; i0 += EB) {
             const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
+            __syncthreads();  // the previous batch is done with LDS
+#pragma unroll
+            for (int f = 0; f < F4; ++f) {
+                const int x = 4 * (tid + f * NT);
+                const int e = x / D, c = x % D;
+                *reinterpret_cast<float4*>(&lds_v[e][c]) = pf.v[f];
+                if constexpr (KDA) {
+                    *reinterpret_cast<float4*>(&lds_kraw[e][c]) = pf.k[f];
+                    *reinterpret_cast<float4*>(&lds_graw[e][c]) = pf.g[f];
+                } else {
+                    double* dk = &lds_k[e][(c / 16) * 18 + (c % 16)];
+                    dk[0] = pf.k[f].x;
+                    dk[1] = pf.k[f].y;
+                    dk[2] = pf.k[f].z;
+                    dk[3] = pf.k[f].w;
+                }
+            }
+            if (tid < EB) {
+                lds_b[tid] = pf.b;
+                if constexpr (!KDA) lds_al[tid] = pf.al;
+            }
             __syncthreads();
+            if (i0 + EB < n_replay)  // in flight during this batch
+                pf = fetch_stage<D, EB, NT, F4, KDA>(bk, bv, bb, bg, i0 + EB, n_replay, tid);
             if constexpr (KDA) {
                 // one thread per column walks the batch: fold G into T if it got
                 // small, then G' = G a and the key scaled both ways
@@ -295,37 +375,35 @@ __global__ __launch_bounds__(D * D / 32) void materialize_kernel(MatArgs a) {
                     if (G < kRescaleBelow) G = 1.0;
                     const int slot = (c / 16) * 18 + (c % 16);
                     for (int e = 0; e < ne; ++e) {
-                        const double ag = fmax((double)bg[(size_t)(i0 + e) * D + c], kMinChannelGate);
+                        const double ag = fmax((double)lds_graw[e][c], kMinChannelGate);
                         G *= ag;
-                        const double kc = (double)bk[(size_t)(i0 + e) * D + c];
+                        const double kc = (double)lds_kraw[e][c];
                         lds_k[e][slot] = G * kc;
                         lds_kd[e][slot] = kc / G;
                     }
                     lds_G[c] = G;
                 }
             } else {
-                for (int x = tid; x < ne * D; x += NT) {
-                    const int e = x / D, c = x - e * D;
-                    lds_k[e][(c / 16) * 18 + (c % 16)] = (double)bk[(size_t)(i0 + e) * D + c];
-                }
+                // the running gate product, token by token (thread 0), then its
+                // reciprocals in parallel (wavefront 0)
                 if (tid == 0) {
                     double g = gam;
                     for (int e = 0; e < ne; ++e) {
-                        const double al = (double)bg[i0 + e];
+                        const double al = (double)lds_al[e];
                         const bool fold = g * al < kRescaleBelow;
                         lds_resc[e] = fold ? 1 : 0;
                         if (fold) g = 1.0;  // T takes the old product first
                         g *= al;
                         lds_coef[e][0] = g;
-                        lds_coef[e][1] = 1.0 / g;
                     }
                 }
+                if (wave == 0) {
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    if (lane < ne) lds_coef[lane][1] = 1.0 / lds_coef[lane][0];
+                }
             }
-            for (int x = tid; x < ne * D; x += NT) {
-                const int e = x / D, c = x - e * D;
-                lds_v[e][c] = bv[(size_t)(i0 + e) * D + c];
-            }
-            if (tid < ne) lds_b[tid] = bb[i0 + tid];
             __syncthreads();
             if constexpr (KDA) {
                 // fold this batch's per-column factors into T (rare)
@@ -546,6 +624,7 @@ __global__ __launch_bounds__(D * D / 32) void materialize_kernel(MatArgs a) {
                 for (int w = 0; w < NW; ++w) m = fmax(m, lds_part[w][tid]);
                 const float sj = m > 0.0 ? (float)sqrt(m) : 1.0f;
                 lds_smooth[tid] = sj;
+                lds_ismooth[tid] = 1.0 / (double)sj;
                 a.blob.smooth[(size_t)u * D + tid] = sj;
             }
             __syncthreads();
@@ -553,23 +632,27 @@ __global__ __launch_bounds__(D * D / 32) void materialize_kernel(MatArgs a) {
 
         // ---------------- C5: per-row scale and codes
         {
-            double sj[16];
+            // divisions by s_j and sigma_i s_j as products with FP64 reciprocals
+            // (a few ulps of FP64 off the quotient; the codes round at 2^-10 of
+            // a tie or closer only by chance either way)
+            double isj[16];
 #pragma unroll
-            for (int c = 0; c < 16; ++c) sj[c] = (double)lds_smooth[c0 + c];
+            for (int c = 0; c < 16; ++c) isj[c] = lds_ismooth[c0 + c];
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
                 double m = 0.0;
 #pragma unroll
-                for (int c = 0; c < 16; ++c) m = fmax(m, fabs(T[rr][c] / sj[c]));
+                for (int c = 0; c < 16; ++c) m = fmax(m, fabs(T[rr][c] * isj[c]));
                 m = group_max<CPR>(m);
                 const float sg = (float)(m / 127.0);
                 if (ch == 0) a.blob.sigma[(size_t)u * D + r0 + rr] = sg;
+                const double isg = sg != 0.0f ? 1.0 / (double)sg : 0.0;
                 uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
                     int code = 0;
                     if (sg != 0.0f) {
-                        double x = rint(T[rr][c] / ((double)sg * sj[c]));
+                        double x = rint(T[rr][c] * (isg * isj[c]));
                         x = fmin(fmax(x, -127.0), 127.0);
                         code = (int)x;
                     }
