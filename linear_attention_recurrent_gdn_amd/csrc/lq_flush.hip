@@ -13,24 +13,31 @@
 // then runs on a fixed grid that walks that list, so a boundary that concerns
 // a few units does not launch a workgroup per unit.
 //
-// Materialize: one workgroup per unit at a time, each thread holding 2 rows x
-// 16 columns of the state in FP64 registers (a row is split over D/16
-// consecutive lanes):
+// Materialize: one workgroup of D/16 wavefronts per unit at a time.  The
+// FP64 state lives in the accumulator layout of the FP64 matrix instruction
+// v_mfma_f64_16x16x4f64 (lane l, register r of a 16x16 result holds row
+// 4r + l/16, column l%16): wavefront w owns rows n = 16w + (l % 16) and lane
+// l holds, for every 16-column block b, the 4 consecutive columns
+// 16b + 4(l/16) .. +3 of its row, as the 16x16 block b of S^T.
 //   A  load: S = Diag(sigma) Q Diag(s) + compensator lines (flush, dequant) or
 //      the caller's FP32 start state (init);
 //   B  forward replay of the buffered tokens in FP64 (FP64 so that the
-//      rounding decisions below match an FP64 reference), in a rescaled form
-//      that costs two FMAs per element and token:
-//        scalar gate  S = g T:  g' = g alpha;  d = T[i,:].k;
-//                     T[i,:] += beta (v_i - g' d) / g' * k
-//        channel gate S = T Diag(G):  G' = G * a;  d = T[i,:].(G' * k);
-//                     T[i,:] += beta (v_i - d) * (k / G')
-//      (a token-by-token restatement of x = g * S[i,:]; S[i,:] = x + beta
-//      (v_i - x.k) k).  g and G are folded into T before they can
-//      underflow.  The key (and for the channel gate its two scaled forms) is
-//      staged through LDS as FP64, a batch of tokens at a time, with a padded
-//      layout so the D/16 column chunks that a wavefront reads at once fall in
-//      different LDS banks;
+//      rounding decisions below match an FP64 reference), 16 tokens per
+//      chunk, in a rescaled form (scalar gate S = g T, channel gate
+//      S = T Diag(G); g and G are folded into T at a chunk start before they
+//      can underflow, gates are floored at 2^-45).  With kf_e, kb_e the
+//      token's key scaled forward and back (k, k for the scalar gate;
+//      G_e k, k / G_e for the channel gate) and v'_e = v_e / g_e (scalar) or
+//      v_e, the token-by-token replay
+//          d_e = T kf_e;  T += beta_e (v'_e - d_e) kb_e^T
+//      is, for a whole chunk,
+//          A = T Kf^T;  C = (v' - A) Diag(beta) M^T;  T += C Kb
+//      with L_ee' = kf_e . kb_e' (e' < e) and M = (I + Diag(beta) L)^-1,
+//      a unit lower-triangular 16x16 matrix shared by all rows.  Both
+//      d_v x d_k x 16 products and C run on the FP64 matrix cores; L is
+//      assembled from per-wavefront partial products over column slices, and
+//      M is solved by forward substitution in one wavefront while the others
+//      form A;
 //   C  quantizer, in the same workgroup (readings; the pages print no
 //      formula): line scores = squared L2 norms of rows and columns; the
 //      n_comp best lines (ties to the lower candidate index, rows before
@@ -39,9 +46,10 @@
 //      zeroed; s_j = sqrt(max_i |R_ij|) (1 if zero), sigma_i =
 //      max_j |R_ij / s_j| / 127, both fp32; codes = clamp(rne(R_ij /
 //      (sigma_i s_j)), -127, 127).
-// Column reductions go lane-to-lane inside a wavefront (reduce-scatter over
-// its row pairs), then across wavefronts through LDS in a fixed order, so
-// results are deterministic.
+// Row reductions combine the four lanes that share a row (permlane swaps);
+// column reductions reduce-scatter over the 16 lanes of a row group, then
+// combine the wavefronts through LDS in a fixed order, so results are
+// deterministic.
 
 #include "lq_internal.h"
 
@@ -49,8 +57,15 @@ namespace lq {
 
 namespace {
 
-constexpr double kRescaleBelow = 0x1p-200;   // fold the gate product into T below this
-constexpr double kMinChannelGate = 0x1p-45;  // per-token channel gate floor inside the flush
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+constexpr double kRescaleBelow = 0x1p-200;  // fold the gate product into T below this
+constexpr double kMinGate = 0x1p-45;        // per-token gate floor inside the flush
+constexpr int kDppRowRor8 = 0x128;          // row_ror:8
+
+__device__ __forceinline__ v4d mfma(double a, double b, v4d c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
 
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
@@ -60,20 +75,62 @@ __device__ __forceinline__ double dpp_f64(double x) {
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-// Sum / max over groups of N consecutive lanes (N = 4 or 8), result in every lane.
-template <int N>
-__device__ __forceinline__ double group_sum(double x) {
-    if constexpr (N == 8) x += dpp_f64<kDppRowHalfMirror>(x);
-    x += dpp_f64<kDppQuadXor2>(x);
-    x += dpp_f64<kDppQuadXor1>(x);
+// Combine the four lanes that share a row (lanes m, m+16, m+32, m+48).
+template <bool MAX>
+__device__ __forceinline__ double across_rows(double x) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const uint64_t b = __builtin_bit_cast(uint64_t, x);
+        const int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
+        int l0, l1, h0, h1;
+        if (s == 0) {
+            const auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+            const auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+            l0 = pl[0]; l1 = pl[1]; h0 = ph[0]; h1 = ph[1];
+        } else {
+            const auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+            const auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+            l0 = pl[0]; l1 = pl[1]; h0 = ph[0]; h1 = ph[1];
+        }
+        const double a = __builtin_bit_cast(double, ((uint64_t)(uint32_t)h0 << 32) | (uint32_t)l0);
+        const double c = __builtin_bit_cast(double, ((uint64_t)(uint32_t)h1 << 32) | (uint32_t)l1);
+        x = MAX ? fmax(a, c) : a + c;
+    }
     return x;
 }
-template <int N>
-__device__ __forceinline__ double group_max(double x) {
-    if constexpr (N == 8) x = fmax(x, dpp_f64<kDppRowHalfMirror>(x));
-    x = fmax(x, dpp_f64<kDppQuadXor2>(x));
-    x = fmax(x, dpp_f64<kDppQuadXor1>(x));
-    return x;
+
+// One reduce-scatter stage over the first N entries of v among the 16 lanes
+// of a row group: the lane and its DPP partner keep one half each (the upper
+// half where `up`) and combine the partner's copy of it.
+template <int N, int CTRL, bool MAX, int M>
+__device__ __forceinline__ void rs_stage(double (&v)[M], bool up) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+        const double send = up ? v[i] : v[i + N / 2];
+        const double keep = up ? v[i + N / 2] : v[i];
+        const double got = dpp_f64<CTRL>(send);
+        v[i] = MAX ? fmax(keep, got) : keep + got;
+    }
+}
+
+// Column reduction of NV = 4 * NB values (value 4b + r = column 16b + 4q + r)
+// over the 16 lanes of a row group.  Afterwards lane m holds NV / 16 totals in
+// v[0..), for the values returned + i; every value is held by exactly one lane.
+template <int NV, bool MAX>
+__device__ __forceinline__ int reduce_columns(double (&v)[NV], int m) {
+    static_assert(NV == 32 || NV == 16, "4 or 8 column blocks");
+    // stage 1: every lane holds every value, so any pairing works (mirror in 8)
+    rs_stage<NV, kDppRowHalfMirror, MAX>(v, (m & 4) != 0);
+    rs_stage<NV / 2, kDppQuadXor1, MAX>(v, (m & 1) != 0);
+    rs_stage<NV / 4, kDppQuadXor2, MAX>(v, (m & 2) != 0);
+    if constexpr (NV == 32) {
+        rs_stage<4, kDppRowRor8, MAX>(v, (m & 8) != 0);
+        return 16 * ((m >> 2) & 1) + 8 * (m & 1) + 4 * ((m >> 1) & 1) + 2 * ((m >> 3) & 1);
+    } else {
+        // 2 values left per lane after three stages: the ror:8 pair splits them
+        rs_stage<2, kDppRowRor8, MAX>(v, (m & 8) != 0);
+        return 8 * ((m >> 2) & 1) + 4 * (m & 1) + 2 * ((m >> 1) & 1) + ((m >> 3) & 1);
+    }
 }
 
 __device__ __forceinline__ double shfl_xor_f64(double x, int m) {
@@ -84,68 +141,30 @@ __device__ __forceinline__ double shfl_xor_f64(double x, int m) {
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-// One reduce-scatter stage over lane bit m: keep half of the N values, add
-// (or max) the partner's copy of that half.
-template <int N, bool MAX>
-__device__ __forceinline__ void rs_stage(double (&v)[16], int m, int& colbase) {
-    constexpr int HALF = N / 2;
-    const bool upper = (lane_id() & m) != 0;
-#pragma unroll
-    for (int i = 0; i < HALF; ++i) {
-        const double keep = upper ? v[HALF + i] : v[i];
-        const double send = upper ? v[i] : v[HALF + i];
-        const double got = shfl_xor_f64(send, m);
-        v[i] = MAX ? fmax(keep, got) : keep + got;
-    }
-    if (upper) colbase += HALF;
-}
-
-// Reduce each of a thread's 16 column values over the row pairs of its
-// wavefront (the lanes that share its column chunk).  Afterwards each lane
-// holds 16 / (64 / CPR) reduced values in v[0..); their columns are
-// c0 + colbase + i.
-template <int CPR, bool MAX>
-__device__ __forceinline__ int reduce_rows_in_wave(double (&v)[16]) {
-    int colbase = 0;
-    if constexpr (CPR == 8) {  // row pairs on lane bits 3..5
-        rs_stage<16, MAX>(v, 8, colbase);
-        rs_stage<8, MAX>(v, 16, colbase);
-        rs_stage<4, MAX>(v, 32, colbase);
-    } else {  // CPR == 4: row pairs on lane bits 2..5
-        rs_stage<16, MAX>(v, 4, colbase);
-        rs_stage<8, MAX>(v, 8, colbase);
-        rs_stage<4, MAX>(v, 16, colbase);
-        rs_stage<2, MAX>(v, 32, colbase);
-    }
-    return colbase;
-}
-
 __device__ __forceinline__ float pick4(const float4& f, int i) {
     return i == 0 ? f.x : i == 1 ? f.y : i == 2 ? f.z : f.w;
 }
 
-// One batch of buffered tokens as fetched by one thread of the materialize
-// kernel: F4 float4 of the batch's keys, values and channel gates (token-major,
-// D floats per token), and, for the first threads, one beta and scalar gate.
-template <int F4, bool KDA>
+// One chunk of buffered tokens as fetched by one thread: one float4 of the
+// chunk's keys, values and channel gates (token-major, D floats per token)
+// and, for the first 16 threads, one beta and scalar gate.
+template <bool KDA>
 struct Stage {
-    float4 k[F4], v[F4], g[KDA ? F4 : 1];
+    float4 k, v, g;
     float b, al;
 };
 
-template <int D, int EB, int NT, int F4, bool KDA>
-__device__ __forceinline__ Stage<F4, KDA> fetch_stage(const float* bk, const float* bv, const float* bb,
-                                                     const float* bg, int i0, int n_replay, int tid) {
-    Stage<F4, KDA> st;
+template <int D, int NT, bool KDA>
+__device__ __forceinline__ Stage<KDA> fetch_stage(const float* bk, const float* bv, const float* bb,
+                                                 const float* bg, int i0, int n_replay, int tid) {
+    constexpr int EB = 16;
+    Stage<KDA> st;
     const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
-#pragma unroll
-    for (int f = 0; f < F4; ++f) {
-        const int x = 4 * (tid + f * NT);
-        const int e = min(x / D, ne - 1), c = x % D;
-        st.k[f] = *reinterpret_cast<const float4*>(bk + (size_t)(i0 + e) * D + c);
-        st.v[f] = *reinterpret_cast<const float4*>(bv + (size_t)(i0 + e) * D + c);
-        if constexpr (KDA) st.g[f] = *reinterpret_cast<const float4*>(bg + (size_t)(i0 + e) * D + c);
-    }
+    const int x = 4 * tid;
+    const int e = min(x / D, ne - 1), c = x % D;
+    st.k = *reinterpret_cast<const float4*>(bk + (size_t)(i0 + e) * D + c);
+    st.v = *reinterpret_cast<const float4*>(bv + (size_t)(i0 + e) * D + c);
+    if constexpr (KDA) st.g = *reinterpret_cast<const float4*>(bg + (size_t)(i0 + e) * D + c);
     st.b = 0.f;
     st.al = 1.f;
     if (tid < EB) {
@@ -156,6 +175,502 @@ __device__ __forceinline__ Stage<F4, KDA> fetch_stage(const float* bk, const flo
 }
 
 }  // namespace
+
+template <int D, bool KDA, int MODE>
+__global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) {
+    constexpr int NW = D / 16;          // wavefronts = 16-row groups
+    constexpr int NT = kWave * NW;      // threads
+    constexpr int NB = D / 16;          // 16-column blocks
+    constexpr int NV = 4 * NB;          // state values per lane
+    constexpr int EB = 16;              // buffered tokens per chunk
+    constexpr int KP = D + 2;           // padded FP64 length of a staged key
+    constexpr int CPL = 2 * D / kWave;  // selection candidates per lane
+
+    __shared__ double lds_kf[EB][KP];                       // forward-scaled keys of the chunk
+    __shared__ double lds_kb[KDA ? EB : 1][KDA ? KP : 1];  // back-scaled keys (channel gate)
+    __shared__ float lds_v[EB][D];                          // values as fetched
+    __shared__ float lds_kraw[KDA ? EB : 1][KDA ? D : 1];  // channel gate: keys as fetched
+    __shared__ float lds_graw[KDA ? EB : 1][KDA ? D : 1];  // channel gate: gates as fetched
+    __shared__ float lds_b[EB];
+    __shared__ float lds_al[EB];                            // scalar gate: gates as fetched
+    __shared__ double lds_ig[EB];                           // scalar gate: 1 / g_e
+    __shared__ double lds_gs[2];                            // scalar gate: fold factor, new g
+    __shared__ double lds_G[KDA ? D : 1];                   // channel gate: running G per column
+    __shared__ double lds_fold[KDA ? D : 1];                // channel gate: fold factor per column
+    __shared__ int lds_anyfold;                             // channel gate: some column folded
+    __shared__ double lds_gram[NW][EB][EB];                 // partial kf . kb over column slices
+    __shared__ double lds_N[EB][EB];                        // Diag(beta) L
+    __shared__ double lds_M[EB][EB];                        // (I + N)^-1
+    __shared__ double lds_score[2 * D];
+    __shared__ double lds_part[NW][D];
+    __shared__ float lds_smooth[D];
+    __shared__ double lds_ismooth[D];
+    __shared__ int lds_slot[2 * D];  // slot + 1 of each selected candidate, 0 otherwise
+    __shared__ int lds_chosen[16];
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int q = lane >> 4;        // column quad inside a 16-column block
+    const int m = lane & 15;        // row inside the wavefront's 16 rows
+    const int n = 16 * wave + m;    // state row of this lane
+    const int W = a.dm.window;
+    const int nc = a.dm.n_comp;
+
+    const int n_work = (MODE == kModeFlush) ? a.blob.work[0] : a.dm.n_units;
+    for (int wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
+        const int u = (MODE == kModeFlush) ? a.blob.work[1 + wi] : wi;
+        const int s = u / a.dm.n_v_heads;
+        const int h = u - s * a.dm.n_v_heads;
+        const int kh = h / a.dm.group;
+        const size_t kvec = (size_t)s * a.dm.n_k_heads + kh;
+
+        int n_replay = 0;
+        if (MODE == kModeFlush || (MODE == kModeDequant && a.include_buffer)) {
+            const int fill = a.blob.fill[u];
+            n_replay = fill < W ? fill : W;
+        }
+
+        // ---------------- A: the window-start state; T[b][r] = S[n][16b + 4q + r]
+        v4d T[NB];
+        if constexpr (MODE == kModeInit) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (a.S0 != nullptr)
+                    f = *reinterpret_cast<const float4*>(a.S0 + ((size_t)u * D + n) * D + 16 * b + 4 * q);
+                T[b] = v4d{(double)f.x, (double)f.y, (double)f.z, (double)f.w};
+            }
+        } else {
+            const double sgr = (double)a.blob.sigma[(size_t)u * D + n];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const float4 s4 = *reinterpret_cast<const float4*>(a.blob.smooth + (size_t)u * D + 16 * b + 4 * q);
+                const uint32_t wd = *reinterpret_cast<const uint32_t*>(a.blob.codes + ((size_t)u * D + n) * D + 16 * b + 4 * q);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int code = (int)(wd << (24 - 8 * r)) >> 24;
+                    T[b][r] = sgr * (double)code * (double)pick4(s4, r);
+                }
+            }
+            // compensator lines: a row slot adds its line to the four lanes of
+            // that row, a column slot adds one value per row; every load is
+            // issued before any is used
+            if (nc > 0) {
+                const int* ci = a.blob.comp_idx + (size_t)u * nc;
+                const float* cv = a.blob.comp_vec + (size_t)u * nc * D;
+                int my_slot = -1;  // the row slot holding this lane's row, if any
+                for (int c = 0; c < nc; ++c)
+                    if (ci[c] == n) my_slot = c;
+                float4 rowv[NB];
+                const float* rv = cv + (size_t)max(my_slot, 0) * D;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) rowv[b] = *reinterpret_cast<const float4*>(rv + 16 * b + 4 * q);
+                float colv[16];
+#pragma unroll
+                for (int c = 0; c < 16; ++c) colv[c] = cv[(size_t)min(c, nc - 1) * D + n];
+                if (my_slot >= 0) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) T[b][r] += (double)pick4(rowv[b], r);
+                }
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    if (c >= nc) break;
+                    const int col = ci[c] - D;
+                    if (col >= 0) {
+#pragma unroll
+                        for (int b = 0; b < NB; ++b)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (16 * b + 4 * q + r == col) T[b][r] += (double)colv[c];
+                    }
+                }
+            }
+        }
+
+        // ---------------- B: forward replay of the buffered tokens, 16 per chunk
+        const float* bk = a.blob.buf_k + kvec * (size_t)W * D;
+        const float* bv = a.blob.buf_v + (size_t)u * W * D;
+        const float* bb = a.blob.buf_beta + (size_t)u * W;
+        const float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
+        double gam = 1.0;  // scalar gate: g of the last replayed token (uniform)
+        if constexpr (KDA) {
+            if (tid < D) lds_G[tid] = 1.0;
+        }
+        Stage<KDA> pf{};
+        if (n_replay > 0) pf = fetch_stage<D, NT, KDA>(bk, bv, bb, bg, 0, n_replay, tid);
+        for (int i0 = 0; i0 < n_replay; i0 += EB) {
+            const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
+            __syncthreads();  // the previous chunk is done with LDS
+            {
+                const int x = 4 * tid;
+                const int e = x / D, c = x % D;
+                const bool live = e < ne;  // padding tokens: zero key, zero beta
+                *reinterpret_cast<float4*>(&lds_v[e][c]) = pf.v;
+                if constexpr (KDA) {
+                    *reinterpret_cast<float4*>(&lds_kraw[e][c]) = pf.k;
+                    *reinterpret_cast<float4*>(&lds_graw[e][c]) = pf.g;
+                } else {
+                    lds_kf[e][c + 0] = live ? (double)pf.k.x : 0.0;
+                    lds_kf[e][c + 1] = live ? (double)pf.k.y : 0.0;
+                    lds_kf[e][c + 2] = live ? (double)pf.k.z : 0.0;
+                    lds_kf[e][c + 3] = live ? (double)pf.k.w : 0.0;
+                }
+                if (tid < EB) {
+                    lds_b[tid] = tid < ne ? pf.b : 0.f;
+                    lds_al[tid] = pf.al;
+                }
+                if (KDA && tid == 0) lds_anyfold = 0;
+                if constexpr (!KDA) {
+                    // the running gate product g_e = g * prod_{l <= e} alpha_l and its
+                    // reciprocal, one token per lane of wavefront 0; the chunk folds g
+                    // into T first when its product could fall below the threshold
+                    if (wave == 0) {
+                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                        __builtin_amdgcn_wave_barrier();
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                        double P = 1.0, pre = 1.0;
+#pragma unroll
+                        for (int l = 0; l < EB; ++l) {
+                            const double al = l < ne ? fmax((double)lds_al[l], kMinGate) : 1.0;
+                            P *= al;
+                            if (l <= lane) pre *= al;
+                        }
+                        const bool fold = gam * P < kRescaleBelow;
+                        const double g = (fold ? 1.0 : gam) * pre;
+                        if (lane < EB) lds_ig[lane] = lane < ne ? 1.0 / g : 0.0;
+                        if (lane == 0) {
+                            lds_gs[0] = fold ? gam : 1.0;
+                            lds_gs[1] = (fold ? 1.0 : gam) * P;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            if (i0 + EB < n_replay)  // in flight during this chunk
+                pf = fetch_stage<D, NT, KDA>(bk, bv, bb, bg, i0 + EB, n_replay, tid);
+            if constexpr (KDA) {
+                // one thread per column: fold G into T if the chunk could take it
+                // below the threshold, then the key scaled both ways
+                if (tid < D) {
+                    const int c = tid;
+                    double G = lds_G[c];
+                    double P = 1.0;
+                    for (int e = 0; e < ne; ++e) P *= fmax((double)lds_graw[e][c], kMinGate);
+                    const bool fold = G * P < kRescaleBelow;
+                    lds_fold[c] = fold ? G : 1.0;
+                    if (fold) {
+                        G = 1.0;
+                        lds_anyfold = 1;  // every writer stores the same value
+                    }
+#pragma unroll
+                    for (int e = 0; e < EB; ++e) {
+                        double kf = 0.0, kbk = 0.0;
+                        if (e < ne) {
+                            G *= fmax((double)lds_graw[e][c], kMinGate);
+                            const double kc = (double)lds_kraw[e][c];
+                            kf = G * kc;
+                            kbk = kc / G;
+                        }
+                        lds_kf[e][c] = kf;
+                        lds_kb[e][c] = kbk;
+                    }
+                    lds_G[c] = G;
+                }
+            }
+            if constexpr (KDA) __syncthreads();
+            // folds into T
+            if constexpr (KDA) {
+                if (lds_anyfold) {  // uniform, rare
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) T[b][r] *= lds_fold[16 * b + 4 * q + r];
+                }
+            } else {
+                const double f = lds_gs[0];
+                if (f != 1.0) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) T[b] *= f;
+                }
+                gam = lds_gs[1];
+            }
+            // partial L over this wavefront's 16-column slice: lane (q, m),
+            // register r -> sum_k kf[4r + q][k] kb[m][k]
+            {
+                const double(*kb)[KDA ? KP : KP] = KDA ? (const double(*)[KP])lds_kb : (const double(*)[KP])lds_kf;
+                v4d g4a = {0.0, 0.0, 0.0, 0.0}, g4b = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                for (int t = 0; t < 4; t += 2) {
+                    const int k = 16 * wave + 4 * t + q;
+                    g4a = mfma(lds_kf[m][k], kb[m][k], g4a);
+                    g4b = mfma(lds_kf[m][k + 4], kb[m][k + 4], g4b);
+                }
+                const v4d g4 = g4a + g4b;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) lds_gram[wave][4 * r + q][m] = g4[r];
+            }
+            __syncthreads();
+            // A = T Kf^T (wavefronts 1..), M (wavefront 0), then A for wavefront 0
+            auto gemm_a = [&]() {
+                // four independent accumulators keep the matrix pipe busy
+                v4d acc[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] = mfma(lds_kf[m][16 * b + 4 * q + r], T[b][r], acc[r]);
+                return (acc[0] + acc[1]) + (acc[2] + acc[3]);  // register r: A[token 4r + q][row n]
+            };
+            v4d A4;
+            if (wave != 0) {
+                A4 = gemm_a();
+            } else {
+                // N = Diag(beta) L (strictly lower), summed over the slices in a fixed order
+#pragma unroll
+                for (int t = 0; t < EB * EB / kWave; ++t) {
+                    const int idx = lane + kWave * t;
+                    const int e = idx / EB, e2 = idx % EB;
+                    double sum = 0.0;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) sum += lds_gram[w][e][e2];
+                    lds_N[e][e2] = e2 < e ? (double)lds_b[e] * sum : 0.0;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                // M = (I + N)^-1 by forward substitution, one column per lane
+                if (lane < EB) {
+                    double x[EB];
+#pragma unroll
+                    for (int e = 0; e < EB; ++e) {
+                        double t = (e == lane) ? 1.0 : 0.0;
+#pragma unroll
+                        for (int e2 = 0; e2 < e; ++e2) t = __builtin_fma(-lds_N[e][e2], x[e2], t);
+                        x[e] = t;
+                    }
+#pragma unroll
+                    for (int e = 0; e < EB; ++e) lds_M[e][lane] = x[e];
+                }
+            }
+            __syncthreads();
+            if (wave == 0) A4 = gemm_a();
+            // R = (v' - A) Diag(beta): register r -> token 4r + q, row n
+            v4d R4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = 4 * r + q;
+                const double vp = KDA ? (double)lds_v[e][n] : (double)lds_v[e][n] * lds_ig[e];
+                R4[r] = (double)lds_b[e] * (vp - A4[r]);
+            }
+            // C = M R (per row): register r -> token 4r + q, row n
+            v4d C4a = {0.0, 0.0, 0.0, 0.0}, C4b = {0.0, 0.0, 0.0, 0.0};
+            C4a = mfma(lds_M[m][q], R4[0], C4a);
+            C4b = mfma(lds_M[m][4 + q], R4[1], C4b);
+            C4a = mfma(lds_M[m][8 + q], R4[2], C4a);
+            C4b = mfma(lds_M[m][12 + q], R4[3], C4b);
+            const v4d C4 = C4a + C4b;
+            // T += C Kb: block b of S^T, token group r
+            {
+                const double(*kb)[KP] = KDA ? (const double(*)[KP])lds_kb : (const double(*)[KP])lds_kf;
+                const int colm = 4 * (m & 3) + (m >> 2);  // column of block b held by result row m
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) T[b] = mfma(kb[4 * r + q][16 * b + colm], C4[r], T[b]);
+            }
+        }
+        // back to S
+        if constexpr (KDA) {
+            __syncthreads();
+            if (n_replay > 0) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) T[b][r] *= lds_G[16 * b + 4 * q + r];
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) T[b] *= gam;
+        }
+
+        if constexpr (MODE == kModeDequant) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                *reinterpret_cast<float4*>(a.S_out + ((size_t)u * D + n) * D + 16 * b + 4 * q) =
+                    make_float4((float)T[b][0], (float)T[b][1], (float)T[b][2], (float)T[b][3]);
+            __syncthreads();  // LDS is reused by the next unit
+            continue;
+        }
+
+        // ---------------- C1: line scores
+        {
+            double rs = 0.0;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) rs = __builtin_fma(T[b][r], T[b][r], rs);
+            rs = across_rows<false>(rs);
+            if (q == 0) lds_score[n] = rs;
+            double sq[NV];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sq[4 * b + r] = T[b][r] * T[b][r];
+            const int v0 = reduce_columns<NV, false>(sq, m);
+#pragma unroll
+            for (int i = 0; i < NV / 16; ++i) {
+                const int v = v0 + i;
+                lds_part[wave][16 * (v / 4) + 4 * q + (v % 4)] = sq[i];
+            }
+            __syncthreads();
+            if (tid < D) {
+                double t = 0.0;
+                for (int w = 0; w < NW; ++w) t += lds_part[w][tid];
+                lds_score[D + tid] = t;
+            }
+            __syncthreads();
+        }
+
+        // ---------------- C2: top-n_comp selection (wavefront 0)
+        if (wave == 0) {
+            // scores are >= 0; a NaN score (non-finite input) ranks below every
+            // real one, and a lane with nothing left offers (-1, INT_MAX), which
+            // always loses, so every round picks one untaken candidate
+            double val[CPL];
+            bool taken[CPL];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const double sc = lds_score[lane * CPL + i];
+                val[i] = __builtin_isnan(sc) ? -0.5 : sc;
+                taken[i] = false;
+            }
+            for (int r = 0; r < nc; ++r) {
+                double bv_ = -1.0;
+                int bi = 0x7fffffff;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i)
+                    if (!taken[i] && val[i] > bv_) {
+                        bv_ = val[i];
+                        bi = lane * CPL + i;
+                    }
+                for (int mm = 1; mm < kWave; mm <<= 1) {
+                    const double ov = shfl_xor_f64(bv_, mm);
+                    const int oi = __shfl_xor(bi, mm);
+                    if (ov > bv_ || (ov == bv_ && oi < bi)) {
+                        bv_ = ov;
+                        bi = oi;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < CPL; ++i)
+                    if (bi == lane * CPL + i) taken[i] = true;
+                if (lane == 0) lds_chosen[r] = bi;
+            }
+            // slots in ascending candidate order (rows, then columns)
+            for (int x = lane; x < 2 * D; x += kWave) lds_slot[x] = 0;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane < nc) {
+                const int me = lds_chosen[lane];
+                int rank = 0;
+                for (int q2 = 0; q2 < nc; ++q2) rank += lds_chosen[q2] < me;
+                lds_slot[me] = rank + 1;
+                a.blob.comp_idx[(size_t)u * nc + rank] = me;
+            }
+        }
+        __syncthreads();
+
+        // ---------------- C3: extract compensator lines, zero them in the residual
+        {
+            float* cvb = a.blob.comp_vec + (size_t)u * nc * D;
+            const int rslot = lds_slot[n];
+            if (rslot) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    *reinterpret_cast<float4*>(cvb + (size_t)(rslot - 1) * D + 16 * b + 4 * q) =
+                        make_float4((float)T[b][0], (float)T[b][1], (float)T[b][2], (float)T[b][3]);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int cs = lds_slot[D + 16 * b + 4 * q + r];
+                    if (cs) {
+                        cvb[(size_t)(cs - 1) * D + n] = rslot ? 0.0f : (float)T[b][r];
+                        T[b][r] = 0.0;
+                    }
+                    if (rslot) T[b][r] = 0.0;
+                }
+            }
+        }
+
+        // ---------------- C4: smoothing per key channel
+        {
+            double am[NV];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) am[4 * b + r] = fabs(T[b][r]);
+            const int v0 = reduce_columns<NV, true>(am, m);
+#pragma unroll
+            for (int i = 0; i < NV / 16; ++i) {
+                const int v = v0 + i;
+                lds_part[wave][16 * (v / 4) + 4 * q + (v % 4)] = am[i];
+            }
+            __syncthreads();
+            if (tid < D) {
+                double mx = 0.0;
+                for (int w = 0; w < NW; ++w) mx = fmax(mx, lds_part[w][tid]);
+                const float sj = mx > 0.0 ? (float)sqrt(mx) : 1.0f;
+                lds_smooth[tid] = sj;
+                lds_ismooth[tid] = 1.0 / (double)sj;
+                a.blob.smooth[(size_t)u * D + tid] = sj;
+            }
+            __syncthreads();
+        }
+
+        // ---------------- C5: per-row scale and codes
+        {
+            // divisions by s_j and sigma_i s_j as products with FP64 reciprocals
+            // (a few ulps of FP64 off the quotient; the codes round at 2^-10 of
+            // a tie or closer only by chance either way)
+            double mx = 0.0;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx = fmax(mx, fabs(T[b][r] * lds_ismooth[16 * b + 4 * q + r]));
+            mx = across_rows<true>(mx);
+            const float sg = (float)(mx / 127.0);
+            if (q == 0) a.blob.sigma[(size_t)u * D + n] = sg;
+            const double isg = sg != 0.0f ? 1.0 / (double)sg : 0.0;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                uint32_t packed = 0u;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    int code = 0;
+                    if (sg != 0.0f) {
+                        double x = rint(T[b][r] * (isg * lds_ismooth[16 * b + 4 * q + r]));
+                        x = fmin(fmax(x, -127.0), 127.0);
+                        code = (int)x;
+                    }
+                    packed |= ((uint32_t)code & 0xFFu) << (8 * r);
+                }
+                *reinterpret_cast<uint32_t*>(a.blob.codes + ((size_t)u * D + n) * D + 16 * b + 4 * q) = packed;
+            }
+        }
+        if (tid == 0) {
+            a.blob.fill[u] = 0;
+            if (MODE == kModeInit && u == 0) *a.blob.status = 0u;
+        }
+        __syncthreads();  // LDS is reused by the next unit
+    }
+}
 
 // Units whose window is due, in ascending order, into the blob's work list.
 __global__ __launch_bounds__(1024) void due_scan_kernel(MatArgs a) {
@@ -193,489 +708,13 @@ __global__ __launch_bounds__(1024) void due_scan_kernel(MatArgs a) {
     if (tid == 0) a.blob.work[0] = base;
 }
 
-template <int D, bool KDA, int MODE>
-__global__ __launch_bounds__(D * D / 32) void materialize_kernel(MatArgs a) {
-    constexpr int CPR = D / 16;         // column chunks per row = threads per row pair
-    constexpr int NT = D * D / 32;      // threads
-    constexpr int NW = NT / kWave;      // wavefronts
-    constexpr int EB = D == 128 ? 16 : 8;  // buffered tokens staged per batch (one float4 per thread)
-    constexpr int KS = CPR * 18;        // padded FP64 length of one staged key (18 per 16-chunk)
-    constexpr int CPL = 2 * D / kWave;  // selection candidates per lane
-    constexpr int RPW = 64 / CPR;       // row pairs per wavefront
-    constexpr int NVAL = 16 / RPW;      // reduced column values per lane after reduce_rows_in_wave
-    constexpr int F4 = EB * D / (4 * NT);  // float4 of a staged batch per thread
-
-    __shared__ double lds_k[EB][KS];                        // key (scalar gate) or G' * key (channel gate)
-    __shared__ double lds_kd[KDA ? EB : 1][KDA ? KS : 1];  // key / G' (channel gate)
-    __shared__ float lds_v[EB][D];
-    __shared__ float lds_kraw[KDA ? EB : 1][KDA ? D : 1];  // channel gate: keys as fetched
-    __shared__ float lds_graw[KDA ? EB : 1][KDA ? D : 1];  // channel gate: gates as fetched
-    __shared__ float lds_al[KDA ? 1 : EB];                  // scalar gate: gates as fetched
-    __shared__ double lds_coef[EB][2];  // scalar gate: g', 1 / g'
-    __shared__ float lds_b[EB];
-    __shared__ int lds_resc[EB];        // scalar gate: fold g into T before this token
-    __shared__ double lds_G[KDA ? D : 1];     // channel gate: running G per column
-    __shared__ double lds_fold[KDA ? D : 1];  // channel gate: per-column fold factor of a batch
-    __shared__ double lds_score[2 * D];
-    __shared__ double lds_part[NW][D];
-    __shared__ float lds_smooth[D];
-    __shared__ double lds_ismooth[D];
-    __shared__ int lds_slot[2 * D];  // slot + 1 of each selected candidate, 0 otherwise
-    __shared__ int lds_chosen[16];
-
-    const int tid = threadIdx.x;
-    const int rp = tid / CPR;  // row pair
-    const int ch = tid % CPR;  // column chunk
-    const int r0 = 2 * rp;
-    const int c0 = ch * 16;
-    const int wave = tid / kWave;
-    const int lane = tid % kWave;
-    const int W = a.dm.window;
-    const int nc = a.dm.n_comp;
-
-    const int n_work = (MODE == kModeFlush) ? a.blob.work[0] : a.dm.n_units;
-    for (int wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
-        const int u = (MODE == kModeFlush) ? a.blob.work[1 + wi] : wi;
-        const int s = u / a.dm.n_v_heads;
-        const int h = u - s * a.dm.n_v_heads;
-        const int kh = h / a.dm.group;
-        const size_t kvec = (size_t)s * a.dm.n_k_heads + kh;
-
-        int n_replay = 0;
-        if (MODE == kModeFlush || (MODE == kModeDequant && a.include_buffer)) {
-            const int fill = a.blob.fill[u];
-            n_replay = fill < W ? fill : W;
-        }
-
-        // ---------------- A: the window-start state, 2 rows x 16 columns per thread
-        double T[2][16];
-        if constexpr (MODE == kModeInit) {
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                if (a.S0 != nullptr) {
-                    const float4* src =
-                        reinterpret_cast<const float4*>(a.S0 + ((size_t)u * D + r0 + rr) * D + c0);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const float4 f = src[t];
-                        T[rr][4 * t + 0] = f.x;
-                        T[rr][4 * t + 1] = f.y;
-                        T[rr][4 * t + 2] = f.z;
-                        T[rr][4 * t + 3] = f.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int c = 0; c < 16; ++c) T[rr][c] = 0.0;
-                }
-            }
-        } else {
-            const float4* sp = reinterpret_cast<const float4*>(a.blob.smooth + (size_t)u * D + c0);
-            float4 s4[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) s4[t] = sp[t];
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                const double sgr = (double)a.blob.sigma[(size_t)u * D + r0 + rr];
-                const uint4 w = *reinterpret_cast<const uint4*>(a.blob.codes + ((size_t)u * D + r0 + rr) * D + c0);
-                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int b = 0; b < 16; ++b) {
-                    const int code = (int)(wd[b / 4] << (24 - 8 * (b % 4))) >> 24;
-                    T[rr][b] = sgr * (double)code * (double)pick4(s4[b / 4], b % 4);
-                }
-            }
-            // compensator lines, four slots at a time: every load of a group is
-            // issued before any is used (row slots use the 16 columns of this
-            // thread, column slots the entries of its two rows)
-            for (int sl0 = 0; sl0 < nc; sl0 += 4) {
-                int idx[4];
-                float4 rowv[4][4];
-                float colv[4][2];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int sl = min(sl0 + q, nc - 1);
-                    idx[q] = a.blob.comp_idx[(size_t)u * nc + sl];
-                    const float* vec = a.blob.comp_vec + ((size_t)u * nc + sl) * D;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) rowv[q][t] = reinterpret_cast<const float4*>(vec + c0)[t];
-                    colv[q][0] = vec[r0];
-                    colv[q][1] = vec[r0 + 1];
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (sl0 + q >= nc) break;
-                    if (idx[q] < D) {
-#pragma unroll
-                        for (int rr = 0; rr < 2; ++rr)
-                            if (idx[q] == r0 + rr) {
-#pragma unroll
-                                for (int c = 0; c < 16; ++c) T[rr][c] += (double)pick4(rowv[q][c / 4], c % 4);
-                            }
-                    } else {
-                        const int col = idx[q] - D;
-#pragma unroll
-                        for (int c = 0; c < 16; ++c)
-                            if (c0 + c == col) {
-                                T[0][c] += (double)colv[q][0];
-                                T[1][c] += (double)colv[q][1];
-                            }
-                    }
-                }
-            }
-        }
-
-        // ---------------- B: forward replay of the buffered tokens (FP64, rescaled)
-        const float* bk = a.blob.buf_k + kvec * (size_t)W * D;
-        const float* bv = a.blob.buf_v + (size_t)u * W * D;
-        const float* bb = a.blob.buf_beta + (size_t)u * W;
-        const float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
-        double gam = 1.0;  // scalar gate: running product g (uniform)
-        if constexpr (KDA) {
-            if (tid < D) lds_G[tid] = 1.0;
-        }
-        // A batch's keys, values (and channel gates) are fetched into registers
-        // one batch ahead, F4 float4 per thread, every load independent of the
-        // others; tokens past the end of the window repeat the last one and are
-        // never used.
-        Stage<F4, KDA> pf{};
-        if (n_replay > 0) pf = fetch_stage<D, EB, NT, F4, KDA>(bk, bv, bb, bg, 0, n_replay, tid);
-        for (int i0 = 0; i0 < n_replay; i0 += EB) {
-            const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
-            __syncthreads();  // the previous batch is done with LDS
-#pragma unroll
-            for (int f = 0; f < F4; ++f) {
-                const int x = 4 * (tid + f * NT);
-                const int e = x / D, c = x % D;
-                *reinterpret_cast<float4*>(&lds_v[e][c]) = pf.v[f];
-                if constexpr (KDA) {
-                    *reinterpret_cast<float4*>(&lds_kraw[e][c]) = pf.k[f];
-                    *reinterpret_cast<float4*>(&lds_graw[e][c]) = pf.g[f];
-                } else {
-                    double* dk = &lds_k[e][(c / 16) * 18 + (c % 16)];
-                    dk[0] = pf.k[f].x;
-                    dk[1] = pf.k[f].y;
-                    dk[2] = pf.k[f].z;
-                    dk[3] = pf.k[f].w;
-                }
-            }
-            if (tid < EB) {
-                lds_b[tid] = pf.b;
-                if constexpr (!KDA) lds_al[tid] = pf.al;
-            }
-            __syncthreads();
-            if (i0 + EB < n_replay)  // in flight during this batch
-                pf = fetch_stage<D, EB, NT, F4, KDA>(bk, bv, bb, bg, i0 + EB, n_replay, tid);
-            if constexpr (KDA) {
-                // one thread per column walks the batch: fold G into T if it got
-                // small, then G' = G a and the key scaled both ways
-                if (tid < D) {
-                    const int c = tid;
-                    double G = lds_G[c];
-                    lds_fold[c] = (G < kRescaleBelow) ? G : 1.0;
-                    if (G < kRescaleBelow) G = 1.0;
-                    const int slot = (c / 16) * 18 + (c % 16);
-                    for (int e = 0; e < ne; ++e) {
-                        const double ag = fmax((double)lds_graw[e][c], kMinChannelGate);
-                        G *= ag;
-                        const double kc = (double)lds_kraw[e][c];
-                        lds_k[e][slot] = G * kc;
-                        lds_kd[e][slot] = kc / G;
-                    }
-                    lds_G[c] = G;
-                }
-            } else {
-                // the running gate product, token by token (thread 0), then its
-                // reciprocals in parallel (wavefront 0)
-                if (tid == 0) {
-                    double g = gam;
-                    for (int e = 0; e < ne; ++e) {
-                        const double al = (double)lds_al[e];
-                        const bool fold = g * al < kRescaleBelow;
-                        lds_resc[e] = fold ? 1 : 0;
-                        if (fold) g = 1.0;  // T takes the old product first
-                        g *= al;
-                        lds_coef[e][0] = g;
-                    }
-                }
-                if (wave == 0) {
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                    __builtin_amdgcn_wave_barrier();
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                    if (lane < ne) lds_coef[lane][1] = 1.0 / lds_coef[lane][0];
-                }
-            }
-            __syncthreads();
-            if constexpr (KDA) {
-                // fold this batch's per-column factors into T (rare)
-                bool any = false;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) any = any || (lds_fold[c0 + c] != 1.0);
-                if (any) {
-#pragma unroll
-                    for (int c = 0; c < 16; ++c) {
-                        const double f = lds_fold[c0 + c];
-                        T[0][c] *= f;
-                        T[1][c] *= f;
-                    }
-                }
-            }
-            for (int e = 0; e < ne; ++e) {
-                double kk[16];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const double2 k2 = *reinterpret_cast<const double2*>(&lds_k[e][ch * 18 + 2 * t]);
-                    kk[2 * t] = k2.x;
-                    kk[2 * t + 1] = k2.y;
-                }
-                if constexpr (!KDA) {
-                    if (lds_resc[e]) {  // uniform: fold the gate product into T
-#pragma unroll
-                        for (int c = 0; c < 16; ++c) {
-                            T[0][c] *= gam;
-                            T[1][c] *= gam;
-                        }
-                    }
-                }
-                double d0a = 0.0, d0b = 0.0, d1a = 0.0, d1b = 0.0;
-#pragma unroll
-                for (int c = 0; c < 16; c += 2) {
-                    d0a = __builtin_fma(T[0][c], kk[c], d0a);
-                    d0b = __builtin_fma(T[0][c + 1], kk[c + 1], d0b);
-                    d1a = __builtin_fma(T[1][c], kk[c], d1a);
-                    d1b = __builtin_fma(T[1][c + 1], kk[c + 1], d1b);
-                }
-                const double d0 = group_sum<CPR>(d0a + d0b);
-                const double d1 = group_sum<CPR>(d1a + d1b);
-                const double be = (double)lds_b[e];
-                double k0, k1;
-                if constexpr (KDA) {
-                    k0 = be * ((double)lds_v[e][r0] - d0);
-                    k1 = be * ((double)lds_v[e][r0 + 1] - d1);
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const double2 k2 = *reinterpret_cast<const double2*>(&lds_kd[e][ch * 18 + 2 * t]);
-                        kk[2 * t] = k2.x;
-                        kk[2 * t + 1] = k2.y;
-                    }
-                } else {
-                    const double g = lds_coef[e][0], ig = lds_coef[e][1];
-                    gam = g;
-                    k0 = be * ((double)lds_v[e][r0] - g * d0) * ig;
-                    k1 = be * ((double)lds_v[e][r0 + 1] - g * d1) * ig;
-                }
-#pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    T[0][c] = __builtin_fma(k0, kk[c], T[0][c]);
-                    T[1][c] = __builtin_fma(k1, kk[c], T[1][c]);
-                }
-            }
-        }
-        // back to S
-        if constexpr (KDA) {
-            __syncthreads();
-            if (n_replay > 0) {
-#pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    const double G = lds_G[c0 + c];
-                    T[0][c] *= G;
-                    T[1][c] *= G;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                T[0][c] *= gam;
-                T[1][c] *= gam;
-            }
-        }
-
-        if constexpr (MODE == kModeDequant) {
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                float4* dst = reinterpret_cast<float4*>(a.S_out + ((size_t)u * D + r0 + rr) * D + c0);
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    dst[t] = make_float4((float)T[rr][4 * t], (float)T[rr][4 * t + 1], (float)T[rr][4 * t + 2],
-                                         (float)T[rr][4 * t + 3]);
-            }
-            __syncthreads();  // LDS is reused by the next unit
-            continue;
-        }
-
-        // ---------------- C1: line scores
-        {
-            double rs0 = 0.0, rs1 = 0.0;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                rs0 = __builtin_fma(T[0][c], T[0][c], rs0);
-                rs1 = __builtin_fma(T[1][c], T[1][c], rs1);
-            }
-            rs0 = group_sum<CPR>(rs0);
-            rs1 = group_sum<CPR>(rs1);
-            if (ch == 0) {
-                lds_score[r0] = rs0;
-                lds_score[r0 + 1] = rs1;
-            }
-            double sq[16];
-#pragma unroll
-            for (int c = 0; c < 16; ++c) sq[c] = T[0][c] * T[0][c] + T[1][c] * T[1][c];
-            const int cb = reduce_rows_in_wave<CPR, false>(sq);
-#pragma unroll
-            for (int i = 0; i < NVAL; ++i) lds_part[wave][c0 + cb + i] = sq[i];
-            __syncthreads();
-            if (tid < D) {
-                double t = 0.0;
-                for (int w = 0; w < NW; ++w) t += lds_part[w][tid];
-                lds_score[D + tid] = t;
-            }
-            __syncthreads();
-        }
-
-        // ---------------- C2: top-n_comp selection (wavefront 0)
-        if (wave == 0) {
-            // scores are >= 0; a NaN score (non-finite input) ranks below every
-            // real one, and a lane with nothing left offers (-1, INT_MAX), which
-            // always loses, so every round picks one untaken candidate
-            double val[CPL];
-            bool taken[CPL];
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const double sc = lds_score[lane * CPL + i];
-                val[i] = __builtin_isnan(sc) ? -0.5 : sc;
-                taken[i] = false;
-            }
-            for (int r = 0; r < nc; ++r) {
-                double bv_ = -1.0;
-                int bi = 0x7fffffff;
-#pragma unroll
-                for (int i = 0; i < CPL; ++i)
-                    if (!taken[i] && val[i] > bv_) {
-                        bv_ = val[i];
-                        bi = lane * CPL + i;
-                    }
-                for (int m = 1; m < kWave; m <<= 1) {
-                    const double ov = shfl_xor_f64(bv_, m);
-                    const int oi = __shfl_xor(bi, m);
-                    if (ov > bv_ || (ov == bv_ && oi < bi)) {
-                        bv_ = ov;
-                        bi = oi;
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < CPL; ++i)
-                    if (bi == lane * CPL + i) taken[i] = true;
-                if (lane == 0) lds_chosen[r] = bi;
-            }
-            // slots in ascending candidate order (rows, then columns)
-            for (int x = lane; x < 2 * D; x += kWave) lds_slot[x] = 0;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane < nc) {
-                const int me = lds_chosen[lane];
-                int rank = 0;
-                for (int q2 = 0; q2 < nc; ++q2) rank += lds_chosen[q2] < me;
-                lds_slot[me] = rank + 1;
-                a.blob.comp_idx[(size_t)u * nc + rank] = me;
-            }
-        }
-        __syncthreads();
-
-        // ---------------- C3: extract compensator lines, zero them in the residual
-        {
-            float* cvb = a.blob.comp_vec + (size_t)u * nc * D;
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                const int rslot = lds_slot[r0 + rr];
-                if (rslot) {
-                    float4* dst = reinterpret_cast<float4*>(cvb + (size_t)(rslot - 1) * D + c0);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        dst[t] = make_float4((float)T[rr][4 * t], (float)T[rr][4 * t + 1], (float)T[rr][4 * t + 2],
-                                             (float)T[rr][4 * t + 3]);
-                }
-            }
-            const int rs0 = lds_slot[r0], rs1 = lds_slot[r0 + 1];
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const int cs = lds_slot[D + c0 + c];
-                if (cs) {
-                    cvb[(size_t)(cs - 1) * D + r0] = rs0 ? 0.0f : (float)T[0][c];
-                    cvb[(size_t)(cs - 1) * D + r0 + 1] = rs1 ? 0.0f : (float)T[1][c];
-                    T[0][c] = 0.0;
-                    T[1][c] = 0.0;
-                }
-                if (rs0) T[0][c] = 0.0;
-                if (rs1) T[1][c] = 0.0;
-            }
-        }
-
-        // ---------------- C4: smoothing per key channel
-        {
-            double am[16];
-#pragma unroll
-            for (int c = 0; c < 16; ++c) am[c] = fmax(fabs(T[0][c]), fabs(T[1][c]));
-            const int cb = reduce_rows_in_wave<CPR, true>(am);
-#pragma unroll
-            for (int i = 0; i < NVAL; ++i) lds_part[wave][c0 + cb + i] = am[i];
-            __syncthreads();
-            if (tid < D) {
-                double m = 0.0;
-                for (int w = 0; w < NW; ++w) m = fmax(m, lds_part[w][tid]);
-                const float sj = m > 0.0 ? (float)sqrt(m) : 1.0f;
-                lds_smooth[tid] = sj;
-                lds_ismooth[tid] = 1.0 / (double)sj;
-                a.blob.smooth[(size_t)u * D + tid] = sj;
-            }
-            __syncthreads();
-        }
-
-        // ---------------- C5: per-row scale and codes
-        {
-            // divisions by s_j and sigma_i s_j as products with FP64 reciprocals
-            // (a few ulps of FP64 off the quotient; the codes round at 2^-10 of
-            // a tie or closer only by chance either way)
-            double isj[16];
-#pragma unroll
-            for (int c = 0; c < 16; ++c) isj[c] = lds_ismooth[c0 + c];
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                double m = 0.0;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) m = fmax(m, fabs(T[rr][c] * isj[c]));
-                m = group_max<CPR>(m);
-                const float sg = (float)(m / 127.0);
-                if (ch == 0) a.blob.sigma[(size_t)u * D + r0 + rr] = sg;
-                const double isg = sg != 0.0f ? 1.0 / (double)sg : 0.0;
-                uint32_t packed[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    int code = 0;
-                    if (sg != 0.0f) {
-                        double x = rint(T[rr][c] * (isg * isj[c]));
-                        x = fmin(fmax(x, -127.0), 127.0);
-                        code = (int)x;
-                    }
-                    packed[c / 4] |= ((uint32_t)code & 0xFFu) << (8 * (c % 4));
-                }
-                *reinterpret_cast<uint4*>(a.blob.codes + ((size_t)u * D + r0 + rr) * D + c0) =
-                    make_uint4(packed[0], packed[1], packed[2], packed[3]);
-            }
-        }
-        if (tid == 0) {
-            a.blob.fill[u] = 0;
-            if (MODE == kModeInit && u == 0) *a.blob.status = 0u;
-        }
-        __syncthreads();  // LDS is reused by the next unit
-    }
-}
 
 __global__ void clear_status_kernel(uint32_t* status) { *status = 0u; }
 
 hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, hipStream_t st) {
     // a fixed grid walks the units (init, dequant) or the work list (flush)
     const int grid_cap = 2048;
-    const dim3 grid(a.dm.n_units < grid_cap ? a.dm.n_units : grid_cap), block(d * d / 32);
+    const dim3 grid(a.dm.n_units < grid_cap ? a.dm.n_units : grid_cap), block(kWave * d / 16);
     const bool kda = gate_kind == LQ_GATE_CHANNEL;
     if (mode == kModeFlush) {
         hipLaunchKernelGGL(due_scan_kernel, dim3(1), dim3(1024), 0, st, a);
