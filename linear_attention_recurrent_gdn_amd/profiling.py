@@ -19,6 +19,12 @@ Three commands:
   stats    --csv FILE --cmd "..." --out FILE
       Formats a ``rocprofv3 --stats`` kernel_stats.csv as a short text
       summary headed by the command that produced it.
+
+  hbm
+      Practical memory bandwidth of this device for plain streaming kernels:
+      a 1 GiB device-to-device copy (read + write) and a 1 GiB read (sum),
+      each timed with HIP events over repeated launches, and the same read
+      over 64 MiB (a working set that stays in the 256 MB last-level cache).
 """
 from __future__ import annotations
 
@@ -83,6 +89,35 @@ def run_window(workload: str) -> None:
     print(f"[window] done, flags={flags:#x}", flush=True)
     if flags:
         sys.exit(1)
+
+
+def hbm() -> dict:
+    import torch
+
+    dev = torch.device("cuda", 0)
+    out = {}
+    for label, nbytes in (("1GiB", 1 << 30), ("64MiB", 64 << 20)):
+        x = torch.ones(nbytes // 4, device=dev)
+        y = torch.empty_like(x)
+        for kind in ("copy", "read"):
+            def body():
+                return y.copy_(x) if kind == "copy" else x.sum()
+            for _ in range(3):
+                body()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 20
+            a.record()
+            for _ in range(reps):
+                body()
+            b.record()
+            torch.cuda.synchronize()
+            sec = a.elapsed_time(b) * 1e-3 / reps
+            moved = nbytes * (2 if kind == "copy" else 1)
+            out[f"{kind}_{label}_TBps"] = round(moved / sec / 1e12, 3)
+        del x, y
+    print(json.dumps(out))
+    return out
 
 
 def _counter_rows(path_or_dir: str, counter: str):
@@ -171,6 +206,7 @@ def main(argv=None):
     b.add_argument("--write", required=True)
     b.add_argument("--out", required=True)
     b.add_argument("--command", default="")
+    sub.add_parser("hbm")
     c = sub.add_parser("stats")
     c.add_argument("--csv", required=True)
     c.add_argument("--command", default="")
@@ -178,6 +214,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "window":
         run_window(args.workload)
+    elif args.cmd == "hbm":
+        hbm()
     elif args.cmd == "traffic":
         print(json.dumps(traffic(args.workload, args.fetch, args.write, args.out, args.command), indent=1))
     else:
