@@ -5,9 +5,11 @@ One step = one decode token for every (sequence, head) unit of every layer
 (lq_decode_step), plus the window-boundary requantization (lq_window_flush)
 for every unit whose window filled on that token.  Inputs are synthetic,
 seeded, and resident in HBM before the timed region starts.  The timed steps
-are captured as one HIP graph and replayed between HIP events, so the host's
-launch cost is not in the figure.  The same steps are then timed on the
-FP32-state comparison kernel.
+are captured as one HIP graph and replayed between HIP events (median of
+--repeats replays), so the host's launch cost is not in the figure.  The same
+steps are then timed on the FP32-state comparison kernel.  --replicas R runs
+every step on R independent copies of the states in turn, which pushes a
+working set that would fit the 256 MB last-level cache out to HBM.
 
 Prints one JSON line:
   value            unit-tokens/s (seq·head·tokens/s) of the INT8 path over the timed steps
@@ -44,6 +46,13 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-fp32", action="store_true", help="skip the FP32-state comparison loop")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="replays of the timed-steps graph, median reported (1 if the steps are not whole "
+                         "windows: only then does a replay restart the same fill pattern)")
+    ap.add_argument("--replicas", type=int, default=1,
+                    help="independent copies of every state, each token run on every copy in turn: with "
+                         "enough copies the working set exceeds the 256 MB last-level cache, so every launch "
+                         "reads its state from HBM (throughput counts the units of all copies)")
     return ap.parse_args()
 
 
@@ -226,6 +235,10 @@ def main():
         lq.lq_state_init(cfg, st, S)
         states.append(st)
         S_fp32.append(S)
+    R = max(1, args.replicas)
+    blobs = [[st] + [st.clone() for _ in range(R - 1)] for st in states]  # [layer][copy]
+    if not args.no_fp32:
+        S_fp32 = [[S] + [S.clone() for _ in range(R - 1)] for S in S_fp32]
     n_tok = warmup + steps
     toks = [device_tokens(wl, n_tok, layer, gen, dev, weights[layer]) for layer in range(L)]
     torch.cuda.synchronize()
@@ -238,7 +251,8 @@ def main():
     def int8_step(t):
         for layer in range(L):
             tk = toks[layer][t]
-            lq.lq_decode_step(cfg, states[layer], tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+            for st in blobs[layer]:
+                lq.lq_decode_step(cfg, st, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
         fill[:] += 1
         forced = (sched == t) if (sched is not None and t < warmup) else np.zeros(wl.n_seq, bool)
         due = (fill >= W) | (forced & (fill > 0))
@@ -248,36 +262,43 @@ def main():
                 force_dev.copy_(torch.from_numpy(forced.astype(np.uint8)))
                 fm = force_dev
             for layer in range(L):
-                lq.lq_window_flush(cfg, states[layer], fm)
+                for st in blobs[layer]:
+                    lq.lq_window_flush(cfg, st, fm)
             flush_calls.append(int(due.sum()) * wl.n_v_heads)
             fill[due] = 0
 
-    def timed_graph(body):
-        """Capture body() as one HIP graph, replay it once between events (ms)."""
+    def timed_graph(body, repeats=1):
+        """Capture body() as one HIP graph, replay it `repeats` times, each between
+        HIP events; the median replay time (ms)."""
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             body()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        g.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b)
+        times = []
+        for _ in range(max(1, repeats)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        del g
+        return float(np.median(times))
 
     for t in range(warmup):
         int8_step(t)
     n_flush_warm = len(flush_calls)
     # the timed steps run as one graph: kernels back to back, no host launch cost
-    int8_ms = timed_graph(lambda: [int8_step(t) for t in range(warmup, n_tok)])
-    flags = [lq.lq_read_status(cfg, st) for st in states]
+    repeats = args.repeats if steps % W == 0 else 1
+    int8_ms = timed_graph(lambda: [int8_step(t) for t in range(warmup, n_tok)], repeats)
+    flags = [lq.lq_read_status(cfg, st) for bl in blobs for st in bl]
     if any(flags):
         raise RuntimeError(f"device flags set during the run: {flags}")
 
     result = {
         "metric": METRIC,
-        "value": U * L * steps / (int8_ms * 1e-3),
+        "value": U * L * R * steps / (int8_ms * 1e-3),
         "unit": "seq·head·tokens/s",
         "n_gpus": 1,
         "steps": steps,
@@ -293,22 +314,23 @@ def main():
             "workload": wl.name,
             "layers": L, "n_seq": wl.n_seq, "n_v_heads": wl.n_v_heads, "n_k_heads": wl.n_k_heads,
             "d_k": d, "d_v": d, "gate": wl.gate, "window": W, "n_comp": wl.n_comp,
-            "prefill": wl.prefill, "units": U * L,
+            "prefill": wl.prefill, "units": U * L * R, "state_copies": R,
         },
-        "timing": "HIP graph replay of the timed steps, HIP events around the replay",
+        "timing": f"HIP graph of the timed steps, median of {repeats} replays, HIP events around each",
     }
 
     # ---- the decode kernel alone over one whole window (every unit at j = 0 .. W-1),
     # replayed as a graph: its average launch time against its algorithmic bytes
     all_seq = torch.ones(wl.n_seq, dtype=torch.uint8, device=dev)
-    for layer in range(L):
-        lq.lq_window_flush(cfg, states[layer], all_seq)  # forced: every window restarts empty
+    for bl in blobs:
+        for st in bl:
+            lq.lq_window_flush(cfg, st, all_seq)  # forced: every window restarts empty
     win_tok = [t % n_tok for t in range(W)]
-    dec_ms = timed_graph(lambda: [lq.lq_decode_step(cfg, states[layer], toks[layer][t]["q"], toks[layer][t]["k"],
+    dec_ms = timed_graph(lambda: [lq.lq_decode_step(cfg, st, toks[layer][t]["q"], toks[layer][t]["k"],
                                                     toks[layer][t]["v"], toks[layer][t]["beta"],
                                                     toks[layer][t]["gate"], o)
-                                  for t in win_tok for layer in range(L)])
-    n_launch = W * L
+                                  for t in win_tok for layer in range(L) for st in blobs[layer]])
+    n_launch = W * L * R
     avg_launch_s = dec_ms * 1e-3 / n_launch
     avg_bytes = float(np.mean([decode_bytes(wl, j) for j in range(W)])) * U
     achieved = avg_bytes / avg_launch_s / 1e9
@@ -326,7 +348,7 @@ def main():
         "note": "one graph of one window of decode launches (j = 0..W-1), events around the replay",
     }
     # flush alone: one forced boundary of every unit after a full window
-    fl_ms = timed_graph(lambda: [lq.lq_window_flush(cfg, states[layer], None) for layer in range(L)])
+    fl_ms = timed_graph(lambda: [lq.lq_window_flush(cfg, blobs[layer][0], None) for layer in range(L)])
     result["flush"] = {
         "avg_launch_us": fl_ms * 1e3 / L,
         "units_per_launch": U,
@@ -339,13 +361,13 @@ def main():
             for t in range(t_from, t_to):
                 for layer in range(L):
                     tk = toks[layer][t]
-                    lq.lq_fp32_decode_step(cfg, S_fp32[layer], tk["q"], tk["k"], tk["v"], tk["beta"],
-                                           tk["gate"], o)
+                    for S in S_fp32[layer]:
+                        lq.lq_fp32_decode_step(cfg, S, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
         fp32_steps(0, warmup)
-        fp32_ms = timed_graph(lambda: fp32_steps(warmup, n_tok))
-        fp32_bytes = U * L * (8 * d * d + 4 * (2 * d // wl.group + 2 * d + 1 + (d if wl.gate == "channel" else 1)))
+        fp32_ms = timed_graph(lambda: fp32_steps(warmup, n_tok), repeats)
+        fp32_bytes = U * L * R * (8 * d * d + 4 * (2 * d // wl.group + 2 * d + 1 + (d if wl.gate == "channel" else 1)))
         result["fp32_state"] = {
-            "value": U * L * steps / (fp32_ms * 1e-3),
+            "value": U * L * R * steps / (fp32_ms * 1e-3),
             "ms_per_step": fp32_ms / steps,
             "alg_GBps": fp32_bytes / (fp32_ms / steps * 1e-3) / 1e9,
             "speedup_int8_vs_fp32": fp32_ms / int8_ms,

@@ -375,10 +375,10 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
 }
 
 #ifndef LQ_RING_GDN
-#define LQ_RING_GDN 8
+#define LQ_RING_GDN 4
 #endif
 #ifndef LQ_RING_KDA
-#define LQ_RING_KDA 8
+#define LQ_RING_KDA 6
 #endif
 
 hipError_t launch_decode_int8(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
