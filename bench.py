@@ -43,6 +43,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=None, help="untimed tokens first (default: one window)")
     ap.add_argument("--workload", default="gdn_decode",
                     help="tiny_gdn | gdn_decode | kda_decode | gdn_serving | hybrid_stack")
+    ap.add_argument("--window", type=int, default=None, help="override the workload's window W (1..256)")
+    ap.add_argument("--n-comp", type=int, default=None, help="override the workload's compensator count (0..16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-fp32", action="store_true", help="skip the FP32-state comparison loop")
@@ -210,6 +212,10 @@ def main():
 
     lq.load_library()
     wl = I.WORKLOADS[args.workload]
+    if args.window is not None:
+        wl = wl.scaled(window=args.window)
+    if args.n_comp is not None:
+        wl = wl.scaled(n_comp=args.n_comp)
     W, U, L, d = wl.window, wl.n_units, wl.layers, wl.d
     steps = wl.decode if args.steps is None else args.steps
     warmup = W if args.warmup is None else args.warmup

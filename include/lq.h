@@ -78,7 +78,7 @@ extern "C" {
 
 /*
  * Problem description.  Supported: d_k == d_v in {64, 128};
- * 1 <= window <= 128; 0 <= n_comp <= 16; n_seq, n_v_heads, n_k_heads >= 1;
+ * 1 <= window <= 256; 0 <= n_comp <= 16; n_seq, n_v_heads, n_k_heads >= 1;
  * n_v_heads % n_k_heads == 0; gate_kind in {LQ_GATE_SCALAR, LQ_GATE_CHANNEL};
  * the unit count n_seq * n_v_heads below 2^31.
  */

@@ -19,7 +19,7 @@ int32_t check_config(const lq_config* c) {
     if (c->gate_kind != LQ_GATE_SCALAR && c->gate_kind != LQ_GATE_CHANNEL) return LQ_EINVAL;
     if ((int64_t)c->n_seq * c->n_v_heads >= ((int64_t)1 << 31)) return LQ_EUNSUPPORTED;
     if (c->d_k != c->d_v || (c->d_k != 64 && c->d_k != 128)) return LQ_EUNSUPPORTED;
-    if (c->window > 128 || c->n_comp > 16) return LQ_EUNSUPPORTED;
+    if (c->window > 256 || c->n_comp > 16) return LQ_EUNSUPPORTED;
     return LQ_OK;
 }
 

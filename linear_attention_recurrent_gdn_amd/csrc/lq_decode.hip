@@ -76,7 +76,7 @@ struct Entry {
 
 }  // namespace
 
-template <int D, bool KDA, int P>
+template <int D, bool KDA, int P, int NWB>
 __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeArgs a) {
     constexpr int EPL = D / kWave;   // state elements per lane in the chain wave
     constexpr int GE = KDA ? EPL : 1;
@@ -129,8 +129,8 @@ __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeArgs a) {
         // loads in the order they are consumed (vector loads return in order):
         // the current token, the newest P buffered tokens (a ring refilled P
         // tokens ahead of use; indices below 0 are clamped to entry 0 and not
-        // used), beta and the scalar gate of the whole window (one per lane),
-        // smoothing and compensators
+        // used), beta and the scalar gate of the whole window (NWB per lane,
+        // window <= 64 NWB), smoothing and compensators
         const Vec<EPL> qv = load_vec<EPL>(a.q + kvec * D + lane * EPL);
         Entry<EPL, GE> cur;
         cur.k = load_vec<EPL>(a.k + kvec * D + lane * EPL);
@@ -149,12 +149,11 @@ __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeArgs a) {
         Entry<EPL, GE> ring[P];
 #pragma unroll
         for (int p = 0; p < P; ++p) load_entry(max(j - 1 - p, 0), ring[p]);
-        const float bwin0 = bb[min(lane, W - 1)];
-        const float bwin1 = bb[min(lane + kWave, W - 1)];
-        float awin0 = 0.f, awin1 = 0.f;
-        if constexpr (!KDA) {
-            awin0 = bg[min(lane, W - 1)];
-            awin1 = bg[min(lane + kWave, W - 1)];
+        float bwin[NWB], awin[NWB];
+#pragma unroll
+        for (int w = 0; w < NWB; ++w) {
+            bwin[w] = bb[min(lane + w * kWave, W - 1)];
+            awin[w] = KDA ? 0.f : bg[min(lane + w * kWave, W - 1)];
         }
         // this wave's tile quarter comes after the data the reverse pass needs first
 #pragma unroll
@@ -211,12 +210,20 @@ __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeArgs a) {
             for (int p = 0; p < P; ++p) {
                 const int i = j - 1 - (s0 + p);
                 if (i >= 0) {
+                    // i is uniform: pick the window register by compare-and-select
+                    // (constant indices only), then read the owning lane
+                    float bsel = bwin[0], asel = awin[0];
+#pragma unroll
+                    for (int w = 1; w < NWB; ++w) {
+                        bsel = (i >= w * kWave) ? bwin[w] : bsel;
+                        asel = (i >= w * kWave) ? awin[w] : asel;
+                    }
                     const float beta = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, i < kWave ? bwin0 : bwin1), i & (kWave - 1)));
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bsel), i & (kWave - 1)));
                     float alpha = 0.f;
                     if constexpr (!KDA)
                         alpha = __builtin_bit_cast(
-                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, i < kWave ? awin0 : awin1), i & (kWave - 1)));
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, asel), i & (kWave - 1)));
                     step(ring[p], beta, alpha);
                 }
                 load_entry(max(i - P, 0), ring[p]);
@@ -381,15 +388,23 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
 #define LQ_RING_KDA 6
 #endif
 
-hipError_t launch_decode_int8(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
+template <int NWB>
+void launch_decode_int8_w(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
     const dim3 grid(a.dm.n_units), block(256);
     if (d == 128) {
-        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_int8_kernel<128, true, LQ_RING_KDA>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((decode_int8_kernel<128, false, LQ_RING_GDN>), grid, block, 0, st, a);
+        if (gate_kind == LQ_GATE_CHANNEL)
+            hipLaunchKernelGGL((decode_int8_kernel<128, true, LQ_RING_KDA, NWB>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((decode_int8_kernel<128, false, LQ_RING_GDN, NWB>), grid, block, 0, st, a);
     } else {
-        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_int8_kernel<64, true, 16>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((decode_int8_kernel<64, false, 16>), grid, block, 0, st, a);
+        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_int8_kernel<64, true, 16, NWB>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_int8_kernel<64, false, 16, NWB>), grid, block, 0, st, a);
     }
+}
+
+hipError_t launch_decode_int8(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
+    if (a.dm.window <= 2 * kWave) launch_decode_int8_w<2>(a, d, gate_kind, st);
+    else launch_decode_int8_w<4>(a, d, gate_kind, st);
     return hipGetLastError();
 }
 

@@ -79,7 +79,7 @@ def test_state_bytes_matches_int8_footprint(lib):
     (dict(n_comp=-1), lq.LQ_EINVAL),
     (dict(d_k=96, d_v=96), lq.LQ_EUNSUPPORTED),
     (dict(d_k=64, d_v=128), lq.LQ_EUNSUPPORTED),
-    (dict(window=129), lq.LQ_EUNSUPPORTED),
+    (dict(window=257), lq.LQ_EUNSUPPORTED),
     (dict(n_comp=17), lq.LQ_EUNSUPPORTED),
     (dict(n_seq=1 << 26, n_v_heads=64, n_k_heads=64), lq.LQ_EUNSUPPORTED),
 ])

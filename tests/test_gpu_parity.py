@@ -45,9 +45,16 @@ CASES = {
     "w1_nc0": (small("gdn_decode", name="w1_nc0", n_seq=2, n_v_heads=3, n_k_heads=3,
                      prefill=20, decode=12, window=1, n_comp=0, outlier_rows=0,
                      outlier_cols=0), dict()),
-    # the largest supported window and compensator count
-    "max_limits": (small("gdn_decode", name="max_limits", n_seq=1, n_v_heads=5, n_k_heads=5,
-                         prefill=64, decode=140, window=128, n_comp=16), dict(dequant_every=70)),
+    # the largest supported window and compensator count: one full window and a partial one
+    "max_limits": (small("gdn_decode", name="max_limits", n_seq=1, n_v_heads=3, n_k_heads=3,
+                         prefill=64, decode=300, window=256, n_comp=16), dict(dequant_every=110)),
+    # a window above 128 that is no multiple of 16 or 64, channel gate
+    "kda_w200": (small("kda_decode", name="kda_w200", n_seq=1, n_v_heads=2, n_k_heads=2,
+                       prefill=32, decode=230, window=200, n_comp=8), dict(dequant_every=97)),
+    # a window above 128 at d = 64
+    "gdn_d64_w144": (small("gdn_decode", name="gdn_d64_w144", n_seq=2, n_v_heads=2, n_k_heads=2,
+                           d=64, prefill=16, decode=160, window=144, n_comp=2, outlier_rows=0,
+                           outlier_cols=0), dict(dequant_every=61)),
     # zero start state (no prefill) with the channel gate at d=128
     "kda_zero_start": (small("kda_decode", name="kda_zero_start", n_seq=1, n_v_heads=2,
                              n_k_heads=2, prefill=0, decode=20, window=8, n_comp=4), dict()),
