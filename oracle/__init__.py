@@ -57,12 +57,15 @@ def _load():
         lib.orc_num_threads.restype = I
         lib.orc_set_num_threads.argtypes = [I]
         lib.orc_recurrence.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
-        lib.orc_qz.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P]
-        lib.orc_dequant.argtypes = [I, I, I, I, P, P, P, P, P, P]
-        lib.orc_replay_output.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
-        lib.orc_windowed_run.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        lib.orc_qz.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        lib.orc_dequant.argtypes = [I, I, I, I, I, P, P, P, P, P, P]
+        lib.orc_replay_output.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
+        lib.orc_windowed_run.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        lib.orc_e4m3_value.argtypes = [I]
+        lib.orc_e4m3_value.restype = ctypes.c_double
+        lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
         for f in ("orc_recurrence", "orc_qz", "orc_dequant", "orc_replay_output",
-                  "orc_windowed_run"):
+                  "orc_windowed_run", "orc_e4m3_encode"):
             getattr(lib, f).restype = I
         _lib = lib
         return lib
@@ -114,17 +117,47 @@ def recurrence(S, q, k, v, beta, gate, want_outputs=True):
     return S, o
 
 
+FORMATS = {"int8": 0, "e4m3": 1}
+
+
+def _fmt(fmt: str) -> int:
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown code format {fmt!r}")
+    return FORMATS[fmt]
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one E4M3 byte (NaN for the two NaN codes)."""
+    return _load().orc_e4m3_value(int(code) & 0xFF)
+
+
+def e4m3_encode(x: float) -> int:
+    """E4M3 byte of the nearest value to x (ties to the even mantissa, saturating at 448)."""
+    return _load().orc_e4m3_encode(float(x))
+
+
+def code_values(codes, fmt: str = "int8") -> np.ndarray:
+    """fp64 values of an array of stored codes."""
+    codes = np.asarray(codes, np.int8)
+    if _fmt(fmt) == 0:
+        return codes.astype(np.float64)
+    table = np.array([e4m3_value(c) for c in range(256)])
+    return table[codes.view(np.uint8)]
+
+
 class Blob:
     """The stored low-bit state of ``U`` units, as the oracle holds it."""
 
-    __slots__ = ("codes", "sigma", "smooth", "comp_idx", "comp_vec")
+    __slots__ = ("codes", "sigma", "smooth", "comp_idx", "comp_vec", "fmt")
 
-    def __init__(self, codes, sigma, smooth, comp_idx, comp_vec):
-        self.codes = np.ascontiguousarray(codes, np.int8)
+    def __init__(self, codes, sigma, smooth, comp_idx, comp_vec, fmt="int8"):
+        self.codes = np.ascontiguousarray(codes).view(np.int8)
         self.sigma = _f32(sigma)
         self.smooth = _f32(smooth)
         self.comp_idx = np.ascontiguousarray(comp_idx, np.int32)
         self.comp_vec = _f32(comp_vec)
+        _fmt(fmt)
+        self.fmt = fmt
 
     @property
     def n_comp(self):
@@ -132,11 +165,12 @@ class Blob:
 
     def take(self, units):
         return Blob(self.codes[units], self.sigma[units], self.smooth[units],
-                    self.comp_idx[units], self.comp_vec[units])
+                    self.comp_idx[units], self.comp_vec[units], self.fmt)
 
 
-def qz(S, n_c, smooth=True, force_sel=None):
-    """Qz: compensators, smoothing and INT8 codes of each unit's state.
+def qz(S, n_c, smooth=True, force_sel=None, fmt="int8"):
+    """Qz: compensators, smoothing and 8-bit codes (``fmt`` "int8" or "e4m3")
+    of each unit's state.
 
     Returns (Blob, x_unrounded [U, dv, dk], scores [U, dv + dk]).
     """
@@ -152,10 +186,10 @@ def qz(S, n_c, smooth=True, force_sel=None):
     x = np.zeros((U, dv, dk), np.float64)
     sc = np.zeros((U, dv + dk), np.float64)
     fs = None if force_sel is None else np.ascontiguousarray(force_sel, np.int32)
-    rc = lib.orc_qz(U, dk, dv, n_c, 1 if smooth else 0, _p(S), _p(fs), _p(codes), _p(sigma),
-                    _p(sm), _p(ci), _p(cv), _p(x), _p(sc))
+    rc = lib.orc_qz(_fmt(fmt), U, dk, dv, n_c, 1 if smooth else 0, _p(S), _p(fs), _p(codes),
+                    _p(sigma), _p(sm), _p(ci), _p(cv), _p(x), _p(sc))
     assert rc == 0
-    return Blob(codes, sigma, sm, ci, cv), x, sc
+    return Blob(codes, sigma, sm, ci, cv, fmt), x, sc
 
 
 def dequant(blob: Blob):
@@ -163,7 +197,7 @@ def dequant(blob: Blob):
     lib = _load()
     U, dv, dk = blob.codes.shape
     S = np.zeros((U, dv, dk), np.float64)
-    rc = lib.orc_dequant(U, dk, dv, blob.n_comp, _p(blob.codes), _p(blob.sigma),
+    rc = lib.orc_dequant(_fmt(blob.fmt), U, dk, dv, blob.n_comp, _p(blob.codes), _p(blob.sigma),
                          _p(blob.smooth), _p(blob.comp_idx), _p(blob.comp_vec), _p(S))
     assert rc == 0
     return S
@@ -181,20 +215,22 @@ def replay_output(blob: Blob, bk, bv, bb, bg, q):
     n = bk.shape[1]
     gk = GATE_SCALAR if bg.shape == (U, n) else GATE_CHANNEL
     o = np.zeros((U, dv), np.float64)
-    rc = lib.orc_replay_output(U, dk, dv, blob.n_comp, gk, n, _p(blob.codes), _p(blob.sigma),
+    rc = lib.orc_replay_output(_fmt(blob.fmt), U, dk, dv, blob.n_comp, gk, n, _p(blob.codes), _p(blob.sigma),
                                _p(blob.smooth), _p(blob.comp_idx), _p(blob.comp_vec), _p(bk),
                                _p(bv), _p(bb), _p(bg), _p(q), _p(o))
     assert rc == 0
     return o
 
 
-def windowed_run(S0, q, k, v, beta, gate, W, n_c, smooth=True, force_at=None, want_state=False):
+def windowed_run(S0, q, k, v, beta, gate, W, n_c, smooth=True, force_at=None, want_state=False,
+                 fmt="int8"):
     """O2: the windowed scheme in its definitional form over T tokens.
 
     S0 [U, dv, dk] unquantized start state; token-major inputs as in
     ``recurrence``.  ``force_at[u]`` = token index after which unit u takes a
     forced partial flush (-1: none).  W=1, n_c=0, smooth=False gives the naive
-    per-token quantization.  Returns o [T, U, dv] (and the final state).
+    per-token quantization; ``fmt`` selects the code format ("int8" or "e4m3").
+    Returns o [T, U, dv] (and the final state).
     """
     lib = _load()
     S0 = _f64(S0)
@@ -205,7 +241,7 @@ def windowed_run(S0, q, k, v, beta, gate, W, n_c, smooth=True, force_at=None, wa
     fa = None if force_at is None else np.ascontiguousarray(force_at, np.int32)
     o = np.zeros((T, U, dv), np.float64)
     Sout = np.zeros((U, dv, dk), np.float64) if want_state else None
-    rc = lib.orc_windowed_run(U, dk, dv, T, gk, W, n_c, 1 if smooth else 0, _p(S0), _p(q),
+    rc = lib.orc_windowed_run(_fmt(fmt), U, dk, dv, T, gk, W, n_c, 1 if smooth else 0, _p(S0), _p(q),
                               _p(k), _p(v), _p(beta), _p(gate), _p(fa), _p(o), _p(Sout))
     assert rc == 0
     return (o, Sout) if want_state else o

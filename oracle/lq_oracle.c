@@ -43,6 +43,9 @@
 #define ORC_GATE_SCALAR 0 /* GDN: one alpha per (token, unit)             */
 #define ORC_GATE_CHANNEL 1 /* KDA: one a-vector of d_k per (token, unit)  */
 
+#define ORC_FMT_INT8 0 /* codes are integers in [-127, 127]             */
+#define ORC_FMT_E4M3 1 /* codes are 8-bit floats, E4M3 (no infinities)  */
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
@@ -57,6 +60,76 @@ void orc_set_num_threads(int n) {
 #else
     (void)n;
 #endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* The two 8-bit code formats                                               */
+/* ------------------------------------------------------------------------ */
+/*
+ * [ABS] says the state is kept in 8 bits; [REV] says INT8.  READING: INT8 is
+ * the main format; an 8-bit floating-point variant is the alternative the
+ * word "8-bit" also allows.  It is the E4M3 format of the OCP 8-bit floating
+ * point specification (the "FN" flavour, no infinities): one sign bit, four
+ * exponent bits with bias 7, three mantissa bits.  Exponent field 0 holds the
+ * subnormals m/8 * 2^-6; exponent field 15 with mantissa 7 is NaN, so the
+ * largest finite magnitude is (1 + 6/8) * 2^8 = 448.  The quantizer is the
+ * same in both formats (compensators, smoothing, per-row scale); only the
+ * code grid and its largest magnitude (127 or 448) differ.
+ */
+double orc_e4m3_value(int code) {
+    const int c = code & 0xFF;
+    const double sign = (c & 0x80) ? -1.0 : 1.0;
+    const int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) return sign * ldexp((double)m / 8.0, -6);
+    return sign * ldexp(1.0 + (double)m / 8.0, e - 7);
+}
+
+/*
+ * Nearest E4M3 value, ties to the even mantissa, magnitudes above 448 taken
+ * as 448.  Around a magnitude a the representable values are spaced
+ * 2^(E-3) with E = max(floor(log2 a), -6); a / 2^(E-3) rounded to an
+ * integer k gives k = m (subnormal), 8 + m (normal) or 16 (the next binade).
+ * READING: zero (also a negative value that rounds to zero) is the code 0x00.
+ */
+int orc_e4m3_encode(double x) {
+    double a = fabs(x);
+    if (a > 448.0) a = 448.0;
+    if (a == 0.0) return 0;
+    int ex;
+    frexp(a, &ex); /* a = f * 2^ex, f in [0.5, 1): floor(log2 a) = ex - 1 */
+    int E = ex - 1;
+    if (E < -6) E = -6;
+    const double k = nearbyint(ldexp(a, 3 - E)); /* exact scaling, then ties-to-even */
+    if (k == 0.0) return 0;
+    int e, m;
+    if (k < 8.0) {
+        e = 0;
+        m = (int)k;
+    } else if (k == 16.0) {
+        e = E + 8;
+        m = 0;
+    } else {
+        e = E + 7;
+        m = (int)k - 8;
+    }
+    return (x < 0.0 ? 0x80 : 0) | (e << 3) | m;
+}
+
+static double code_value(int fmt, int8_t c) {
+    return fmt == ORC_FMT_E4M3 ? orc_e4m3_value((uint8_t)c) : (double)c;
+}
+
+static double code_max(int fmt) { return fmt == ORC_FMT_E4M3 ? 448.0 : 127.0; }
+
+/* The code of an unrounded value x = R / (sigma s), |x| <= code_max up to
+ * the rounding of sigma. */
+static int8_t code_round(int fmt, double x) {
+    if (fmt == ORC_FMT_E4M3) return (int8_t)(uint8_t)orc_e4m3_encode(x);
+    double c = nearbyint(x); /* default rounding mode: nearest, ties to even */
+    if (c > 127.0) c = 127.0;
+    if (c < -127.0) c = -127.0;
+    return (int8_t)c;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -154,12 +227,14 @@ int orc_recurrence(int n_units, int dk, int dv, int n_tok, int gate_kind, double
  *  - smoothing per key channel: s_j = sqrt(max_i |R[i,j]|), 1 when that is 0
  *    (SmoothQuant's migration strength 0.5; SmoothQuant is among the cited
  *    works); rounded to fp32;
- *  - scale per row: sigma_i = max_j |R[i,j] / s_j| / 127, rounded to fp32;
- *  - code = clamp(round-half-even(R[i,j] / (sigma_i s_j)), -127, 127) with the
- *    fp32-rounded sigma and s; rows with sigma_i = 0 get code 0.
+ *  - scale per row: sigma_i = max_j |R[i,j] / s_j| / qmax, rounded to fp32,
+ *    with qmax = 127 (INT8) or 448 (E4M3);
+ *  - code of x = R[i,j] / (sigma_i s_j), with the fp32-rounded sigma and s:
+ *    INT8 clamp(round-half-even(x), -127, 127); E4M3 the nearest E4M3 value,
+ *    ties to the even mantissa; rows with sigma_i = 0 get code 0.
  *
  * Outputs per unit u:
- *   codes    [dv][dk] int8
+ *   codes    [dv][dk] 8-bit codes (int8 values, or E4M3 bytes)
  *   sigma    [dv] fp32, smooth [dk] fp32
  *   comp_idx [n_c] int32 (c < dv: row c; c >= dv: column c - dv)
  *   comp_vec [n_c][D] fp32, D = max(dk, dv); a row slot holds k_c (dk values),
@@ -192,7 +267,7 @@ static void select_topn(int n_cand, int n_c, const double* score, int* sel, unsi
 
 /* One unit; all pointers already offset to unit u except that element
  * offsets below still use u = 0. */
-static void qz_unit(int dk, int dv, int n_c, int smooth_enable, const double* Su,
+static void qz_unit(int fmt, int dk, int dv, int n_c, int smooth_enable, const double* Su,
                     const int* force_sel_u, int8_t* codes, float* sigma, float* smooth,
                     int* comp_idx, float* comp_vec, double* x_out, double* scores_out) {
     const int D = dk > dv ? dk : dv;
@@ -270,7 +345,7 @@ static void qz_unit(int dk, int dv, int n_c, int smooth_enable, const double* Su
                 double a = fabs(R[(size_t)i * dk + j] / sj[j]);
                 if (a > m) m = a;
             }
-            float sg = (float)(m / 127.0);
+            float sg = (float)(m / code_max(fmt));
             sigma[(size_t)u * dv + i] = sg;
             for (int j = 0; j < dk; ++j) {
                 size_t e = (size_t)u * dv * dk + (size_t)i * dk + j;
@@ -281,10 +356,7 @@ static void qz_unit(int dk, int dv, int n_c, int smooth_enable, const double* Su
                 }
                 double x = R[(size_t)i * dk + j] / ((double)sg * sj[j]);
                 if (x_out) x_out[e] = x;
-                double c = nearbyint(x); /* default rounding mode: nearest, ties to even */
-                if (c > 127.0) c = 127.0;
-                if (c < -127.0) c = -127.0;
-                codes[e] = (int8_t)c;
+                codes[e] = code_round(fmt, x);
             }
         }
         free(R);
@@ -297,15 +369,16 @@ static void qz_unit(int dk, int dv, int n_c, int smooth_enable, const double* Su
     }
 }
 
-int orc_qz(int n_units, int dk, int dv, int n_c, int smooth_enable, const double* S,
+int orc_qz(int fmt, int n_units, int dk, int dv, int n_c, int smooth_enable, const double* S,
            const int* force_sel, int8_t* codes, float* sigma, float* smooth, int* comp_idx,
            float* comp_vec, double* x_out, double* scores_out) {
     if (n_units < 0 || dk <= 0 || dv <= 0 || n_c < 0 || n_c > dk + dv) return -1;
+    if (fmt != ORC_FMT_INT8 && fmt != ORC_FMT_E4M3) return -1;
     const int D = dk > dv ? dk : dv;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int u = 0; u < n_units; ++u) {
         size_t e = (size_t)u * dv * dk;
-        qz_unit(dk, dv, n_c, smooth_enable, S + e, force_sel ? force_sel + (size_t)u * n_c : NULL,
+        qz_unit(fmt, dk, dv, n_c, smooth_enable, S + e, force_sel ? force_sel + (size_t)u * n_c : NULL,
                 codes + e, sigma + (size_t)u * dv, smooth + (size_t)u * dk,
                 comp_idx + (size_t)u * n_c, comp_vec + (size_t)u * n_c * D,
                 x_out ? x_out + e : NULL, scores_out ? scores_out + (size_t)u * (dv + dk) : NULL);
@@ -321,7 +394,7 @@ int orc_qz(int n_units, int dk, int dv, int n_c, int smooth_enable, const double
  * window start; the compensator tokens are part of it.  A row slot adds
  * e_row k_c^T, a column slot adds v_c e_col^T.
  */
-static void dequant_unit(int dk, int dv, int n_c, const int8_t* codes, const float* sigma,
+static void dequant_unit(int fmt, int dk, int dv, int n_c, const int8_t* codes, const float* sigma,
                          const float* smooth, const int* comp_idx, const float* comp_vec,
                          double* Su) {
     const int D = dk > dv ? dk : dv;
@@ -330,7 +403,7 @@ static void dequant_unit(int dk, int dv, int n_c, const int8_t* codes, const flo
         for (int i = 0; i < dv; ++i)
             for (int j = 0; j < dk; ++j)
                 Su[(size_t)i * dk + j] = (double)sigma[(size_t)u * dv + i] *
-                                         (double)codes[(size_t)u * dv * dk + (size_t)i * dk + j] *
+                                         code_value(fmt, codes[(size_t)u * dv * dk + (size_t)i * dk + j]) *
                                          (double)smooth[(size_t)u * dk + j];
         for (int r = 0; r < n_c; ++r) {
             int c = comp_idx[(size_t)u * n_c + r];
@@ -344,13 +417,14 @@ static void dequant_unit(int dk, int dv, int n_c, const int8_t* codes, const flo
     }
 }
 
-int orc_dequant(int n_units, int dk, int dv, int n_c, const int8_t* codes, const float* sigma,
+int orc_dequant(int fmt, int n_units, int dk, int dv, int n_c, const int8_t* codes, const float* sigma,
                 const float* smooth, const int* comp_idx, const float* comp_vec, double* S) {
     if (n_units < 0 || dk <= 0 || dv <= 0 || n_c < 0) return -1;
+    if (fmt != ORC_FMT_INT8 && fmt != ORC_FMT_E4M3) return -1;
     const int D = dk > dv ? dk : dv;
 #pragma omp parallel for schedule(static)
     for (int u = 0; u < n_units; ++u) {
-        dequant_unit(dk, dv, n_c, codes + (size_t)u * dv * dk, sigma + (size_t)u * dv,
+        dequant_unit(fmt, dk, dv, n_c, codes + (size_t)u * dv * dk, sigma + (size_t)u * dv,
                      smooth + (size_t)u * dk, comp_idx + (size_t)u * n_c,
                      comp_vec + (size_t)u * n_c * D, S + (size_t)u * dv * dk);
     }
@@ -381,12 +455,13 @@ int orc_dequant(int n_units, int dk, int dv, int n_c, const int8_t* codes, const
  * bv [n_units][n_ent][dv], bb [n_units][n_ent], bg [n_units][n_ent] or
  * [n_units][n_ent][dk]; q [n_units][dk]; o [n_units][dv].
  */
-int orc_replay_output(int n_units, int dk, int dv, int n_c, int gate_kind, int n_ent,
+int orc_replay_output(int fmt, int n_units, int dk, int dv, int n_c, int gate_kind, int n_ent,
                       const int8_t* codes, const float* sigma, const float* smooth,
                       const int* comp_idx, const float* comp_vec, const float* bk,
                       const float* bv, const float* bb, const float* bg, const float* q,
                       double* o) {
     if (n_units < 0 || dk <= 0 || dv <= 0 || n_c < 0 || n_ent < 0) return -1;
+    if (fmt != ORC_FMT_INT8 && fmt != ORC_FMT_E4M3) return -1;
     const int D = dk > dv ? dk : dv;
     const int gstride = (gate_kind == ORC_GATE_SCALAR) ? 1 : dk;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -411,7 +486,7 @@ int orc_replay_output(int n_units, int dk, int dv, int n_c, int gate_kind, int n
         for (int i = 0; i < dv; ++i) {
             double a = 0.0;
             for (int j = 0; j < dk; ++j)
-                a += (double)codes[(size_t)u * dv * dk + (size_t)i * dk + j] *
+                a += code_value(fmt, codes[(size_t)u * dv * dk + (size_t)i * dk + j]) *
                      (double)smooth[(size_t)u * dk + j] * r[j];
             ou[i] = (double)sigma[(size_t)u * dv + i] * a + acc[i];
         }
@@ -455,11 +530,12 @@ int orc_replay_output(int n_units, int dk, int dv, int n_c, int gate_kind, int n
  *   o        [n_tok][n_units][dv]
  *   S_out    [n_units][dv][dk] final S_hat, or NULL
  */
-int orc_windowed_run(int n_units, int dk, int dv, int n_tok, int gate_kind, int W, int n_c,
+int orc_windowed_run(int fmt, int n_units, int dk, int dv, int n_tok, int gate_kind, int W, int n_c,
                      int smooth_enable, const double* S0, const float* q, const float* k,
                      const float* v, const float* beta, const float* gate, const int* force_at,
                      double* o, double* S_out) {
     if (n_units < 0 || dk <= 0 || dv <= 0 || n_tok < 0 || W < 1 || n_c < 0) return -1;
+    if (fmt != ORC_FMT_INT8 && fmt != ORC_FMT_E4M3) return -1;
     const int D = dk > dv ? dk : dv;
     const int gstride = (gate_kind == ORC_GATE_SCALAR) ? 1 : dk;
     int rc = 0;
@@ -473,8 +549,8 @@ int orc_windowed_run(int n_units, int dk, int dv, int n_tok, int gate_kind, int 
         int* ci = (int*)malloc(sizeof(int) * (size_t)(n_c > 0 ? n_c : 1));
         float* cv = (float*)malloc(sizeof(float) * (size_t)(n_c > 0 ? n_c : 1) * D);
         memcpy(S, S0 + (size_t)u * dv * dk, sizeof(double) * (size_t)dv * dk);
-        qz_unit(dk, dv, n_c, smooth_enable, S, NULL, cq, sg, sm, ci, cv, NULL, NULL);
-        dequant_unit(dk, dv, n_c, cq, sg, sm, ci, cv, S);
+        qz_unit(fmt, dk, dv, n_c, smooth_enable, S, NULL, cq, sg, sm, ci, cv, NULL, NULL);
+        dequant_unit(fmt, dk, dv, n_c, cq, sg, sm, ci, cv, S);
         int fill = 0;
         for (int t = 0; t < n_tok; ++t) {
             size_t tu = (size_t)t * n_units + u;
@@ -483,8 +559,8 @@ int orc_windowed_run(int n_units, int dk, int dv, int n_tok, int gate_kind, int 
             fill += 1;
             int forced = force_at && force_at[u] == t;
             if (fill == W || forced) {
-                qz_unit(dk, dv, n_c, smooth_enable, S, NULL, cq, sg, sm, ci, cv, NULL, NULL);
-                dequant_unit(dk, dv, n_c, cq, sg, sm, ci, cv, S);
+                qz_unit(fmt, dk, dv, n_c, smooth_enable, S, NULL, cq, sg, sm, ci, cv, NULL, NULL);
+                dequant_unit(fmt, dk, dv, n_c, cq, sg, sm, ci, cv, S);
                 fill = 0;
             }
         }

@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "lq_oracle.c")
 PINS = ["tests/test_oracle_recurrence.py", "tests/test_oracle_quantizer.py",
-        "tests/test_oracle_window.py"]
+        "tests/test_oracle_window.py", "tests/test_oracle_fp8.py"]
 
 MUTANTS = {
     "delta_sign": ("S[(size_t)i * dk + j] - (double)beta * Mk[i]", "S[(size_t)i * dk + j] + (double)beta * Mk[i]"),
@@ -24,7 +24,13 @@ MUTANTS = {
     "score_l1": ("a += Su[(size_t)i * dk + j] * Su[(size_t)i * dk + j];", "a += fabs(Su[(size_t)i * dk + j]);"),
     "tie_to_higher_index": ("score[c] > score[best]", "score[c] >= score[best]"),
     "smoothing_without_sqrt": ("s = (float)sqrt(a);", "s = (float)a;"),
-    "scale_divisor": ("(float)(m / 127.0)", "(float)(m / 128.0)"),
+    "scale_divisor": ("ORC_FMT_E4M3 ? 448.0 : 127.0", "ORC_FMT_E4M3 ? 448.0 : 128.0"),
+    "e4m3_scale_divisor": ("ORC_FMT_E4M3 ? 448.0 : 127.0", "ORC_FMT_E4M3 ? 240.0 : 127.0"),
+    "e4m3_exponent_bias": ("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
+    "e4m3_subnormal_scale": ("ldexp((double)m / 8.0, -6)", "ldexp((double)m / 8.0, -7)"),
+    "e4m3_ties_away": ("nearbyint(ldexp(a, 3 - E))", "round(ldexp(a, 3 - E))"),
+    "e4m3_no_subnormal_floor": ("if (E < -6) E = -6;", "if (E < -9) E = -9;"),
+    "e4m3_carry_dropped": ("e = E + 8;", "e = E + 7;"),
     "ties_away_from_zero": ("double c = nearbyint(x);", "double c = round(x);"),
     "column_slot_unmasked": ("row_sel[i] ? 0.0f : (float)Su", "0 ? 0.0f : (float)Su"),
     "replay_forward_order": ("for (int i = n_ent - 1; i >= 0; --i)", "for (int i = 0; i < n_ent; ++i)"),
