@@ -45,6 +45,8 @@ def parse_args():
                     help="tiny_gdn | gdn_decode | kda_decode | gdn_serving | hybrid_stack")
     ap.add_argument("--window", type=int, default=None, help="override the workload's window W (1..256)")
     ap.add_argument("--n-comp", type=int, default=None, help="override the workload's compensator count (0..16)")
+    ap.add_argument("--format", default="int8", choices=("int8", "e4m3"),
+                    help="8-bit code format of the stored state")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-fp32", action="store_true", help="skip the FP32-state comparison loop")
@@ -131,7 +133,7 @@ def projected(wl, w, h):
 # CPU baseline: the oracle as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl, n_tok, target_s):
+def cpu_baseline(wl, n_tok, target_s, fmt="int8"):
     import numpy as np
 
     import oracle as orc
@@ -149,7 +151,7 @@ def cpu_baseline(wl, n_tok, target_s):
     cal_tok = min(n_tok, 2 * wl.window)
     S0, st = sample(cal_units, cal_tok)
     t0 = time.perf_counter()
-    orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp)
+    orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp, fmt=fmt)
     rate = len(cal_units) * cal_tok / max(time.perf_counter() - t0, 1e-6)
     n_units = int(max(1, min(wl.n_units, rate * target_s / n_tok)))
     # the whole workload may take well under target_s: repeat it to get a steady figure
@@ -158,7 +160,7 @@ def cpu_baseline(wl, n_tok, target_s):
     S0, st = sample(units, n_tok)
     t0 = time.perf_counter()
     for _ in range(reps):
-        orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp)
+        orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp, fmt=fmt)
     dt = time.perf_counter() - t0
     cpu_model = ""
     try:
@@ -181,8 +183,13 @@ def cpu_baseline(wl, n_tok, target_s):
 # measured HBM traffic (rocprofv3 --pmc), valid only for the kernel it was taken on
 # ---------------------------------------------------------------------------
 
-def measured_traffic(workload):
-    p = os.path.join(ROOT, "profiles", f"decode_int8_{workload}_traffic.json")
+def traffic_file(workload, fmt="int8"):
+    tag = workload if fmt == "int8" else f"{workload}_{fmt}"
+    return os.path.join(ROOT, "profiles", f"decode_q8_{tag}_traffic.json")
+
+
+def measured_traffic(workload, fmt="int8"):
+    p = traffic_file(workload, fmt)
     try:
         rec = json.load(open(p))
     except Exception:
@@ -222,7 +229,8 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     gen = torch.Generator(dev).manual_seed(1000 + wl.seed)
-    cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind)
+    code_format = {"int8": lq.LQ_CODE_INT8, "e4m3": lq.LQ_CODE_E4M3}[args.format]
+    cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind, code_format)
     stream = torch.cuda.current_stream()
 
     # ---- start states: FP32 prefill through the FP32-state kernel (input synthesis)
@@ -254,7 +262,7 @@ def main():
     force_dev = torch.zeros(wl.n_seq, dtype=torch.uint8, device=dev)
     flush_calls = []
 
-    def int8_step(t):
+    def q8_step(t):
         for layer in range(L):
             tk = toks[layer][t]
             for st in blobs[layer]:
@@ -293,33 +301,34 @@ def main():
         return float(np.median(times))
 
     for t in range(warmup):
-        int8_step(t)
+        q8_step(t)
     n_flush_warm = len(flush_calls)
     # the timed steps run as one graph: kernels back to back, no host launch cost
     repeats = args.repeats if steps % W == 0 else 1
-    int8_ms = timed_graph(lambda: [int8_step(t) for t in range(warmup, n_tok)], repeats)
+    q8_ms = timed_graph(lambda: [q8_step(t) for t in range(warmup, n_tok)], repeats)
     flags = [lq.lq_read_status(cfg, st) for bl in blobs for st in bl]
     if any(flags):
         raise RuntimeError(f"device flags set during the run: {flags}")
 
     result = {
         "metric": METRIC,
-        "value": U * L * R * steps / (int8_ms * 1e-3),
+        "value": U * L * R * steps / (q8_ms * 1e-3),
         "unit": "seq·head·tokens/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
-        "ms_per_step": int8_ms / steps,
+        "ms_per_step": q8_ms / steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "state_dtype": "int8",
+        "state_dtype": args.format,
         "data": "synthetic",
         "config": {
             "workload": wl.name,
             "layers": L, "n_seq": wl.n_seq, "n_v_heads": wl.n_v_heads, "n_k_heads": wl.n_k_heads,
             "d_k": d, "d_v": d, "gate": wl.gate, "window": W, "n_comp": wl.n_comp,
+            "code_format": args.format,
             "prefill": wl.prefill, "units": U * L * R, "state_copies": R,
         },
         "timing": f"HIP graph of the timed steps, median of {repeats} replays, HIP events around each",
@@ -346,8 +355,8 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": achieved / HBM_PEAK_GBS,
-        "traffic": measured_traffic(wl.name),
-        "kernel": "decode_int8_kernel",
+        "traffic": measured_traffic(wl.name, args.format),
+        "kernel": "decode_q8_kernel",
         "avg_launch_us": avg_launch_s * 1e6,
         "alg_bytes_per_launch": avg_bytes,
         "launches": n_launch,
@@ -376,11 +385,11 @@ def main():
             "value": U * L * R * steps / (fp32_ms * 1e-3),
             "ms_per_step": fp32_ms / steps,
             "alg_GBps": fp32_bytes / (fp32_ms / steps * 1e-3) / 1e9,
-            "speedup_int8_vs_fp32": fp32_ms / int8_ms,
+            "speedup_vs_fp32": fp32_ms / q8_ms,
         }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds, args.format)
     print(json.dumps(result), flush=True)
 
 

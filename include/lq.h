@@ -72,6 +72,10 @@ extern "C" {
 #define LQ_GATE_SCALAR 0  /* Gated DeltaNet: one alpha per unit and token */
 #define LQ_GATE_CHANNEL 1 /* Kimi Delta Attention: one gate per key channel */
 
+/* state code formats (the 8-bit codes of the stored state) */
+#define LQ_CODE_INT8 0 /* integers in [-127, 127] */
+#define LQ_CODE_E4M3 1 /* 8-bit floats: OCP E4M3 without infinities, magnitudes up to 448 */
+
 /* sticky device flags (lq_read_status) */
 #define LQ_DEV_WINDOW_OVERFLOW 0x1u /* lq_decode_step found a full window: that unit's o is NaN, nothing appended */
 #define LQ_DEV_NONFINITE_INPUT 0x2u /* a decode input (q, k, v, beta, gate) was NaN or Inf */
@@ -80,6 +84,7 @@ extern "C" {
  * Problem description.  Supported: d_k == d_v in {64, 128};
  * 1 <= window <= 256; 0 <= n_comp <= 16; n_seq, n_v_heads, n_k_heads >= 1;
  * n_v_heads % n_k_heads == 0; gate_kind in {LQ_GATE_SCALAR, LQ_GATE_CHANNEL};
+ * code_format in {LQ_CODE_INT8, LQ_CODE_E4M3};
  * the unit count n_seq * n_v_heads below 2^31.
  */
 typedef struct lq_config {
@@ -91,6 +96,9 @@ typedef struct lq_config {
     int32_t window;   /* W: tokens per quantization window */
     int32_t n_comp;   /* compensator lines kept per unit */
     int32_t gate_kind;
+    int32_t code_format; /* LQ_CODE_INT8 (the review's INT8) or LQ_CODE_E4M3 (the
+                            abstract's "8-bit" read as a floating-point format): the
+                            scales are chosen so the largest code is 127 or 448 */
 } lq_config;
 
 /*
@@ -99,7 +107,7 @@ typedef struct lq_config {
  * the whole decode state.
  *   status    uint32 sticky flags
  *   fill      int32 [units]            tokens buffered in the current window
- *   codes     int8  [units][d_v][d_k]  the INT8 state
+ *   codes     8-bit [units][d_v][d_k]  the quantized state (int8, or E4M3 bytes)
  *   sigma     fp32  [units][d_v]       per-row scales
  *   smooth    fp32  [units][d_k]       per-key-channel smoothing factors
  *   comp_idx  int32 [units][n_comp]    c < d_v: row c; c >= d_v: column c - d_v

@@ -25,6 +25,8 @@ LQ_EUNSUPPORTED = -2
 LQ_EHIP = -3
 LQ_GATE_SCALAR = 0
 LQ_GATE_CHANNEL = 1
+LQ_CODE_INT8 = 0
+LQ_CODE_E4M3 = 1
 LQ_DEV_WINDOW_OVERFLOW = 0x1
 LQ_DEV_NONFINITE_INPUT = 0x2
 
@@ -41,7 +43,8 @@ class LQError(RuntimeError):
 
 class _CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("n_seq", "n_v_heads", "n_k_heads", "d_k", "d_v", "window", "n_comp", "gate_kind")]
+                ("n_seq", "n_v_heads", "n_k_heads", "d_k", "d_v", "window", "n_comp", "gate_kind",
+                 "code_format")]
 
 
 _LAYOUT_FIELDS = ("total_bytes", "status", "fill", "codes", "sigma", "smooth", "comp_idx",
@@ -63,6 +66,7 @@ class Config:
     window: int
     n_comp: int
     gate_kind: int = LQ_GATE_SCALAR
+    code_format: int = LQ_CODE_INT8
 
     @property
     def n_units(self) -> int:

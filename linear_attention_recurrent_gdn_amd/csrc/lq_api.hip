@@ -17,6 +17,7 @@ int32_t check_config(const lq_config* c) {
         return LQ_EINVAL;
     if (c->n_v_heads % c->n_k_heads != 0) return LQ_EINVAL;
     if (c->gate_kind != LQ_GATE_SCALAR && c->gate_kind != LQ_GATE_CHANNEL) return LQ_EINVAL;
+    if (c->code_format != LQ_CODE_INT8 && c->code_format != LQ_CODE_E4M3) return LQ_EINVAL;
     if ((int64_t)c->n_seq * c->n_v_heads >= ((int64_t)1 << 31)) return LQ_EUNSUPPORTED;
     if (c->d_k != c->d_v || (c->d_k != 64 && c->d_k != 128)) return LQ_EUNSUPPORTED;
     if (c->window > 256 || c->n_comp > 16) return LQ_EUNSUPPORTED;
@@ -33,6 +34,7 @@ Dims dims_of(const lq_config* c) {
     d.group = c->n_v_heads / c->n_k_heads;
     d.window = c->window;
     d.n_comp = c->n_comp;
+    d.code_format = c->code_format;
     return d;
 }
 
@@ -97,7 +99,7 @@ int32_t lq_decode_step(const lq_config* cfg, void* state, const float* q, const 
     a.beta = beta;
     a.gate = gate;
     a.o = o;
-    return hip_status(launch_decode_int8(a, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+    return hip_status(launch_decode_q8(a, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
 }
 
 int32_t lq_window_flush(const lq_config* cfg, void* state, const uint8_t* force_mask,

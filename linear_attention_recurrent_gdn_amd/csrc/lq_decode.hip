@@ -1,6 +1,7 @@
 // lq_decode.hip -- per-token decode kernels for gfx950.
 //
-// decode_int8_kernel: one token of the windowed INT8 scheme.  The arXiv
+// decode_q8_kernel: one token of the windowed 8-bit scheme (INT8 codes, or
+// E4M3 8-bit floats: the review says INT8, the abstract only "8-bit").  The arXiv
 // 2609.38166 abstract ("Abstract (arXiv)" section, mlsanity.com paper page):
 // within a window, outputs are computed from the fixed low-bit state together
 // with high-precision buffered updates.  The bedrocknews.com review: the cost
@@ -12,10 +13,12 @@
 //     for i = n..1:  c = k_i . r;  acc += beta_i c v_i;  r = g_i * (r - beta_i c k_i)
 //     o = sigma * (Q (s * r)) + sum_c v_c (k_c . r) + acc
 // so r = A_1..A_n q and acc = sum_i beta_i v_i k_i^T A_{i+1}..A_n q, and o is
-// S_n q.  The INT8 tile, sigma, s and compensators are only read.
+// S_n q.  The 8-bit tile, sigma, s and compensators are only read.  Q holds
+// the code values: the integers themselves, or the E4M3 values, which the
+// gfx950 conversion v_cvt_pk_f32_fp8 produces exactly (two per instruction).
 //
 // Mapping: one workgroup of four wavefronts per unit.  Each wavefront
-// requests its quarter of the INT8 tile (4 KiB at d = 128) with 16-byte
+// requests its quarter of the 8-bit tile (4 KiB at d = 128) with 16-byte
 // coalesced loads at kernel start.  Wavefront 0 runs the reverse pass: the
 // buffered tokens stream through a register ring refilled a fixed number of
 // tokens ahead (so the wait counts are exact and memory latency is paid once
@@ -36,6 +39,8 @@
 namespace lq {
 
 namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int EPL>
 struct Vec {
@@ -76,8 +81,8 @@ struct Entry {
 
 }  // namespace
 
-template <int D, bool KDA, int P, int NWB>
-__global__ __launch_bounds__(256) void decode_int8_kernel(DecodeArgs a) {
+template <int D, bool KDA, int P, int NWB, int FMT>
+__global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     constexpr int EPL = D / kWave;   // state elements per lane in the chain wave
     constexpr int GE = KDA ? EPL : 1;
     constexpr int RW = D / 4;        // tile rows per wave
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeArgs a) {
     const int kh = h / a.dm.group;
     const size_t kvec = ((size_t)s * a.dm.n_k_heads + kh);  // key-head row of q, k
 
-    // ---- every wave owns a quarter of the INT8 tile (RW rows) and writes those rows of o
+    // ---- every wave owns a quarter of the 8-bit tile (RW rows) and writes those rows of o
     const int cg = lane % LPR;  // this lane's 16-column group
     const int row0 = wave * RW;
     const uint4* tile = reinterpret_cast<const uint4*>(a.blob.codes + ((size_t)u * D + row0) * D);
@@ -287,10 +292,20 @@ __global__ __launch_bounds__(256) void decode_int8_kernel(DecodeArgs a) {
         float p0 = 0.f, p1 = 0.f;
 #pragma unroll
         for (int wi = 0; wi < 4; ++wi) {
+            if constexpr (FMT == LQ_CODE_E4M3) {
+                // bytes 0, 1 and 2, 3 of the word (columns 4 wi .. 4 wi + 3)
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[wi], false);
+                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[wi], true);
+                p0 = __builtin_fmaf(lo.x, xs[4 * wi + 0], p0);
+                p1 = __builtin_fmaf(lo.y, xs[4 * wi + 1], p1);
+                p0 = __builtin_fmaf(hi.x, xs[4 * wi + 2], p0);
+                p1 = __builtin_fmaf(hi.y, xs[4 * wi + 3], p1);
+            } else {
 #pragma unroll
-            for (int by = 0; by < 4; by += 2) {
-                p0 = __builtin_fmaf((float)((int)(wd[wi] << (24 - 8 * by)) >> 24), xs[4 * wi + by], p0);
-                p1 = __builtin_fmaf((float)((int)(wd[wi] << (16 - 8 * by)) >> 24), xs[4 * wi + by + 1], p1);
+                for (int by = 0; by < 4; by += 2) {
+                    p0 = __builtin_fmaf((float)((int)(wd[wi] << (24 - 8 * by)) >> 24), xs[4 * wi + by], p0);
+                    p1 = __builtin_fmaf((float)((int)(wd[wi] << (16 - 8 * by)) >> 24), xs[4 * wi + by + 1], p1);
+                }
             }
         }
         float p = p0 + p1;
@@ -388,23 +403,31 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
 #define LQ_RING_KDA 6
 #endif
 
-template <int NWB>
-void launch_decode_int8_w(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
+template <int NWB, int FMT>
+void launch_decode_q8_w(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
     const dim3 grid(a.dm.n_units), block(256);
     if (d == 128) {
         if (gate_kind == LQ_GATE_CHANNEL)
-            hipLaunchKernelGGL((decode_int8_kernel<128, true, LQ_RING_KDA, NWB>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<128, true, LQ_RING_KDA, NWB, FMT>), grid, block, 0, st, a);
         else
-            hipLaunchKernelGGL((decode_int8_kernel<128, false, LQ_RING_GDN, NWB>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<128, false, LQ_RING_GDN, NWB, FMT>), grid, block, 0, st, a);
     } else {
-        if (gate_kind == LQ_GATE_CHANNEL) hipLaunchKernelGGL((decode_int8_kernel<64, true, 16, NWB>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((decode_int8_kernel<64, false, 16, NWB>), grid, block, 0, st, a);
+        if (gate_kind == LQ_GATE_CHANNEL)
+            hipLaunchKernelGGL((decode_q8_kernel<64, true, 16, NWB, FMT>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((decode_q8_kernel<64, false, 16, NWB, FMT>), grid, block, 0, st, a);
     }
 }
 
-hipError_t launch_decode_int8(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
-    if (a.dm.window <= 2 * kWave) launch_decode_int8_w<2>(a, d, gate_kind, st);
-    else launch_decode_int8_w<4>(a, d, gate_kind, st);
+template <int FMT>
+void launch_decode_q8_f(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
+    if (a.dm.window <= 2 * kWave) launch_decode_q8_w<2, FMT>(a, d, gate_kind, st);
+    else launch_decode_q8_w<4, FMT>(a, d, gate_kind, st);
+}
+
+hipError_t launch_decode_q8(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
+    if (a.dm.code_format == LQ_CODE_E4M3) launch_decode_q8_f<LQ_CODE_E4M3>(a, d, gate_kind, st);
+    else launch_decode_q8_f<LQ_CODE_INT8>(a, d, gate_kind, st);
     return hipGetLastError();
 }
 

@@ -44,8 +44,9 @@
 //      columns) go to fp32 compensator slots, rows taken whole, columns with
 //      the selected rows' entries zeroed; the residual R has those lines
 //      zeroed; s_j = sqrt(max_i |R_ij|) (1 if zero), sigma_i =
-//      max_j |R_ij / s_j| / 127, both fp32; codes = clamp(rne(R_ij /
-//      (sigma_i s_j)), -127, 127).
+//      max_j |R_ij / s_j| / qmax, both fp32; codes of x = R_ij /
+//      (sigma_i s_j): INT8 clamp(rne(x), -127, 127) with qmax = 127, or
+//      the nearest E4M3 8-bit float (ties to even) with qmax = 448.
 // Row reductions combine the four lanes that share a row (permlane swaps);
 // column reductions reduce-scatter over the 16 lanes of a row group, then
 // combine the wavefronts through LDS in a fixed order, so results are
@@ -58,6 +59,7 @@ namespace lq {
 namespace {
 
 typedef double v4d __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr double kRescaleBelow = 0x1p-200;  // fold the gate product into T below this
 constexpr double kMinGate = 0x1p-45;        // per-token gate floor inside the flush
@@ -139,6 +141,32 @@ __device__ __forceinline__ double shfl_xor_f64(double x, int m) {
     const int lo = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)b);
     const int hi = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(b >> 32));
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// E4M3 byte of x (FP64): the nearest value of the 8-bit float format with
+// 4 exponent bits (bias 7) and 3 mantissa bits, ties to the even mantissa,
+// magnitudes above the largest finite 448 taken as 448, zero as the byte 0.
+// Around a magnitude a the values are spaced 2^(E-3), E = max(floor(log2 a),
+// -6); a / 2^(E-3) rounds to k = m (subnormal), 8 + m, or 16 (next binade).
+// Both scalings are exact powers of two built from the exponent bits.
+__device__ __forceinline__ uint32_t e4m3_code(double x) {
+    const double ax = fmin(fabs(x), 448.0);
+    const int E = max((int)((__builtin_bit_cast(uint64_t, ax) >> 52) & 0x7FF) - 1023, -6);
+    const double up = __builtin_bit_cast(double, (uint64_t)(1023 + 3 - E) << 52);  // 2^(3-E)
+    const int k = (int)rint(ax * up);
+    if (k == 0) return 0u;
+    uint32_t e, m;
+    if (k < 8) {
+        e = 0u;
+        m = (uint32_t)k;
+    } else if (k == 16) {
+        e = (uint32_t)(E + 8);
+        m = 0u;
+    } else {
+        e = (uint32_t)(E + 7);
+        m = (uint32_t)(k - 8);
+    }
+    return (x < 0.0 ? 0x80u : 0u) | (e << 3) | m;
 }
 
 __device__ __forceinline__ float pick4(const float4& f, int i) {
@@ -243,15 +271,26 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             }
         } else {
             const double sgr = (double)a.blob.sigma[(size_t)u * D + n];
+            const bool e4m3 = a.dm.code_format == LQ_CODE_E4M3;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const float4 s4 = *reinterpret_cast<const float4*>(a.blob.smooth + (size_t)u * D + 16 * b + 4 * q);
                 const uint32_t wd = *reinterpret_cast<const uint32_t*>(a.blob.codes + ((size_t)u * D + n) * D + 16 * b + 4 * q);
+                float cv[4];
+                if (e4m3) {
+                    // exact: every E4M3 value is an fp32 value
+                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd, false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd, true);
+                    cv[0] = lo.x;
+                    cv[1] = lo.y;
+                    cv[2] = hi.x;
+                    cv[3] = hi.y;
+                } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int code = (int)(wd << (24 - 8 * r)) >> 24;
-                    T[b][r] = sgr * (double)code * (double)pick4(s4, r);
+                    for (int r = 0; r < 4; ++r) cv[r] = (float)((int)(wd << (24 - 8 * r)) >> 24);
                 }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) T[b][r] = sgr * (double)cv[r] * (double)pick4(s4, r);
             }
             // compensator lines: a row slot adds its line to the four lanes of
             // that row, a column slot adds one value per row; every load is
@@ -645,7 +684,8 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) mx = fmax(mx, fabs(T[b][r] * lds_ismooth[16 * b + 4 * q + r]));
             mx = across_rows<true>(mx);
-            const float sg = (float)(mx / 127.0);
+            const bool e4m3 = a.dm.code_format == LQ_CODE_E4M3;
+            const float sg = (float)(mx / (e4m3 ? 448.0 : 127.0));
             if (q == 0) a.blob.sigma[(size_t)u * D + n] = sg;
             const double isg = sg != 0.0f ? 1.0 / (double)sg : 0.0;
 #pragma unroll
@@ -653,13 +693,16 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 uint32_t packed = 0u;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    int code = 0;
+                    uint32_t code = 0u;
                     if (sg != 0.0f) {
-                        double x = rint(T[b][r] * (isg * lds_ismooth[16 * b + 4 * q + r]));
-                        x = fmin(fmax(x, -127.0), 127.0);
-                        code = (int)x;
+                        const double x = T[b][r] * (isg * lds_ismooth[16 * b + 4 * q + r]);
+                        if (e4m3) {
+                            code = e4m3_code(x);
+                        } else {
+                            code = (uint32_t)(int)fmin(fmax(rint(x), -127.0), 127.0) & 0xFFu;
+                        }
                     }
-                    packed |= ((uint32_t)code & 0xFFu) << (8 * r);
+                    packed |= code << (8 * r);
                 }
                 *reinterpret_cast<uint32_t*>(a.blob.codes + ((size_t)u * D + n) * D + 16 * b + 4 * q) = packed;
             }

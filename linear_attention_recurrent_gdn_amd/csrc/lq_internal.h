@@ -85,6 +85,7 @@ struct Dims {
     int group;      // n_v_heads / n_k_heads
     int window;
     int n_comp;
+    int code_format;  // LQ_CODE_INT8 or LQ_CODE_E4M3
 };
 
 struct DecodeArgs {
@@ -122,7 +123,7 @@ struct MatArgs {
 
 // Host launchers (lq_decode.hip / lq_flush.hip).  Return hipSuccess or the
 // launch error.
-hipError_t launch_decode_int8(const DecodeArgs& a, int d, int gate_kind, hipStream_t st);
+hipError_t launch_decode_q8(const DecodeArgs& a, int d, int gate_kind, hipStream_t st);
 hipError_t launch_decode_fp32(const Fp32DecodeArgs& a, int d, int gate_kind, hipStream_t st);
 hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, hipStream_t st);
 hipError_t launch_clear_status(uint32_t* status, hipStream_t st);

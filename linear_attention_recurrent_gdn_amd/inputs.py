@@ -56,6 +56,7 @@ class Workload:
     layers: int = 1
     projected: bool = False  # inputs come from random bf16 projections of a hidden state
     hidden: int = 0
+    code_format: str = "int8"  # 8-bit code format of the stored state: "int8" or "e4m3"
 
     @property
     def n_units(self) -> int:

@@ -2,7 +2,7 @@
 
 Three commands:
 
-  window   --workload W
+  window   --workload W [--format int8|e4m3]
       Runs, eagerly on cuda:0, one plain device-to-device copy of COPY_BYTES
       (the calibration kernel for the memory counters), then one whole window
       of decode launches (every unit at fill j = 0 .. W-1) on a freshly
@@ -38,7 +38,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
-DECODE_KERNEL = "decode_int8_kernel"
+DECODE_KERNEL = "decode_q8_kernel"
 COPY_KERNEL = "copyBuffer"
 
 
@@ -48,7 +48,7 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def run_window(workload: str) -> None:
+def run_window(workload: str, fmt: str = "int8") -> None:
     import torch
 
     import linear_attention_recurrent_gdn_amd as lq
@@ -59,7 +59,8 @@ def run_window(workload: str) -> None:
     U, d, W = wl.n_units, wl.d, wl.window
     dev = torch.device("cuda", 0)
     gen = torch.Generator(dev).manual_seed(2000 + wl.seed)
-    cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind)
+    code_format = {"int8": lq.LQ_CODE_INT8, "e4m3": lq.LQ_CODE_E4M3}[fmt]
+    cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind, code_format)
 
     src = torch.empty(COPY_BYTES // 4, device=dev).normal_(generator=gen)
     dst = torch.empty_like(src)
@@ -200,6 +201,7 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     a = sub.add_parser("window")
     a.add_argument("--workload", default="gdn_decode")
+    a.add_argument("--format", default="int8", choices=("int8", "e4m3"))
     b = sub.add_parser("traffic")
     b.add_argument("--workload", default="gdn_decode")
     b.add_argument("--fetch", required=True)
@@ -213,7 +215,7 @@ def main(argv=None):
     c.add_argument("--out", required=True)
     args = ap.parse_args(argv)
     if args.cmd == "window":
-        run_window(args.workload)
+        run_window(args.workload, args.format)
     elif args.cmd == "hbm":
         hbm()
     elif args.cmd == "traffic":

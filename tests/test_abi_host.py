@@ -75,6 +75,7 @@ def test_state_bytes_matches_int8_footprint(lib):
     (dict(n_seq=0), lq.LQ_EINVAL),
     (dict(n_v_heads=3, n_k_heads=2), lq.LQ_EINVAL),
     (dict(gate_kind=7), lq.LQ_EINVAL),
+    (dict(code_format=2), lq.LQ_EINVAL),
     (dict(window=0), lq.LQ_EINVAL),
     (dict(n_comp=-1), lq.LQ_EINVAL),
     (dict(d_k=96, d_v=96), lq.LQ_EUNSUPPORTED),

@@ -23,9 +23,10 @@ def sample_units(wl, n=24, seed=7):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name", ["tiny_gdn", "gdn_decode", "kda_decode", "gdn_serving"])
-def test_fullsize_parity(name):
-    wl = I.WORKLOADS[name]
+@pytest.mark.parametrize("name,fmt", [("tiny_gdn", "int8"), ("gdn_decode", "int8"), ("kda_decode", "int8"),
+                                      ("gdn_serving", "int8"), ("gdn_decode", "e4m3"), ("kda_decode", "e4m3")])
+def test_fullsize_parity(name, fmt):
+    wl = I.WORKLOADS[name].scaled(code_format=fmt)
     checked = None if wl.n_units == 1 else sample_units(wl)
     n_tok = wl.decode + (wl.window if wl.stagger else 0)  # staggered: warm-up window first
     rep = parity.run(wl, n_tokens=n_tok, checked=checked, dequant_every=wl.window // 2 + 1)

@@ -55,6 +55,14 @@ CASES = {
     "gdn_d64_w144": (small("gdn_decode", name="gdn_d64_w144", n_seq=2, n_v_heads=2, n_k_heads=2,
                            d=64, prefill=16, decode=160, window=144, n_comp=2, outlier_rows=0,
                            outlier_cols=0), dict(dequant_every=61)),
+    # the E4M3 code format: GDN with outlier lines, KDA with heavy tails, d = 64
+    "gdn_small_e4m3": (small("gdn_decode", name="gdn_small_e4m3", n_seq=3, n_v_heads=5, n_k_heads=5,
+                             prefill=96, decode=150, code_format="e4m3"), dict(dequant_every=37)),
+    "kda_small_e4m3": (small("kda_decode", name="kda_small_e4m3", n_seq=2, n_v_heads=3, n_k_heads=3,
+                             prefill=48, decode=170, code_format="e4m3"), dict(dequant_every=41)),
+    "gqa_d64_e4m3": (small("gdn_decode", name="gqa_d64_e4m3", n_seq=2, n_v_heads=4, n_k_heads=2, d=64,
+                           prefill=40, decode=70, window=32, n_comp=3, code_format="e4m3"),
+                     dict(dequant_every=23)),
     # zero start state (no prefill) with the channel gate at d=128
     "kda_zero_start": (small("kda_decode", name="kda_zero_start", n_seq=1, n_v_heads=2,
                              n_k_heads=2, prefill=0, decode=20, window=8, n_comp=4), dict()),
