@@ -60,7 +60,10 @@ def _load():
         lib.orc_qz.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
         lib.orc_dequant.argtypes = [I, I, I, I, I, P, P, P, P, P, P]
         lib.orc_replay_output.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
-        lib.orc_windowed_run.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        lib.orc_windowed_run.argtypes = [I, I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        lib.orc_fp16_round.argtypes = [ctypes.c_float]
+        lib.orc_fp16_round.restype = ctypes.c_float
+        lib.orc_fp16_round_array.argtypes = [ctypes.c_long, P, P]
         lib.orc_e4m3_value.argtypes = [I]
         lib.orc_e4m3_value.restype = ctypes.c_double
         lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
@@ -134,6 +137,15 @@ def e4m3_value(code: int) -> float:
 def e4m3_encode(x: float) -> int:
     """E4M3 byte of the nearest value to x (ties to the even mantissa, saturating at 448)."""
     return _load().orc_e4m3_encode(float(x))
+
+
+def fp16_round(x) -> np.ndarray:
+    """Each fp32 value as stored in a binary16 buffer (nearest, ties to even,
+    saturating at 65504), returned as fp32."""
+    x = _f32(x)
+    out = np.empty_like(x)
+    _load().orc_fp16_round_array(x.size, _p(x), _p(out))
+    return out
 
 
 def code_values(codes, fmt: str = "int8") -> np.ndarray:
@@ -223,13 +235,15 @@ def replay_output(blob: Blob, bk, bv, bb, bg, q):
 
 
 def windowed_run(S0, q, k, v, beta, gate, W, n_c, smooth=True, force_at=None, want_state=False,
-                 fmt="int8"):
+                 fmt="int8", buffer="fp32"):
     """O2: the windowed scheme in its definitional form over T tokens.
 
     S0 [U, dv, dk] unquantized start state; token-major inputs as in
     ``recurrence``.  ``force_at[u]`` = token index after which unit u takes a
     forced partial flush (-1: none).  W=1, n_c=0, smooth=False gives the naive
-    per-token quantization; ``fmt`` selects the code format ("int8" or "e4m3").
+    per-token quantization; ``fmt`` selects the code format ("int8" or "e4m3");
+    ``buffer="fp16"`` rounds every token's k and v to binary16 as the window
+    buffer stores them.
     Returns o [T, U, dv] (and the final state).
     """
     lib = _load()
@@ -241,7 +255,9 @@ def windowed_run(S0, q, k, v, beta, gate, W, n_c, smooth=True, force_at=None, wa
     fa = None if force_at is None else np.ascontiguousarray(force_at, np.int32)
     o = np.zeros((T, U, dv), np.float64)
     Sout = np.zeros((U, dv, dk), np.float64) if want_state else None
-    rc = lib.orc_windowed_run(_fmt(fmt), U, dk, dv, T, gk, W, n_c, 1 if smooth else 0, _p(S0), _p(q),
+    if buffer not in ("fp32", "fp16"):
+        raise ValueError(f"unknown buffer format {buffer!r}")
+    rc = lib.orc_windowed_run(_fmt(fmt), 1 if buffer == "fp16" else 0, U, dk, dv, T, gk, W, n_c, 1 if smooth else 0, _p(S0), _p(q),
                               _p(k), _p(v), _p(beta), _p(gate), _p(fa), _p(o), _p(Sout))
     assert rc == 0
     return (o, Sout) if want_state else o

@@ -116,6 +116,38 @@ int orc_e4m3_encode(double x) {
     return (x < 0.0 ? 0x80 : 0) | (e << 3) | m;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Buffer precision                                                          */
+/* ------------------------------------------------------------------------ */
+/*
+ * [ABS]: inside a window the outputs use high-precision buffered updates.
+ * READING: the buffer holds each token's k and v either in fp32 (as given)
+ * or in IEEE binary16 (1 sign bit, 5 exponent bits with bias 15, 10 mantissa
+ * bits; subnormals m/1024 * 2^-14; largest finite 65504), the buffered token
+ * then being the rounded one everywhere (its own output, later replays and
+ * the window-end state).  Rounding is to nearest, ties to the even mantissa;
+ * magnitudes above 65504 are stored as 65504 (saturation, READING) and NaN
+ * stays NaN.  Around a magnitude a the binary16 values are spaced 2^(E-10),
+ * E = max(floor(log2 a), -14).
+ */
+float orc_fp16_round(float xf) {
+    const double x = (double)xf;
+    if (isnan(x)) return xf;
+    double a = fabs(x);
+    if (a > 65504.0) a = 65504.0;
+    if (a == 0.0) return xf;
+    int ex;
+    frexp(a, &ex); /* a = f * 2^ex, f in [0.5, 1) */
+    int E = ex - 1;
+    if (E < -14) E = -14;
+    const double r = ldexp(nearbyint(ldexp(a, 10 - E)), E - 10);
+    return (float)(x < 0.0 ? -r : r);
+}
+
+void orc_fp16_round_array(long n, const float* in, float* out) {
+    for (long i = 0; i < n; ++i) out[i] = orc_fp16_round(in[i]);
+}
+
 static double code_value(int fmt, int8_t c) {
     return fmt == ORC_FMT_E4M3 ? orc_e4m3_value((uint8_t)c) : (double)c;
 }
@@ -530,7 +562,7 @@ int orc_replay_output(int fmt, int n_units, int dk, int dv, int n_c, int gate_ki
  *   o        [n_tok][n_units][dv]
  *   S_out    [n_units][dv][dk] final S_hat, or NULL
  */
-int orc_windowed_run(int fmt, int n_units, int dk, int dv, int n_tok, int gate_kind, int W, int n_c,
+int orc_windowed_run(int fmt, int buf_fp16, int n_units, int dk, int dv, int n_tok, int gate_kind, int W, int n_c,
                      int smooth_enable, const double* S0, const float* q, const float* k,
                      const float* v, const float* beta, const float* gate, const int* force_at,
                      double* o, double* S_out) {
@@ -548,14 +580,24 @@ int orc_windowed_run(int fmt, int n_units, int dk, int dv, int n_tok, int gate_k
         float* sm = (float*)malloc(sizeof(float) * (size_t)dk);
         int* ci = (int*)malloc(sizeof(int) * (size_t)(n_c > 0 ? n_c : 1));
         float* cv = (float*)malloc(sizeof(float) * (size_t)(n_c > 0 ? n_c : 1) * D);
+        float* kr = (float*)malloc(sizeof(float) * (size_t)dk);
+        float* vr = (float*)malloc(sizeof(float) * (size_t)dv);
         memcpy(S, S0 + (size_t)u * dv * dk, sizeof(double) * (size_t)dv * dk);
         qz_unit(fmt, dk, dv, n_c, smooth_enable, S, NULL, cq, sg, sm, ci, cv, NULL, NULL);
         dequant_unit(fmt, dk, dv, n_c, cq, sg, sm, ci, cv, S);
         int fill = 0;
         for (int t = 0; t < n_tok; ++t) {
             size_t tu = (size_t)t * n_units + u;
-            step_one(dk, dv, gate_kind, S, q + tu * dk, k + tu * dk, v + tu * dv, beta[tu],
-                     gate + tu * gstride, o + tu * dv, Mk);
+            const float* kt = k + tu * dk;
+            const float* vt = v + tu * dv;
+            if (buf_fp16) { /* the window holds the token as rounded into the buffer */
+                for (int j = 0; j < dk; ++j) kr[j] = orc_fp16_round(kt[j]);
+                for (int i = 0; i < dv; ++i) vr[i] = orc_fp16_round(vt[i]);
+                kt = kr;
+                vt = vr;
+            }
+            step_one(dk, dv, gate_kind, S, q + tu * dk, kt, vt, beta[tu], gate + tu * gstride,
+                     o + tu * dv, Mk);
             fill += 1;
             int forced = force_at && force_at[u] == t;
             if (fill == W || forced) {
@@ -572,6 +614,8 @@ int orc_windowed_run(int fmt, int n_units, int dk, int dv, int n_tok, int gate_k
         free(sm);
         free(ci);
         free(cv);
+        free(kr);
+        free(vr);
     }
     return rc;
 }

@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "lq_oracle.c")
 PINS = ["tests/test_oracle_recurrence.py", "tests/test_oracle_quantizer.py",
-        "tests/test_oracle_window.py", "tests/test_oracle_fp8.py"]
+        "tests/test_oracle_window.py", "tests/test_oracle_fp8.py", "tests/test_oracle_fp16_buffer.py"]
 
 MUTANTS = {
     "delta_sign": ("S[(size_t)i * dk + j] - (double)beta * Mk[i]", "S[(size_t)i * dk + j] + (double)beta * Mk[i]"),
@@ -31,6 +31,11 @@ MUTANTS = {
     "e4m3_ties_away": ("nearbyint(ldexp(a, 3 - E))", "round(ldexp(a, 3 - E))"),
     "e4m3_no_subnormal_floor": ("if (E < -6) E = -6;", "if (E < -9) E = -9;"),
     "e4m3_carry_dropped": ("e = E + 8;", "e = E + 7;"),
+    "fp16_ties_away": ("nearbyint(ldexp(a, 10 - E))", "round(ldexp(a, 10 - E))"),
+    "fp16_nine_mantissa_bits": ("ldexp(nearbyint(ldexp(a, 10 - E)), E - 10)", "ldexp(nearbyint(ldexp(a, 9 - E)), E - 9)"),
+    "fp16_no_subnormal_floor": ("if (E < -14) E = -14;", "if (E < -24) E = -24;"),
+    "fp16_no_saturation": ("if (a > 65504.0) a = 65504.0;", "if (a > 65536.0) a = 65536.0;"),
+    "fp16_buffer_keeps_raw_v": ("vt = vr;", "vt = vt;"),
     "ties_away_from_zero": ("double c = nearbyint(x);", "double c = round(x);"),
     "column_slot_unmasked": ("row_sel[i] ? 0.0f : (float)Su", "0 ? 0.0f : (float)Su"),
     "replay_forward_order": ("for (int i = n_ent - 1; i >= 0; --i)", "for (int i = 0; i < n_ent; ++i)"),
