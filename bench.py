@@ -47,6 +47,8 @@ def parse_args():
     ap.add_argument("--n-comp", type=int, default=None, help="override the workload's compensator count (0..16)")
     ap.add_argument("--format", default="int8", choices=("int8", "e4m3"),
                     help="8-bit code format of the stored state")
+    ap.add_argument("--buffer", default="fp32", choices=("fp32", "fp16"),
+                    help="precision of the window buffer's k and v")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-fp32", action="store_true", help="skip the FP32-state comparison loop")
@@ -66,7 +68,8 @@ def parse_args():
 
 def entry_bytes(wl) -> int:
     g = wl.d if wl.gate == "channel" else 1
-    return 4 * (wl.d // wl.group + wl.d + 1 + g)
+    e = 2 if wl.buffer_format == "fp16" else 4  # k and v elements
+    return e * (wl.d // wl.group + wl.d) + 4 * (1 + g)
 
 
 def decode_bytes(wl, j: int) -> int:
@@ -133,7 +136,7 @@ def projected(wl, w, h):
 # CPU baseline: the oracle as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl, n_tok, target_s, fmt="int8"):
+def cpu_baseline(wl, n_tok, target_s, fmt="int8", buffer="fp32"):
     import numpy as np
 
     import oracle as orc
@@ -151,7 +154,8 @@ def cpu_baseline(wl, n_tok, target_s, fmt="int8"):
     cal_tok = min(n_tok, 2 * wl.window)
     S0, st = sample(cal_units, cal_tok)
     t0 = time.perf_counter()
-    orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp, fmt=fmt)
+    orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp, fmt=fmt,
+                     buffer=buffer)
     rate = len(cal_units) * cal_tok / max(time.perf_counter() - t0, 1e-6)
     n_units = int(max(1, min(wl.n_units, rate * target_s / n_tok)))
     # the whole workload may take well under target_s: repeat it to get a steady figure
@@ -160,7 +164,8 @@ def cpu_baseline(wl, n_tok, target_s, fmt="int8"):
     S0, st = sample(units, n_tok)
     t0 = time.perf_counter()
     for _ in range(reps):
-        orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp, fmt=fmt)
+        orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp, fmt=fmt,
+                         buffer=buffer)
     dt = time.perf_counter() - t0
     cpu_model = ""
     try:
@@ -183,13 +188,13 @@ def cpu_baseline(wl, n_tok, target_s, fmt="int8"):
 # measured HBM traffic (rocprofv3 --pmc), valid only for the kernel it was taken on
 # ---------------------------------------------------------------------------
 
-def traffic_file(workload, fmt="int8"):
-    tag = workload if fmt == "int8" else f"{workload}_{fmt}"
-    return os.path.join(ROOT, "profiles", f"decode_q8_{tag}_traffic.json")
+def variant_tag(workload, fmt="int8", buffer="fp32"):
+    """Name of a workload variant in profile file names."""
+    return workload + ("" if fmt == "int8" else f"_{fmt}") + ("" if buffer == "fp32" else f"_{buffer}buf")
 
 
-def measured_traffic(workload, fmt="int8"):
-    p = traffic_file(workload, fmt)
+def measured_traffic(workload, fmt="int8", buffer="fp32"):
+    p = os.path.join(ROOT, "profiles", f"decode_q8_{variant_tag(workload, fmt, buffer)}_traffic.json")
     try:
         rec = json.load(open(p))
     except Exception:
@@ -223,6 +228,7 @@ def main():
         wl = wl.scaled(window=args.window)
     if args.n_comp is not None:
         wl = wl.scaled(n_comp=args.n_comp)
+    wl = wl.scaled(code_format=args.format, buffer_format=args.buffer)
     W, U, L, d = wl.window, wl.n_units, wl.layers, wl.d
     steps = wl.decode if args.steps is None else args.steps
     warmup = W if args.warmup is None else args.warmup
@@ -230,7 +236,9 @@ def main():
     torch.cuda.set_device(dev)
     gen = torch.Generator(dev).manual_seed(1000 + wl.seed)
     code_format = {"int8": lq.LQ_CODE_INT8, "e4m3": lq.LQ_CODE_E4M3}[args.format]
-    cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind, code_format)
+    buffer_format = {"fp32": lq.LQ_BUFFER_FP32, "fp16": lq.LQ_BUFFER_FP16}[args.buffer]
+    cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind, code_format,
+                    buffer_format)
     stream = torch.cuda.current_stream()
 
     # ---- start states: FP32 prefill through the FP32-state kernel (input synthesis)
@@ -328,7 +336,7 @@ def main():
             "workload": wl.name,
             "layers": L, "n_seq": wl.n_seq, "n_v_heads": wl.n_v_heads, "n_k_heads": wl.n_k_heads,
             "d_k": d, "d_v": d, "gate": wl.gate, "window": W, "n_comp": wl.n_comp,
-            "code_format": args.format,
+            "code_format": args.format, "buffer_format": args.buffer,
             "prefill": wl.prefill, "units": U * L * R, "state_copies": R,
         },
         "timing": f"HIP graph of the timed steps, median of {repeats} replays, HIP events around each",
@@ -355,7 +363,7 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": achieved / HBM_PEAK_GBS,
-        "traffic": measured_traffic(wl.name, args.format),
+        "traffic": measured_traffic(wl.name, args.format, args.buffer),
         "kernel": "decode_q8_kernel",
         "avg_launch_us": avg_launch_s * 1e6,
         "alg_bytes_per_launch": avg_bytes,
@@ -389,7 +397,7 @@ def main():
         }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds, args.format)
+        result["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds, args.format, args.buffer)
     print(json.dumps(result), flush=True)
 
 

@@ -76,15 +76,21 @@ extern "C" {
 #define LQ_CODE_INT8 0 /* integers in [-127, 127] */
 #define LQ_CODE_E4M3 1 /* 8-bit floats: OCP E4M3 without infinities, magnitudes up to 448 */
 
+/* window-buffer formats (the buffered tokens' k and v) */
+#define LQ_BUFFER_FP32 0 /* as given */
+#define LQ_BUFFER_FP16 1 /* IEEE binary16, nearest-even, magnitudes above 65504 stored as 65504 */
+
 /* sticky device flags (lq_read_status) */
 #define LQ_DEV_WINDOW_OVERFLOW 0x1u /* lq_decode_step found a full window: that unit's o is NaN, nothing appended */
 #define LQ_DEV_NONFINITE_INPUT 0x2u /* a decode input (q, k, v, beta, gate) was NaN or Inf */
+#define LQ_DEV_BUFFER_SATURATED 0x4u /* binary16 buffer: a k or v magnitude above 65504 was stored as 65504 */
 
 /*
  * Problem description.  Supported: d_k == d_v in {64, 128};
  * 1 <= window <= 256; 0 <= n_comp <= 16; n_seq, n_v_heads, n_k_heads >= 1;
  * n_v_heads % n_k_heads == 0; gate_kind in {LQ_GATE_SCALAR, LQ_GATE_CHANNEL};
  * code_format in {LQ_CODE_INT8, LQ_CODE_E4M3};
+ * buffer_format in {LQ_BUFFER_FP32, LQ_BUFFER_FP16};
  * the unit count n_seq * n_v_heads below 2^31.
  */
 typedef struct lq_config {
@@ -99,6 +105,10 @@ typedef struct lq_config {
     int32_t code_format; /* LQ_CODE_INT8 (the review's INT8) or LQ_CODE_E4M3 (the
                             abstract's "8-bit" read as a floating-point format): the
                             scales are chosen so the largest code is 127 or 448 */
+    int32_t buffer_format; /* LQ_BUFFER_FP32, or LQ_BUFFER_FP16: each token's k and v
+                              enter the window rounded to binary16 (half the buffer
+                              bytes); the rounded token is then the token everywhere:
+                              its own output, later replays, the window-end state */
 } lq_config;
 
 /*
@@ -113,8 +123,8 @@ typedef struct lq_config {
  *   comp_idx  int32 [units][n_comp]    c < d_v: row c; c >= d_v: column c - d_v
  *   comp_vec  fp32  [units][n_comp][max(d_k,d_v)]  row slot: the row (d_k);
  *                                      column slot: the column (d_v)
- *   buf_k     fp32  [n_seq][n_k_heads][window][d_k]  (shared by a key head's value heads)
- *   buf_v     fp32  [units][window][d_v]
+ *   buf_k     fp32 or fp16 [n_seq][n_k_heads][window][d_k]  (shared by a key head's value heads)
+ *   buf_v     fp32 or fp16 [units][window][d_v]
  *   buf_beta  fp32  [units][window]
  *   buf_gate  fp32  [units][window] (scalar) or [units][window][d_k] (channel)
  *   work      int32 [1 + units]        scratch of lq_window_flush: count, then the

@@ -27,8 +27,11 @@ LQ_GATE_SCALAR = 0
 LQ_GATE_CHANNEL = 1
 LQ_CODE_INT8 = 0
 LQ_CODE_E4M3 = 1
+LQ_BUFFER_FP32 = 0
+LQ_BUFFER_FP16 = 1
 LQ_DEV_WINDOW_OVERFLOW = 0x1
 LQ_DEV_NONFINITE_INPUT = 0x2
+LQ_DEV_BUFFER_SATURATED = 0x4
 
 EXPORTS = ("lq_state_bytes", "lq_state_layout", "lq_state_init", "lq_decode_step",
            "lq_window_flush", "lq_dequant_state", "lq_fp32_decode_step", "lq_read_status",
@@ -44,7 +47,7 @@ class LQError(RuntimeError):
 class _CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_seq", "n_v_heads", "n_k_heads", "d_k", "d_v", "window", "n_comp", "gate_kind",
-                 "code_format")]
+                 "code_format", "buffer_format")]
 
 
 _LAYOUT_FIELDS = ("total_bytes", "status", "fill", "codes", "sigma", "smooth", "comp_idx",
@@ -67,6 +70,7 @@ class Config:
     n_comp: int
     gate_kind: int = LQ_GATE_SCALAR
     code_format: int = LQ_CODE_INT8
+    buffer_format: int = LQ_BUFFER_FP32
 
     @property
     def n_units(self) -> int:
@@ -277,6 +281,7 @@ def state_views(cfg: Config, state) -> Dict[str, "object"]:
     U, D = cfg.n_units, max(cfg.d_k, cfg.d_v)
     W, nc = cfg.window, cfg.n_comp
     g = cfg.d_k if cfg.gate_kind == LQ_GATE_CHANNEL else 1
+    bt = torch.float16 if cfg.buffer_format == LQ_BUFFER_FP16 else torch.float32
 
     def view(off, n, dtype, shape):
         nbytes = n * torch.empty((), dtype=dtype).element_size()
@@ -290,9 +295,9 @@ def state_views(cfg: Config, state) -> Dict[str, "object"]:
         "smooth": view(L["smooth"], U * cfg.d_k, torch.float32, (U, cfg.d_k)),
         "comp_idx": view(L["comp_idx"], U * nc, torch.int32, (U, nc)),
         "comp_vec": view(L["comp_vec"], U * nc * D, torch.float32, (U, nc, D)),
-        "buf_k": view(L["buf_k"], cfg.n_seq * cfg.n_k_heads * W * cfg.d_k, torch.float32,
+        "buf_k": view(L["buf_k"], cfg.n_seq * cfg.n_k_heads * W * cfg.d_k, bt,
                       (cfg.n_seq, cfg.n_k_heads, W, cfg.d_k)),
-        "buf_v": view(L["buf_v"], U * W * cfg.d_v, torch.float32, (U, W, cfg.d_v)),
+        "buf_v": view(L["buf_v"], U * W * cfg.d_v, bt, (U, W, cfg.d_v)),
         "buf_beta": view(L["buf_beta"], U * W, torch.float32, (U, W)),
         "buf_gate": view(L["buf_gate"], U * W * g, torch.float32, (U, W) if g == 1 else (U, W, g)),
         "work": view(L["work"], U + 1, torch.int32, (U + 1,)),

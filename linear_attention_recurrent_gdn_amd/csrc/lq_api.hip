@@ -18,6 +18,7 @@ int32_t check_config(const lq_config* c) {
     if (c->n_v_heads % c->n_k_heads != 0) return LQ_EINVAL;
     if (c->gate_kind != LQ_GATE_SCALAR && c->gate_kind != LQ_GATE_CHANNEL) return LQ_EINVAL;
     if (c->code_format != LQ_CODE_INT8 && c->code_format != LQ_CODE_E4M3) return LQ_EINVAL;
+    if (c->buffer_format != LQ_BUFFER_FP32 && c->buffer_format != LQ_BUFFER_FP16) return LQ_EINVAL;
     if ((int64_t)c->n_seq * c->n_v_heads >= ((int64_t)1 << 31)) return LQ_EUNSUPPORTED;
     if (c->d_k != c->d_v || (c->d_k != 64 && c->d_k != 128)) return LQ_EUNSUPPORTED;
     if (c->window > 256 || c->n_comp > 16) return LQ_EUNSUPPORTED;
@@ -35,6 +36,7 @@ Dims dims_of(const lq_config* c) {
     d.window = c->window;
     d.n_comp = c->n_comp;
     d.code_format = c->code_format;
+    d.buffer_format = c->buffer_format;
     return d;
 }
 

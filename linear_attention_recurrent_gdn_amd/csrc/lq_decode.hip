@@ -16,6 +16,9 @@
 // S_n q.  The 8-bit tile, sigma, s and compensators are only read.  Q holds
 // the code values: the integers themselves, or the E4M3 values, which the
 // gfx950 conversion v_cvt_pk_f32_fp8 produces exactly (two per instruction).
+// The buffer keeps each token's k and v in fp32 or in binary16 (rounded as the
+// token enters the window, then used in that rounded form everywhere), which
+// halves the replay's bytes.
 //
 // Mapping: one workgroup of four wavefronts per unit.  Each wavefront
 // requests its quarter of the 8-bit tile (4 KiB at d = 128) with 16-byte
@@ -35,6 +38,7 @@
 // reads and writes each 512-byte row once.
 
 #include "lq_internal.h"
+
 
 namespace lq {
 
@@ -71,6 +75,34 @@ __device__ __forceinline__ void store_vec(float* p, const Vec<EPL>& v) {
 
 __device__ __forceinline__ bool finite(float x) { return __builtin_isfinite(x); }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Stores values that are already binary16-representable when H16.
+template <int EPL, bool H16>
+__device__ __forceinline__ void store_buf(void* base, size_t off, const Vec<EPL>& v) {
+    if constexpr (H16) {
+        _Float16* p = reinterpret_cast<_Float16*>(base) + off;
+        if constexpr (EPL == 2) {
+            *reinterpret_cast<f16x2*>(p) = f16x2{(_Float16)v.e[0], (_Float16)v.e[1]};
+        } else {
+            p[0] = (_Float16)v.e[0];
+        }
+    } else {
+        store_vec(reinterpret_cast<float*>(base) + off, v);
+    }
+}
+
+// A value as the binary16 buffer holds it: nearest-even (the default rounding
+// mode of v_cvt_f16_f32), magnitudes above 65504 stored as 65504 (sat set),
+// NaN kept.
+__device__ __forceinline__ float to_f16_buffer(float x, bool& sat) {
+    if (__builtin_fabsf(x) > 65504.f) {
+        sat = true;
+        x = __builtin_copysignf(65504.f, x);
+    }
+    return (float)(_Float16)x;
+}
+
 // One buffered token as held in registers during the reverse pass.
 template <int EPL, int GE>
 struct Entry {
@@ -79,9 +111,65 @@ struct Entry {
     float beta;
 };
 
+// A buffered token in the register ring.  With the binary16 buffer, k and v
+// stay packed (one 32-bit word holds this lane's EPL <= 2 halves) until the
+// token is used, so a ring entry costs half the registers.
+template <int EPL, int GE, bool H16>
+struct RingEntry {
+    Vec<EPL> k, v;
+    Vec<GE> g;
+};
+
+template <int EPL, int GE>
+struct RingEntry<EPL, GE, true> {
+    uint32_t k, v;
+    Vec<GE> g;
+};
+
+// beta and scalar gate of the whole window, NWB per lane (token i in lane i % 64
+// of register i / 64)
+template <int NWB>
+struct WindowRegs {
+    float b[NWB], a[NWB];
+};
+
+// beta and scalar gate of buffered token i (uniform): pick the register by
+// compare-and-select (constant indices only), then read the owning lane
+template <int NWB, bool KDA>
+__device__ __forceinline__ float2 window_scalars(WindowRegs<NWB> win, int i) {
+    float bsel = win.b[0], asel = win.a[0];
+#pragma unroll
+    for (int w = 1; w < NWB; ++w) {
+        bsel = (i >= w * kWave) ? win.b[w] : bsel;
+        asel = (i >= w * kWave) ? win.a[w] : asel;
+    }
+    float2 ba;
+    ba.x = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bsel), i & (kWave - 1)));
+    ba.y = 0.f;
+    if constexpr (!KDA)
+        ba.y = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, asel), i & (kWave - 1)));
+    return ba;
+}
+
+template <int EPL>
+__device__ __forceinline__ uint32_t load_half_word(const void* base, size_t off) {
+    const _Float16* p = reinterpret_cast<const _Float16*>(base) + off;
+    if constexpr (EPL == 2) return *reinterpret_cast<const uint32_t*>(p);
+    else return (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+}
+
+template <int EPL>
+__device__ __forceinline__ Vec<EPL> unpack_halves(uint32_t w) {
+    Vec<EPL> r;
+    const f16x2 h = __builtin_bit_cast(f16x2, w);
+    r.e[0] = (float)h.x;
+    if constexpr (EPL == 2) r.e[1] = (float)h.y;
+    return r;
+}
+
 }  // namespace
 
-template <int D, bool KDA, int P, int NWB, int FMT>
+template <int D, bool KDA, int P, int NWB, int FMT, bool H16>
 __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     constexpr int EPL = D / kWave;   // state elements per lane in the chain wave
     constexpr int GE = KDA ? EPL : 1;
@@ -126,8 +214,8 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         for (int t = 0; t < NLW; ++t) tw[t] = tile[t * kWave + lane];
         sg_row = a.blob.sigma[(size_t)u * D + my_row];
     } else {
-        float* bk = a.blob.buf_k + kvec * (size_t)W * D;
-        float* bv = a.blob.buf_v + (size_t)u * W * D;
+        const size_t kb0 = kvec * (size_t)W * D;  // element offsets of this unit's k and v entries
+        const size_t vb0 = (size_t)u * W * D;
         float* bb = a.blob.buf_beta + (size_t)u * W;
         float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
 
@@ -146,21 +234,27 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         } else {
             cur.g.e[0] = a.gate[u];
         }
-        auto load_entry = [&](int i, Entry<EPL, GE>& en) {
-            en.k = load_vec<EPL>(bk + (size_t)i * D + lane * EPL);
-            en.v = load_vec<EPL>(bv + (size_t)i * D + lane * EPL);
+        auto load_entry = [&](int i, RingEntry<EPL, GE, H16>& en) {
+            if constexpr (H16) {
+                en.k = load_half_word<EPL>(a.blob.buf_k, kb0 + (size_t)i * D + lane * EPL);
+                en.v = load_half_word<EPL>(a.blob.buf_v, vb0 + (size_t)i * D + lane * EPL);
+            } else {
+                en.k = load_vec<EPL>(reinterpret_cast<const float*>(a.blob.buf_k) + kb0 + (size_t)i * D + lane * EPL);
+                en.v = load_vec<EPL>(reinterpret_cast<const float*>(a.blob.buf_v) + vb0 + (size_t)i * D + lane * EPL);
+            }
             if constexpr (KDA) en.g = load_vec<GE>(bg + (size_t)i * D + lane * EPL);
         };
-        Entry<EPL, GE> ring[P];
+        RingEntry<EPL, GE, H16> ring[P];
 #pragma unroll
         for (int p = 0; p < P; ++p) load_entry(max(j - 1 - p, 0), ring[p]);
-        float bwin[NWB], awin[NWB];
+        WindowRegs<NWB> win;
 #pragma unroll
         for (int w = 0; w < NWB; ++w) {
-            bwin[w] = bb[min(lane + w * kWave, W - 1)];
-            awin[w] = KDA ? 0.f : bg[min(lane + w * kWave, W - 1)];
+            win.b[w] = bb[min(lane + w * kWave, W - 1)];
+            win.a[w] = KDA ? 0.f : bg[min(lane + w * kWave, W - 1)];
         }
-        // this wave's tile quarter comes after the data the reverse pass needs first
+        // this wave's tile quarter, smoothing and compensators come after the
+        // data the reverse pass needs first
 #pragma unroll
         for (int t = 0; t < NLW; ++t) tw[t] = tile[t * kWave + lane];
         sg_row = a.blob.sigma[(size_t)u * D + my_row];
@@ -176,8 +270,17 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         for (int e = 0; e < EPL; ++e) ok = ok && finite(qv.e[e]) && finite(cur.k.e[e]) && finite(cur.v.e[e]);
         for (int e = 0; e < GE; ++e) ok = ok && finite(cur.g.e[e]);
         if (__any(!ok) && lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_NONFINITE_INPUT);
-        if (h % a.dm.group == 0) store_vec(bk + (size_t)j * D + lane * EPL, cur.k);
-        store_vec(bv + (size_t)j * D + lane * EPL, cur.v);
+        if constexpr (H16) {
+            // the token enters the window as the buffer holds it, and is used so
+            bool sat = false;
+            for (int e = 0; e < EPL; ++e) {
+                cur.k.e[e] = to_f16_buffer(cur.k.e[e], sat);
+                cur.v.e[e] = to_f16_buffer(cur.v.e[e], sat);
+            }
+            if (__any(sat) && lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_BUFFER_SATURATED);
+        }
+        if (h % a.dm.group == 0) store_buf<EPL, H16>(a.blob.buf_k, kb0 + (size_t)j * D + lane * EPL, cur.k);
+        store_buf<EPL, H16>(a.blob.buf_v, vb0 + (size_t)j * D + lane * EPL, cur.v);
         if constexpr (KDA) {
             store_vec(bg + (size_t)j * D + lane * EPL, cur.g);
         } else {
@@ -192,44 +295,40 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         Vec<EPL> acc;
         for (int e = 0; e < EPL; ++e) acc.e[e] = 0.f;
         float sc = 1.0f;
-        auto step = [&](const Entry<EPL, GE>& en, float beta, float alpha) {
+        auto step = [&](const Vec<EPL>& ek, const Vec<EPL>& ev, const Vec<GE>& eg, float beta, float alpha) {
             float p = 0.f;
-            for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(en.k.e[e], r.e[e], p);
+            for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(ek.e[e], r.e[e], p);
             const float red = wave_sum(p);
             const float cr = beta * red;
             if constexpr (KDA) {
                 for (int e = 0; e < EPL; ++e) {
-                    r.e[e] = en.g.e[e] * __builtin_fmaf(-cr, en.k.e[e], r.e[e]);
-                    acc.e[e] = __builtin_fmaf(cr, en.v.e[e], acc.e[e]);
+                    r.e[e] = eg.e[e] * __builtin_fmaf(-cr, ek.e[e], r.e[e]);
+                    acc.e[e] = __builtin_fmaf(cr, ev.e[e], acc.e[e]);
                 }
             } else {
-                for (int e = 0; e < EPL; ++e) r.e[e] = __builtin_fmaf(-cr, en.k.e[e], r.e[e]);
+                for (int e = 0; e < EPL; ++e) r.e[e] = __builtin_fmaf(-cr, ek.e[e], r.e[e]);
                 const float w = cr * sc;
-                for (int e = 0; e < EPL; ++e) acc.e[e] = __builtin_fmaf(w, en.v.e[e], acc.e[e]);
+                for (int e = 0; e < EPL; ++e) acc.e[e] = __builtin_fmaf(w, ev.e[e], acc.e[e]);
                 sc *= alpha;
             }
         };
-        step(cur, cur.beta, cur.g.e[0]);
+        step(cur.k, cur.v, cur.g, cur.beta, cur.g.e[0]);
+        // k and v of ring entry p as fp32
+        auto ring_k = [&](int p) {
+            if constexpr (H16) return unpack_halves<EPL>(ring[p].k);
+            else return ring[p].k;
+        };
+        auto ring_v = [&](int p) {
+            if constexpr (H16) return unpack_halves<EPL>(ring[p].v);
+            else return ring[p].v;
+        };
         for (int s0 = 0; s0 < j; s0 += P) {
 #pragma unroll
             for (int p = 0; p < P; ++p) {
                 const int i = j - 1 - (s0 + p);
                 if (i >= 0) {
-                    // i is uniform: pick the window register by compare-and-select
-                    // (constant indices only), then read the owning lane
-                    float bsel = bwin[0], asel = awin[0];
-#pragma unroll
-                    for (int w = 1; w < NWB; ++w) {
-                        bsel = (i >= w * kWave) ? bwin[w] : bsel;
-                        asel = (i >= w * kWave) ? awin[w] : asel;
-                    }
-                    const float beta = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bsel), i & (kWave - 1)));
-                    float alpha = 0.f;
-                    if constexpr (!KDA)
-                        alpha = __builtin_bit_cast(
-                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, asel), i & (kWave - 1)));
-                    step(ring[p], beta, alpha);
+                    const float2 ba = window_scalars<NWB, KDA>(win, i);
+                    step(ring_k(p), ring_v(p), ring[p].g, ba.x, ba.y);
                 }
                 load_entry(max(i - P, 0), ring[p]);
             }
@@ -402,32 +501,46 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
 #ifndef LQ_RING_KDA
 #define LQ_RING_KDA 6
 #endif
+#ifndef LQ_RING_GDN_H16
+#define LQ_RING_GDN_H16 6
+#endif
+#ifndef LQ_RING_KDA_H16
+#define LQ_RING_KDA_H16 6
+#endif
 
-template <int NWB, int FMT>
+template <int NWB, int FMT, bool H16>
 void launch_decode_q8_w(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
     const dim3 grid(a.dm.n_units), block(256);
     if (d == 128) {
+        constexpr int PK = H16 ? LQ_RING_KDA_H16 : LQ_RING_KDA;
+        constexpr int PG = H16 ? LQ_RING_GDN_H16 : LQ_RING_GDN;
         if (gate_kind == LQ_GATE_CHANNEL)
-            hipLaunchKernelGGL((decode_q8_kernel<128, true, LQ_RING_KDA, NWB, FMT>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<128, true, PK, NWB, FMT, H16>), grid, block, 0, st, a);
         else
-            hipLaunchKernelGGL((decode_q8_kernel<128, false, LQ_RING_GDN, NWB, FMT>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<128, false, PG, NWB, FMT, H16>), grid, block, 0, st, a);
     } else {
         if (gate_kind == LQ_GATE_CHANNEL)
-            hipLaunchKernelGGL((decode_q8_kernel<64, true, 16, NWB, FMT>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<64, true, 16, NWB, FMT, H16>), grid, block, 0, st, a);
         else
-            hipLaunchKernelGGL((decode_q8_kernel<64, false, 16, NWB, FMT>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<64, false, 16, NWB, FMT, H16>), grid, block, 0, st, a);
     }
 }
 
-template <int FMT>
+template <int FMT, bool H16>
 void launch_decode_q8_f(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
-    if (a.dm.window <= 2 * kWave) launch_decode_q8_w<2, FMT>(a, d, gate_kind, st);
-    else launch_decode_q8_w<4, FMT>(a, d, gate_kind, st);
+    if (a.dm.window <= 2 * kWave) launch_decode_q8_w<2, FMT, H16>(a, d, gate_kind, st);
+    else launch_decode_q8_w<4, FMT, H16>(a, d, gate_kind, st);
+}
+
+template <bool H16>
+void launch_decode_q8_b(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
+    if (a.dm.code_format == LQ_CODE_E4M3) launch_decode_q8_f<LQ_CODE_E4M3, H16>(a, d, gate_kind, st);
+    else launch_decode_q8_f<LQ_CODE_INT8, H16>(a, d, gate_kind, st);
 }
 
 hipError_t launch_decode_q8(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
-    if (a.dm.code_format == LQ_CODE_E4M3) launch_decode_q8_f<LQ_CODE_E4M3>(a, d, gate_kind, st);
-    else launch_decode_q8_f<LQ_CODE_INT8>(a, d, gate_kind, st);
+    if (a.dm.buffer_format == LQ_BUFFER_FP16) launch_decode_q8_b<true>(a, d, gate_kind, st);
+    else launch_decode_q8_b<false>(a, d, gate_kind, st);
     return hipGetLastError();
 }
 

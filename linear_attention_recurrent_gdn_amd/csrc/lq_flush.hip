@@ -182,16 +182,27 @@ struct Stage {
     float b, al;
 };
 
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Four consecutive buffer elements (fp32, or binary16 converted exactly).
+__device__ __forceinline__ float4 load4_buf(const void* base, size_t off, bool h16) {
+    if (h16) {
+        const f16x4 h = *reinterpret_cast<const f16x4*>(reinterpret_cast<const _Float16*>(base) + off);
+        return make_float4((float)h.x, (float)h.y, (float)h.z, (float)h.w);
+    }
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+}
+
 template <int D, int NT, bool KDA>
-__device__ __forceinline__ Stage<KDA> fetch_stage(const float* bk, const float* bv, const float* bb,
+__device__ __forceinline__ Stage<KDA> fetch_stage(const void* bk, const void* bv, bool h16, const float* bb,
                                                  const float* bg, int i0, int n_replay, int tid) {
     constexpr int EB = 16;
     Stage<KDA> st;
     const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
     const int x = 4 * tid;
     const int e = min(x / D, ne - 1), c = x % D;
-    st.k = *reinterpret_cast<const float4*>(bk + (size_t)(i0 + e) * D + c);
-    st.v = *reinterpret_cast<const float4*>(bv + (size_t)(i0 + e) * D + c);
+    st.k = load4_buf(bk, (size_t)(i0 + e) * D + c, h16);
+    st.v = load4_buf(bv, (size_t)(i0 + e) * D + c, h16);
     if constexpr (KDA) st.g = *reinterpret_cast<const float4*>(bg + (size_t)(i0 + e) * D + c);
     st.b = 0.f;
     st.al = 1.f;
@@ -330,8 +341,10 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
         }
 
         // ---------------- B: forward replay of the buffered tokens, 16 per chunk
-        const float* bk = a.blob.buf_k + kvec * (size_t)W * D;
-        const float* bv = a.blob.buf_v + (size_t)u * W * D;
+        const bool h16 = a.dm.buffer_format == LQ_BUFFER_FP16;
+        const size_t esz = h16 ? 2 : 4;
+        const void* bk = (const char*)a.blob.buf_k + kvec * (size_t)W * D * esz;
+        const void* bv = (const char*)a.blob.buf_v + (size_t)u * W * D * esz;
         const float* bb = a.blob.buf_beta + (size_t)u * W;
         const float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
         double gam = 1.0;  // scalar gate: g of the last replayed token (uniform)
@@ -339,7 +352,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             if (tid < D) lds_G[tid] = 1.0;
         }
         Stage<KDA> pf{};
-        if (n_replay > 0) pf = fetch_stage<D, NT, KDA>(bk, bv, bb, bg, 0, n_replay, tid);
+        if (n_replay > 0) pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, 0, n_replay, tid);
         for (int i0 = 0; i0 < n_replay; i0 += EB) {
             const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
             __syncthreads();  // the previous chunk is done with LDS
@@ -389,7 +402,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             }
             __syncthreads();
             if (i0 + EB < n_replay)  // in flight during this chunk
-                pf = fetch_stage<D, NT, KDA>(bk, bv, bb, bg, i0 + EB, n_replay, tid);
+                pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, i0 + EB, n_replay, tid);
             if constexpr (KDA) {
                 // one thread per column: fold G into T if the chunk could take it
                 // below the threshold, then the key scaled both ways

@@ -22,6 +22,7 @@ inline void compute_layout(const lq_config& c, lq_layout& L) {
     const size_t D = (size_t)(c.d_k > c.d_v ? c.d_k : c.d_v);
     const size_t W = (size_t)c.window;
     const size_t nc = (size_t)c.n_comp;
+    const size_t esz = c.buffer_format == LQ_BUFFER_FP16 ? 2 : 4;  // k, v element bytes
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -35,8 +36,8 @@ inline void compute_layout(const lq_config& c, lq_layout& L) {
     L.smooth = take(U * c.d_k * sizeof(float));
     L.comp_idx = take(U * nc * sizeof(int32_t));
     L.comp_vec = take(U * nc * D * sizeof(float));
-    L.buf_k = take(KH * W * c.d_k * sizeof(float));
-    L.buf_v = take(U * W * c.d_v * sizeof(float));
+    L.buf_k = take(KH * W * c.d_k * esz);
+    L.buf_v = take(U * W * c.d_v * esz);
     L.buf_beta = take(U * W * sizeof(float));
     L.buf_gate = take(U * W * (c.gate_kind == LQ_GATE_CHANNEL ? c.d_k : 1) * sizeof(float));
     L.work = take((U + 1) * sizeof(int32_t));
@@ -52,8 +53,8 @@ struct BlobPtrs {
     float* smooth;
     int32_t* comp_idx;
     float* comp_vec;
-    float* buf_k;
-    float* buf_v;
+    void* buf_k;  // float or _Float16 elements (Dims::buffer_format)
+    void* buf_v;
     float* buf_beta;
     float* buf_gate;
     int32_t* work;  // [0] = count, [1..] = units due at the window boundary
@@ -69,8 +70,8 @@ inline BlobPtrs blob_ptrs(void* base, const lq_layout& L) {
     p.smooth = (float*)(b + L.smooth);
     p.comp_idx = (int32_t*)(b + L.comp_idx);
     p.comp_vec = (float*)(b + L.comp_vec);
-    p.buf_k = (float*)(b + L.buf_k);
-    p.buf_v = (float*)(b + L.buf_v);
+    p.buf_k = (void*)(b + L.buf_k);
+    p.buf_v = (void*)(b + L.buf_v);
     p.buf_beta = (float*)(b + L.buf_beta);
     p.buf_gate = (float*)(b + L.buf_gate);
     p.work = (int32_t*)(b + L.work);
@@ -85,7 +86,8 @@ struct Dims {
     int group;      // n_v_heads / n_k_heads
     int window;
     int n_comp;
-    int code_format;  // LQ_CODE_INT8 or LQ_CODE_E4M3
+    int code_format;    // LQ_CODE_INT8 or LQ_CODE_E4M3
+    int buffer_format;  // LQ_BUFFER_FP32 or LQ_BUFFER_FP16 (k and v of the window buffer)
 };
 
 struct DecodeArgs {

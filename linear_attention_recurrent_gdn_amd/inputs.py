@@ -57,6 +57,7 @@ class Workload:
     projected: bool = False  # inputs come from random bf16 projections of a hidden state
     hidden: int = 0
     code_format: str = "int8"  # 8-bit code format of the stored state: "int8" or "e4m3"
+    buffer_format: str = "fp32"  # window buffer's k and v: "fp32" or "fp16"
 
     @property
     def n_units(self) -> int:

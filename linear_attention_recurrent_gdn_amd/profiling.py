@@ -2,7 +2,7 @@
 
 Three commands:
 
-  window   --workload W [--format int8|e4m3]
+  window   --workload W [--format int8|e4m3] [--buffer fp32|fp16]
       Runs, eagerly on cuda:0, one plain device-to-device copy of COPY_BYTES
       (the calibration kernel for the memory counters), then one whole window
       of decode launches (every unit at fill j = 0 .. W-1) on a freshly
@@ -48,7 +48,7 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def run_window(workload: str, fmt: str = "int8") -> None:
+def run_window(workload: str, fmt: str = "int8", buffer: str = "fp32") -> None:
     import torch
 
     import linear_attention_recurrent_gdn_amd as lq
@@ -60,7 +60,9 @@ def run_window(workload: str, fmt: str = "int8") -> None:
     dev = torch.device("cuda", 0)
     gen = torch.Generator(dev).manual_seed(2000 + wl.seed)
     code_format = {"int8": lq.LQ_CODE_INT8, "e4m3": lq.LQ_CODE_E4M3}[fmt]
-    cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind, code_format)
+    buffer_format = {"fp32": lq.LQ_BUFFER_FP32, "fp16": lq.LQ_BUFFER_FP16}[buffer]
+    cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind, code_format,
+                    buffer_format)
 
     src = torch.empty(COPY_BYTES // 4, device=dev).normal_(generator=gen)
     dst = torch.empty_like(src)
@@ -202,6 +204,7 @@ def main(argv=None):
     a = sub.add_parser("window")
     a.add_argument("--workload", default="gdn_decode")
     a.add_argument("--format", default="int8", choices=("int8", "e4m3"))
+    a.add_argument("--buffer", default="fp32", choices=("fp32", "fp16"))
     b = sub.add_parser("traffic")
     b.add_argument("--workload", default="gdn_decode")
     b.add_argument("--fetch", required=True)
@@ -215,7 +218,7 @@ def main(argv=None):
     c.add_argument("--out", required=True)
     args = ap.parse_args(argv)
     if args.cmd == "window":
-        run_window(args.workload, args.format)
+        run_window(args.workload, args.format, args.buffer)
     elif args.cmd == "hbm":
         hbm()
     elif args.cmd == "traffic":

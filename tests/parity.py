@@ -51,8 +51,9 @@ def rel_l2(a, b) -> float:
 
 def config_of(wl: I.Workload) -> lq.Config:
     fmt = {"int8": lq.LQ_CODE_INT8, "e4m3": lq.LQ_CODE_E4M3}[wl.code_format]
+    buf = {"fp32": lq.LQ_BUFFER_FP32, "fp16": lq.LQ_BUFFER_FP16}[wl.buffer_format]
     return lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, wl.d, wl.d, wl.window, wl.n_comp,
-                     wl.gate_kind, fmt)
+                     wl.gate_kind, fmt, buf)
 
 
 @dataclasses.dataclass
@@ -217,6 +218,21 @@ def run(wl: I.Workload, n_tokens: Optional[int] = None, checked: Optional[Sequen
         lq.lq_decode_step(cfg, state, dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], o_dev)
         o_chk = o_dev.view(U, d).index_select(0, chk_dev).cpu().numpy()
         pu = I.tokens_per_unit(wl, {k_: v_[None] for k_, v_ in tk.items()})
+        if wl.buffer_format == "fp16":
+            # the token enters the window as the binary16 buffer holds it
+            pu["k"], pu["v"] = orc.fp16_round(pu["k"]), orc.fp16_round(pu["v"])
+        # the appended entry holds exactly the (rounded) k and v
+        j_chk = fill[checked]
+        bv_chk = views["buf_v"].index_select(0, chk_dev).float().cpu().numpy()
+        assert np.array_equal(bv_chk[np.arange(len(checked)), j_chk], pu["v"][0][checked]), \
+            f"{wl.name}: token {t}: buffered v differs from the appended token"
+        kh_of = (checked % wl.n_v_heads) // wl.group
+        bk_all = views["buf_k"]
+        bk_chk = bk_all[torch.as_tensor(checked // wl.n_v_heads, device=device),
+                        torch.as_tensor(kh_of, device=device),
+                        torch.as_tensor(j_chk, device=device)].float().cpu().numpy()
+        assert np.array_equal(bk_chk, pu["k"][0][checked]), \
+            f"{wl.name}: token {t}: buffered k differs from the appended token"
         sel = lambda a: np.ascontiguousarray(a[:, checked])
         S_hat, o_ref = orc.recurrence(S_hat, sel(pu["q"]), sel(pu["k"]), sel(pu["v"]), sel(pu["beta"]),
                                       sel(pu["gate"]))

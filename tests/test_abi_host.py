@@ -45,14 +45,15 @@ def cfg(**kw):
 
 def test_layout_sections_aligned_and_disjoint(lib):
     for c in (cfg(), cfg(gate_kind=lq.LQ_GATE_CHANNEL, d_k=64, d_v=64, window=7, n_comp=0),
-              cfg(n_seq=512, n_v_heads=32, n_k_heads=32)):
+              cfg(n_seq=512, n_v_heads=32, n_k_heads=32), cfg(buffer_format=lq.LQ_BUFFER_FP16, window=5)):
         L = lq.lq_state_layout(c)
         U, D, W, nc = c.n_units, c.d_k, c.window, c.n_comp
         g = D if c.gate_kind == lq.LQ_GATE_CHANNEL else 1
+        e = 2 if c.buffer_format == lq.LQ_BUFFER_FP16 else 4
         sizes = {
             "status": 4, "fill": 4 * U, "codes": U * D * D, "sigma": 4 * U * D,
             "smooth": 4 * U * D, "comp_idx": 4 * U * nc, "comp_vec": 4 * U * nc * D,
-            "buf_k": 4 * c.n_seq * c.n_k_heads * W * D, "buf_v": 4 * U * W * D,
+            "buf_k": e * c.n_seq * c.n_k_heads * W * D, "buf_v": e * U * W * D,
             "buf_beta": 4 * U * W, "buf_gate": 4 * U * W * g, "work": 4 * (U + 1),
         }
         spans = sorted((L[k], L[k] + n, k) for k, n in sizes.items())
@@ -76,6 +77,7 @@ def test_state_bytes_matches_int8_footprint(lib):
     (dict(n_v_heads=3, n_k_heads=2), lq.LQ_EINVAL),
     (dict(gate_kind=7), lq.LQ_EINVAL),
     (dict(code_format=2), lq.LQ_EINVAL),
+    (dict(buffer_format=2), lq.LQ_EINVAL),
     (dict(window=0), lq.LQ_EINVAL),
     (dict(n_comp=-1), lq.LQ_EINVAL),
     (dict(d_k=96, d_v=96), lq.LQ_EUNSUPPORTED),

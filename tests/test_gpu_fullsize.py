@@ -24,9 +24,11 @@ def sample_units(wl, n=24, seed=7):
 
 
 @pytest.mark.parametrize("name,fmt", [("tiny_gdn", "int8"), ("gdn_decode", "int8"), ("kda_decode", "int8"),
-                                      ("gdn_serving", "int8"), ("gdn_decode", "e4m3"), ("kda_decode", "e4m3")])
+                                      ("gdn_serving", "int8"), ("gdn_decode", "e4m3"), ("kda_decode", "e4m3"),
+                                      ("gdn_decode", "int8+fp16"), ("kda_decode", "int8+fp16")])
 def test_fullsize_parity(name, fmt):
-    wl = I.WORKLOADS[name].scaled(code_format=fmt)
+    code, _, buf = fmt.partition("+")
+    wl = I.WORKLOADS[name].scaled(code_format=code, buffer_format=buf or "fp32")
     checked = None if wl.n_units == 1 else sample_units(wl)
     n_tok = wl.decode + (wl.window if wl.stagger else 0)  # staggered: warm-up window first
     rep = parity.run(wl, n_tokens=n_tok, checked=checked, dequant_every=wl.window // 2 + 1)

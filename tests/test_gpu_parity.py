@@ -63,6 +63,14 @@ CASES = {
     "gqa_d64_e4m3": (small("gdn_decode", name="gqa_d64_e4m3", n_seq=2, n_v_heads=4, n_k_heads=2, d=64,
                            prefill=40, decode=70, window=32, n_comp=3, code_format="e4m3"),
                      dict(dequant_every=23)),
+    # the binary16 window buffer: GDN, KDA (W above 128), GQA with E4M3 codes at d = 64
+    "gdn_small_h16": (small("gdn_decode", name="gdn_small_h16", n_seq=3, n_v_heads=5, n_k_heads=5,
+                            prefill=96, decode=150, buffer_format="fp16"), dict(dequant_every=37)),
+    "kda_h16_w160": (small("kda_decode", name="kda_h16_w160", n_seq=2, n_v_heads=2, n_k_heads=2,
+                           prefill=48, decode=200, window=160, buffer_format="fp16"), dict(dequant_every=83)),
+    "gqa_d64_h16_e4m3": (small("gdn_decode", name="gqa_d64_h16_e4m3", n_seq=2, n_v_heads=4, n_k_heads=2, d=64,
+                               prefill=40, decode=70, window=32, n_comp=3, code_format="e4m3",
+                               buffer_format="fp16"), dict(dequant_every=23)),
     # zero start state (no prefill) with the channel gate at d=128
     "kda_zero_start": (small("kda_decode", name="kda_zero_start", n_seq=1, n_v_heads=2,
                              n_k_heads=2, prefill=0, decode=20, window=8, n_comp=4), dict()),
@@ -79,6 +87,26 @@ def test_parity_small(name):
 
 def _cfg(wl):
     return parity.config_of(wl)
+
+
+def test_fp16_buffer_saturates_and_flags():
+    wl = small("gdn_decode", name="h16_sat", n_seq=1, n_v_heads=2, n_k_heads=2, window=4, n_comp=1,
+               buffer_format="fp16")
+    cfg = _cfg(wl)
+    st = lq.new_state(cfg)
+    lq.lq_state_init(cfg, st, None)
+    tk = {k: torch.from_numpy(v).cuda() for k, v in I.token(wl, 0).items()}
+    o = torch.empty(wl.n_units * wl.d, device="cuda")
+    lq.lq_decode_step(cfg, st, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+    assert lq.lq_read_status(cfg, st) == 0
+    v = tk["v"].clone()
+    v[0, 1, 5] = 1e6
+    v[0, 0, 7] = -7e4
+    lq.lq_decode_step(cfg, st, tk["q"], tk["k"], v, tk["beta"], tk["gate"], o)
+    assert lq.lq_read_status(cfg, st, clear=True) == lq.LQ_DEV_BUFFER_SATURATED
+    bv = lq.state_views(cfg, st)["buf_v"]
+    assert float(bv[1, 1, 5]) == 65504.0 and float(bv[0, 1, 7]) == -65504.0
+    assert torch.isfinite(o).all()
 
 
 def test_window_overflow_sets_flag_and_nan():

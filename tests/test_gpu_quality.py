@@ -39,10 +39,12 @@ def rel(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
-@pytest.mark.parametrize("fmt", ["int8", "e4m3"])
+@pytest.mark.parametrize("variant", ["int8", "e4m3", "int8+fp16"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_quality_report(name, fmt):
-    wl = I.WORKLOADS[name].scaled(code_format=fmt, **CASES[name])
+def test_quality_report(name, variant):
+    fmt, _, buf = variant.partition("+")
+    buf = buf or "fp32"
+    wl = I.WORKLOADS[name].scaled(code_format=fmt, buffer_format=buf, **CASES[name])
     cfg = parity.config_of(wl)
     U, d, W, T = wl.n_units, wl.d, wl.window, wl.decode
     S0 = parity.start_states(wl, np.arange(U))
@@ -52,7 +54,8 @@ def test_quality_report(name, fmt):
 
     _, o_ref = orc.recurrence(S0.astype(np.float64), st["q"], st["k"], st["v"], st["beta"], st["gate"])
     o_naive = orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], 1, 0, smooth=False)
-    o_o2 = orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], W, wl.n_comp, fmt=fmt)
+    o_o2 = orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], W, wl.n_comp, fmt=fmt,
+                            buffer=buf)
 
     dev = torch.device("cuda", 0)
     state = lq.new_state(cfg, dev)
@@ -74,7 +77,7 @@ def test_quality_report(name, fmt):
     e = {"leapquant": rel(o_lq, o_ref), "naive_per_token": rel(o_naive, o_ref), "fp32_kernel": rel(o_fp32, o_ref),
          "oracle_windowed": rel(o_o2, o_ref), "leapquant_vs_oracle_windowed": rel(o_lq, o_o2)}
     last = {"leapquant": rel(o_lq[-1], o_ref[-1]), "naive_per_token": rel(o_naive[-1], o_ref[-1])}
-    print(f"[quality] {wl.name} {fmt} units={U} tokens={T} W={W} n_c={wl.n_comp}: "
+    print(f"[quality] {wl.name} {variant} units={U} tokens={T} W={W} n_c={wl.n_comp}: "
           + " ".join(f"{k}={v:.3e}" for k, v in e.items())
           + f" | last token: leapquant={last['leapquant']:.3e} naive={last['naive_per_token']:.3e}", flush=True)
     assert e["leapquant"] < e["naive_per_token"]
