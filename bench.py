@@ -52,6 +52,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-fp32", action="store_true", help="skip the FP32-state comparison loop")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip timing lq_prefill on the workload's prompt against the token-by-token FP32 kernel")
     ap.add_argument("--repeats", type=int, default=5,
                     help="replays of the timed-steps graph, median reported (1 if the steps are not whole "
                          "windows: only then does a replay restart the same fill pattern)")
@@ -181,6 +183,62 @@ def cpu_baseline(wl, n_tok, target_s, fmt="int8", buffer="fp32"):
         "sample": (f"{n_units} of {wl.n_units} units x {n_tok} decode tokens (flushes included) x {reps} passes, "
                    f"FP64 definitional windowed form, {dt:.1f} s; input generation excluded; "
                    f"host CPU: {cpu_model}"),
+    }
+
+
+# ---------------------------------------------------------------------------
+# prefill: the chunked FP64 matrix-core prompt pass against the FP32 token loop
+# ---------------------------------------------------------------------------
+
+PEAK_FP64_MFMA_TFLOPS = 78.6
+
+
+def prefill_flops(wl, n_tok) -> float:
+    """Matrix-core flops of the chunked prompt pass per unit: per token the
+    products T Kf^T, T Qf^T and the rank-16 update C Kb (2 d^2 each), per
+    16-token chunk the two 16 x 16 x d Gram products, M R and the output
+    correction (2 * 16 * 16 * d each)."""
+    d = wl.d
+    chunks = -(-n_tok // 16)
+    return n_tok * 6.0 * d * d + chunks * 4 * (2.0 * 16 * 16 * d)
+
+
+def prefill_timing(lq, wl, cfg, gen, dev, timed_graph):
+    import torch
+
+    from linear_attention_recurrent_gdn_amd import inputs as I
+
+    P, U, d = wl.prefill, wl.n_units, wl.d
+    first = I.torch_token(wl, gen, dev)
+    x = {k: torch.empty((P, *v.shape), dtype=v.dtype, device=dev) for k, v in first.items()}
+    for t in range(P):
+        tk = first if t == 0 else I.torch_token(wl, gen, dev)
+        for k in x:
+            x[k][t].copy_(tk[k])
+    S0 = torch.randn((U, d, d), generator=gen, device=dev) * 0.3
+    o = torch.empty((P, wl.n_seq, wl.n_v_heads, d), device=dev)
+    blob = lq.new_state(cfg, dev)
+    chunked_ms = timed_graph(lambda: lq.lq_prefill(cfg, blob, S0, x["q"], x["k"], x["v"], x["beta"], x["gate"], o),
+                             3)
+    S = S0.clone()
+    o1 = torch.empty((wl.n_seq, wl.n_v_heads, d), device=dev)
+    loop_ms = timed_graph(lambda: [lq.lq_fp32_decode_step(cfg, S, x["q"][t], x["k"][t], x["v"][t], x["beta"][t],
+                                                          x["gate"][t], o1) for t in range(P)])
+    if lq.lq_read_status(cfg, blob):
+        raise RuntimeError("device flags set by lq_prefill")
+    flops = prefill_flops(wl, P) * U
+    return {
+        "tokens": P, "units": U,
+        "chunked_ms": chunked_ms,
+        "fp32_token_loop_ms": loop_ms,
+        "speedup": loop_ms / chunked_ms,
+        "unit_tokens_per_s": P * U / (chunked_ms * 1e-3),
+        "roofline": {"bound": "mfma", "achieved": flops / (chunked_ms * 1e-3) / 1e12,
+                     "peak": PEAK_FP64_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / (chunked_ms * 1e-3) / 1e12 / PEAK_FP64_MFMA_TFLOPS,
+                     "kernel": "materialize_kernel (prefill mode)", "dtype": "f64"},
+        "note": "lq_prefill (outputs written, final state quantized) vs the FP32 decode kernel token by token "
+                "over the same prompt from the same start state; each as one HIP graph",
     }
 
 
@@ -395,6 +453,9 @@ def main():
             "alg_GBps": fp32_bytes / (fp32_ms / steps * 1e-3) / 1e9,
             "speedup_vs_fp32": fp32_ms / q8_ms,
         }
+
+    if not args.no_prefill and wl.prefill > 0 and not wl.projected and L == 1:
+        result["prefill"] = prefill_timing(lq, wl, cfg, gen, dev, timed_graph)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds, args.format, args.buffer)

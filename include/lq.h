@@ -177,6 +177,28 @@ int32_t lq_window_flush(const lq_config* cfg, void* state, const uint8_t* force_
                         void* stream);
 
 /*
+ * Prefill: run a prompt of n_tok tokens (n_tok >= 0, the same for every
+ * sequence) through the plain recurrence, from S0 (fp32 [n_seq][n_v_heads]
+ * [d_v][d_k], or NULL for the zero state), and quantize the final state into
+ * the blob as lq_state_init does (fill = 0, status = 0).  The arXiv abstract
+ * ("Abstract (arXiv)" section, mlsanity.com paper page): the recurrent state
+ * compresses the context; the prompt is that context, and the state is
+ * quantized once, at its end.  Inside the prompt nothing is quantized: the
+ * state is advanced 16 tokens at a time in FP64 on the matrix cores (the
+ * chunked form of the delta rule, as in the window-end flush).
+ * Inputs are token-major: q, k [n_tok][n_seq][n_k_heads][d_k]; v
+ * [n_tok][n_seq][n_v_heads][d_v]; beta [n_tok][n_seq][n_v_heads]; gate
+ * [n_tok][n_seq][n_v_heads] (scalar) or [n_tok][n_seq][n_v_heads][d_k]
+ * (channel), all fp32, same conventions as lq_decode_step.  o (fp32
+ * [n_tok][n_seq][n_v_heads][d_v], or NULL) receives o_t = S_t q_t for every
+ * prompt token.  Pointers are device pointers owned by the caller, 16-byte
+ * aligned (beta and a scalar gate 4-byte); errors as for lq_state_init.
+ */
+int32_t lq_prefill(const lq_config* cfg, void* state, const float* S0, int32_t n_tok,
+                   const float* q, const float* k, const float* v, const float* beta,
+                   const float* gate, float* o, void* stream);
+
+/*
  * Dequantized state into S_out (fp32): the window-start state
  * Diag(sigma) Q Diag(s) + compensator lines, or, with include_buffer != 0,
  * that state advanced through the buffered tokens (the state after the last

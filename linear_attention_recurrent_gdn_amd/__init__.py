@@ -33,7 +33,7 @@ LQ_DEV_WINDOW_OVERFLOW = 0x1
 LQ_DEV_NONFINITE_INPUT = 0x2
 LQ_DEV_BUFFER_SATURATED = 0x4
 
-EXPORTS = ("lq_state_bytes", "lq_state_layout", "lq_state_init", "lq_decode_step",
+EXPORTS = ("lq_state_bytes", "lq_state_layout", "lq_state_init", "lq_prefill", "lq_decode_step",
            "lq_window_flush", "lq_dequant_state", "lq_fp32_decode_step", "lq_read_status",
            "lq_strerror")
 
@@ -99,6 +99,7 @@ def load_library(path: Optional[str] = None):
     lib.lq_state_layout.argtypes = [CP, ctypes.POINTER(_CLayout)]
     lib.lq_state_init.argtypes = [CP, P, P, P]
     lib.lq_decode_step.argtypes = [CP, P, P, P, P, P, P, P, P]
+    lib.lq_prefill.argtypes = [CP, P, P, ctypes.c_int32, P, P, P, P, P, P, P]
     lib.lq_window_flush.argtypes = [CP, P, P, P]
     lib.lq_dequant_state.argtypes = [CP, P, P, ctypes.c_int32, P]
     lib.lq_fp32_decode_step.argtypes = [CP, P, P, P, P, P, P, P, P]
@@ -204,6 +205,25 @@ def lq_state_init(cfg: Config, state, S0=None, stream=None) -> None:
                                       _ptr(S0, "S0", torch.float32, sz["state"], allow_none=True),
                                       _stream(stream))
     _check("lq_state_init", rc)
+
+
+def lq_prefill(cfg: Config, state, S0, q, k, v, beta, gate, o=None, stream=None) -> None:
+    """Prompt of T tokens (token-major tensors, leading dimension T) through the
+    recurrence from S0 (or zero), outputs into o (or none), final state quantized."""
+    import torch
+
+    sz = _sizes(cfg)
+    T = int(k.shape[0]) if k is not None else 0
+    rc = load_library().lq_prefill(
+        ctypes.byref(cfg.c()), _state_ptr(cfg, state),
+        _ptr(S0, "S0", torch.float32, sz["state"], allow_none=True), T,
+        _ptr(q, "q", torch.float32, T * sz["qk"], allow_none=T == 0),
+        _ptr(k, "k", torch.float32, T * sz["qk"], allow_none=T == 0),
+        _ptr(v, "v", torch.float32, T * sz["v"], allow_none=T == 0),
+        _ptr(beta, "beta", torch.float32, T * sz["beta"], allow_none=T == 0),
+        _ptr(gate, "gate", torch.float32, T * sz["gate"], allow_none=T == 0),
+        _ptr(o, "o", torch.float32, T * sz["v"], allow_none=True), _stream(stream))
+    _check("lq_prefill", rc)
 
 
 def lq_decode_step(cfg: Config, state, q, k, v, beta, gate, o, stream=None) -> None:

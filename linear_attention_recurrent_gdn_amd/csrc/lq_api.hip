@@ -78,6 +78,38 @@ int32_t lq_state_init(const lq_config* cfg, void* state, const float* S0, void* 
     return hip_status(launch_materialize(a, kModeInit, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
 }
 
+int32_t lq_prefill(const lq_config* cfg, void* state, const float* S0, int32_t n_tok, const float* q,
+                   const float* k, const float* v, const float* beta, const float* gate, float* o,
+                   void* stream) {
+    int32_t rc = check_config(cfg);
+    if (rc != LQ_OK) return rc;
+    if (state == nullptr || n_tok < 0) return LQ_EINVAL;
+    // offsets inside a 16-token chunk of the prompt are 32-bit element counts
+    if ((uint64_t)16 * cfg->n_seq * cfg->n_v_heads * cfg->d_k > 0xFFFFFFFFull) return LQ_EUNSUPPORTED;
+    if (!aligned(state, kSectionAlign) || (S0 != nullptr && !aligned(S0, 16))) return LQ_EINVAL;
+    if (n_tok > 0) {
+        if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || gate == nullptr)
+            return LQ_EINVAL;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(beta, 4) ||
+            !aligned(gate, cfg->gate_kind == LQ_GATE_CHANNEL ? 16 : 4) || (o != nullptr && !aligned(o, 16)))
+            return LQ_EINVAL;
+    }
+    lq_layout L;
+    compute_layout(*cfg, L);
+    MatArgs a{};
+    a.blob = blob_ptrs(state, L);
+    a.dm = dims_of(cfg);
+    a.S0 = S0;
+    a.n_tok = n_tok;
+    a.pq = q;
+    a.pk = k;
+    a.pv = v;
+    a.pbeta = beta;
+    a.pgate = gate;
+    a.po = n_tok > 0 ? o : nullptr;
+    return hip_status(launch_materialize(a, kModePrefill, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+}
+
 int32_t lq_decode_step(const lq_config* cfg, void* state, const float* q, const float* k,
                        const float* v, const float* beta, const float* gate, float* o,
                        void* stream) {

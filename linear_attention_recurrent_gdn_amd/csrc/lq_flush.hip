@@ -184,8 +184,10 @@ struct Stage {
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-// Four consecutive buffer elements (fp32, or binary16 converted exactly).
-__device__ __forceinline__ float4 load4_buf(const void* base, size_t off, bool h16) {
+// Four consecutive buffer elements (fp32, or binary16 converted exactly).  A
+// 32-bit element offset from a uniform base keeps the address in the
+// scalar-base form (no 64-bit per-lane address registers).
+__device__ __forceinline__ float4 load4_buf(const void* base, uint32_t off, bool h16) {
     if (h16) {
         const f16x4 h = *reinterpret_cast<const f16x4*>(reinterpret_cast<const _Float16*>(base) + off);
         return make_float4((float)h.x, (float)h.y, (float)h.z, (float)h.w);
@@ -193,24 +195,57 @@ __device__ __forceinline__ float4 load4_buf(const void* base, size_t off, bool h
     return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
 }
 
+// Token strides (elements) of the replayed tokens: the window buffer holds
+// them entry-major per unit (k, v: D; beta: 1; gate: 1 or D); a prompt is
+// token-major over all units.
+struct TokStrides {
+    size_t k, v, b, g;
+};
+
 template <int D, int NT, bool KDA>
 __device__ __forceinline__ Stage<KDA> fetch_stage(const void* bk, const void* bv, bool h16, const float* bb,
-                                                 const float* bg, int i0, int n_replay, int tid) {
+                                                 const float* bg, TokStrides ts, int i0, int n_replay, int tid) {
     constexpr int EB = 16;
     Stage<KDA> st;
     const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
     const int x = 4 * tid;
-    const int e = min(x / D, ne - 1), c = x % D;
-    st.k = load4_buf(bk, (size_t)(i0 + e) * D + c, h16);
-    st.v = load4_buf(bv, (size_t)(i0 + e) * D + c, h16);
-    if constexpr (KDA) st.g = *reinterpret_cast<const float4*>(bg + (size_t)(i0 + e) * D + c);
+    const uint32_t e = (uint32_t)min(x / D, ne - 1), c = (uint32_t)(x % D);
+    // uniform chunk bases, then 32-bit offsets inside the chunk (16 token strides)
+    const size_t esz = h16 ? 2 : 4;
+    const char* k0 = (const char*)bk + (size_t)i0 * ts.k * esz;
+    const char* v0 = (const char*)bv + (size_t)i0 * ts.v * esz;
+    const float* g0 = bg + (size_t)i0 * ts.g;
+    const float* b0 = bb + (size_t)i0 * ts.b;
+    st.k = load4_buf(k0, e * (uint32_t)ts.k + c, h16);
+    st.v = load4_buf(v0, e * (uint32_t)ts.v + c, h16);
+    if constexpr (KDA) st.g = *reinterpret_cast<const float4*>(g0 + (e * (uint32_t)ts.g + c));
     st.b = 0.f;
     st.al = 1.f;
     if (tid < EB) {
-        st.b = bb[i0 + min(tid, ne - 1)];
-        if constexpr (!KDA) st.al = bg[i0 + min(tid, ne - 1)];
+        const uint32_t t = (uint32_t)min(tid, ne - 1);
+        st.b = b0[t * (uint32_t)ts.b];
+        if constexpr (!KDA) st.al = g0[t * (uint32_t)ts.g];
     }
     return st;
+}
+
+// The chunk's queries straight into LDS (no registers): thread t copies 16
+// bytes of token-major [16][D] fp32 to byte 16 t of dst; a wavefront's 64
+// copies land consecutively from its base (the LDS address of
+// global_load_lds_dwordx4 is M0 + 16 * lane).  Completion is counted by
+// vmcnt: wait for it, then a barrier, before reading dst.
+template <int D>
+__device__ __forceinline__ void fetch_q_to_lds(const float* bq, size_t stride, int i0, int n_replay, int tid,
+                                               float* dst) {
+    constexpr int EB = 16;
+    const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
+    const int x = 4 * tid;
+    const uint32_t e = (uint32_t)min(x / D, ne - 1), c = (uint32_t)(x % D);
+    const int wave = tid / kWave;
+    const float* q0 = bq + (size_t)i0 * stride;
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(q0 + (e * (uint32_t)stride + c)),
+        (void __attribute__((address_space(3)))*)(dst + 4 * kWave * wave), 16, 0, 0);
 }
 
 }  // namespace
@@ -224,6 +259,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     constexpr int EB = 16;              // buffered tokens per chunk
     constexpr int KP = D + 2;           // padded FP64 length of a staged key
     constexpr int CPL = 2 * D / kWave;  // selection candidates per lane
+    constexpr bool PF = MODE == kModePrefill;
 
     __shared__ double lds_kf[EB][KP];                       // forward-scaled keys of the chunk
     __shared__ double lds_kb[KDA ? EB : 1][KDA ? KP : 1];  // back-scaled keys (channel gate)
@@ -239,6 +275,12 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     __shared__ int lds_anyfold;                             // channel gate: some column folded
     __shared__ double lds_gram[NW][EB][EB];                 // partial kf . kb over column slices
     __shared__ double lds_N[EB][EB];                        // Diag(beta) L
+    // prefill outputs: queries as fetched and scaled, qf . kb, its future part
+    __shared__ float lds_qraw[PF ? 2 : 1][PF ? EB : 1][PF ? D : 1];  // double buffer by chunk parity
+    __shared__ double lds_qf[PF ? EB : 1][PF ? KP : 1];
+    __shared__ double lds_gq[PF ? EB : 1];                  // scalar gate: g_e
+    __shared__ double lds_gramq[PF ? NW : 1][PF ? EB : 1][PF ? EB : 1];
+    __shared__ double lds_P[PF ? EB : 1][PF ? EB : 1];      // (e' <= e) qf_e . kb_e'
     __shared__ double lds_M[EB][EB];                        // (I + N)^-1
     __shared__ double lds_score[2 * D];
     __shared__ double lds_part[NW][D];
@@ -269,10 +311,11 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             const int fill = a.blob.fill[u];
             n_replay = fill < W ? fill : W;
         }
+        if constexpr (PF) n_replay = a.n_tok;
 
         // ---------------- A: the window-start state; T[b][r] = S[n][16b + 4q + r]
         v4d T[NB];
-        if constexpr (MODE == kModeInit) {
+        if constexpr (MODE == kModeInit || PF) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -340,21 +383,39 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             }
         }
 
-        // ---------------- B: forward replay of the buffered tokens, 16 per chunk
-        const bool h16 = a.dm.buffer_format == LQ_BUFFER_FP16;
+        // ---------------- B: forward replay of the buffered tokens (or the prompt), 16 per chunk
+        bool h16 = a.dm.buffer_format == LQ_BUFFER_FP16;
         const size_t esz = h16 ? 2 : 4;
         const void* bk = (const char*)a.blob.buf_k + kvec * (size_t)W * D * esz;
         const void* bv = (const char*)a.blob.buf_v + (size_t)u * W * D * esz;
         const float* bb = a.blob.buf_beta + (size_t)u * W;
         const float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
+        const float* bq = nullptr;
+        TokStrides ts{(size_t)D, (size_t)D, 1, KDA ? (size_t)D : 1};
+        if constexpr (PF) {
+            const size_t U = (size_t)a.dm.n_units;
+            const size_t KU = U / a.dm.n_v_heads * a.dm.n_k_heads;  // key-head rows per token
+            h16 = false;
+            bk = a.pk + kvec * D;
+            bq = a.pq + kvec * D;
+            bv = a.pv + (size_t)u * D;
+            bb = a.pbeta + u;
+            bg = a.pgate + (size_t)u * (KDA ? D : 1);
+            ts = TokStrides{KU * D, U * D, U, U * (KDA ? D : 1)};
+        }
         double gam = 1.0;  // scalar gate: g of the last replayed token (uniform)
         if constexpr (KDA) {
             if (tid < D) lds_G[tid] = 1.0;
         }
         Stage<KDA> pf{};
-        if (n_replay > 0) pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, 0, n_replay, tid);
+        if (n_replay > 0) {
+            pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, ts, 0, n_replay, tid);
+            if constexpr (PF) fetch_q_to_lds<D>(bq, ts.k, 0, n_replay, tid, &lds_qraw[0][0][0]);
+        }
         for (int i0 = 0; i0 < n_replay; i0 += EB) {
             const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
+            const int qb = (i0 / EB) & 1;  // prefill: this chunk's query buffer
+            if constexpr (PF) __builtin_amdgcn_s_waitcnt(0);  // this chunk's queries are in LDS
             __syncthreads();  // the previous chunk is done with LDS
             {
                 const int x = 4 * tid;
@@ -393,6 +454,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                         const bool fold = gam * P < kRescaleBelow;
                         const double g = (fold ? 1.0 : gam) * pre;
                         if (lane < EB) lds_ig[lane] = lane < ne ? 1.0 / g : 0.0;
+                        if (PF && lane < EB) lds_gq[lane] = lane < ne ? g : 0.0;
                         if (lane == 0) {
                             lds_gs[0] = fold ? gam : 1.0;
                             lds_gs[1] = (fold ? 1.0 : gam) * P;
@@ -401,8 +463,10 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 }
             }
             __syncthreads();
-            if (i0 + EB < n_replay)  // in flight during this chunk
-                pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, i0 + EB, n_replay, tid);
+            if (i0 + EB < n_replay) {  // in flight during this chunk
+                pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, ts, i0 + EB, n_replay, tid);
+                if constexpr (PF) fetch_q_to_lds<D>(bq, ts.k, i0 + EB, n_replay, tid, &lds_qraw[qb ^ 1][0][0]);
+            }
             if constexpr (KDA) {
                 // one thread per column: fold G into T if the chunk could take it
                 // below the threshold, then the key scaled both ways
@@ -419,20 +483,29 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                     }
 #pragma unroll
                     for (int e = 0; e < EB; ++e) {
-                        double kf = 0.0, kbk = 0.0;
+                        double kf = 0.0, kbk = 0.0, qf = 0.0;
                         if (e < ne) {
                             G *= fmax((double)lds_graw[e][c], kMinGate);
                             const double kc = (double)lds_kraw[e][c];
                             kf = G * kc;
                             kbk = kc / G;
+                            if constexpr (PF) qf = G * (double)lds_qraw[qb][e][c];
                         }
                         lds_kf[e][c] = kf;
                         lds_kb[e][c] = kbk;
+                        if constexpr (PF) lds_qf[e][c] = qf;
                     }
                     lds_G[c] = G;
                 }
             }
-            if constexpr (KDA) __syncthreads();
+            if constexpr (PF && !KDA) {
+                // queries scaled by the running gate: qf_e = g_e q_e
+                const int x = 4 * tid;
+                const int e = x / D, c = x % D;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lds_qf[e][c + i] = lds_gq[e] * (double)lds_qraw[qb][e][c + i];
+            }
+            if constexpr (KDA || PF) __syncthreads();
             // folds into T
             if constexpr (KDA) {
                 if (lds_anyfold) {  // uniform, rare
@@ -463,19 +536,46 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 const v4d g4 = g4a + g4b;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) lds_gram[wave][4 * r + q][m] = g4[r];
+                if constexpr (PF) {
+                    // partial qf . kb: lane (q, m), register r -> qf[4r + q] . kb[m]
+                    v4d h4a = {0.0, 0.0, 0.0, 0.0}, h4b = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                    for (int t = 0; t < 4; t += 2) {
+                        const int k = 16 * wave + 4 * t + q;
+                        h4a = mfma(lds_qf[m][k], kb[m][k], h4a);
+                        h4b = mfma(lds_qf[m][k + 4], kb[m][k + 4], h4b);
+                    }
+                    const v4d h4 = h4a + h4b;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) lds_gramq[wave][4 * r + q][m] = h4[r];
+                }
             }
             __syncthreads();
             // A = T Kf^T (wavefronts 1..), M (wavefront 0), then A for wavefront 0
+            // prefill: Aq = T Qf^T in the same pass (register r: token 4r + q, row n)
+            v4d Aq4 = {0.0, 0.0, 0.0, 0.0};
             auto gemm_a = [&]() {
                 // four independent accumulators keep the matrix pipe busy
                 v4d acc[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] = v4d{0.0, 0.0, 0.0, 0.0};
+                if constexpr (PF) {
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
+                    for (int b = 0; b < NB; ++b)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] = mfma(lds_kf[m][16 * b + 4 * q + r], T[b][r], acc[r]);
-                return (acc[0] + acc[1]) + (acc[2] + acc[3]);  // register r: A[token 4r + q][row n]
+                        for (int r = 0; r < 4; ++r) {
+                            acc[r & 1] = mfma(lds_kf[m][16 * b + 4 * q + r], T[b][r], acc[r & 1]);
+                            acc[2 + (r & 1)] = mfma(lds_qf[m][16 * b + 4 * q + r], T[b][r], acc[2 + (r & 1)]);
+                        }
+                    Aq4 = acc[2] + acc[3];
+                    return acc[0] + acc[1];
+                } else {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[r] = mfma(lds_kf[m][16 * b + 4 * q + r], T[b][r], acc[r]);
+                    return (acc[0] + acc[1]) + (acc[2] + acc[3]);  // register r: A[token 4r + q][row n]
+                }
             };
             v4d A4;
             if (wave != 0) {
@@ -490,6 +590,12 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 #pragma unroll
                     for (int w = 0; w < NW; ++w) sum += lds_gram[w][e][e2];
                     lds_N[e][e2] = e2 < e ? (double)lds_b[e] * sum : 0.0;
+                    if constexpr (PF) {
+                        double sq = 0.0;
+#pragma unroll
+                        for (int w = 0; w < NW; ++w) sq += lds_gramq[w][e][e2];
+                        lds_P[e][e2] = e2 <= e ? sq : 0.0;
+                    }
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
@@ -525,6 +631,21 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             C4a = mfma(lds_M[m][8 + q], R4[2], C4a);
             C4b = mfma(lds_M[m][12 + q], R4[3], C4b);
             const v4d C4 = C4a + C4b;
+            if constexpr (PF) {
+                // outputs of the chunk's tokens: o_e = T qf_e + sum_{e' <= e} C_e' (kb_e' . qf_e)
+                if (a.po != nullptr) {
+                    Aq4 = mfma(lds_P[m][q], C4[0], Aq4);
+                    Aq4 = mfma(lds_P[m][4 + q], C4[1], Aq4);
+                    Aq4 = mfma(lds_P[m][8 + q], C4[2], Aq4);
+                    Aq4 = mfma(lds_P[m][12 + q], C4[3], Aq4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int e = 4 * r + q;
+                        float* o0 = a.po + ((size_t)i0 * a.dm.n_units + u) * D;  // uniform
+                        if (e < ne) o0[(uint32_t)e * (uint32_t)a.dm.n_units * D + n] = (float)Aq4[r];
+                    }
+                }
+            }
             // T += C Kb: block b of S^T, token group r
             {
                 const double(*kb)[KP] = KDA ? (const double(*)[KP])lds_kb : (const double(*)[KP])lds_kf;
@@ -722,7 +843,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
         }
         if (tid == 0) {
             a.blob.fill[u] = 0;
-            if (MODE == kModeInit && u == 0) *a.blob.status = 0u;
+            if ((MODE == kModeInit || PF) && u == 0) *a.blob.status = 0u;
         }
         __syncthreads();  // LDS is reused by the next unit
     }
@@ -782,6 +903,7 @@ hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, 
     do {                                                         \
         if (mode == kModeInit) LQ_MAT(D_, K_, kModeInit);        \
         else if (mode == kModeFlush) LQ_MAT(D_, K_, kModeFlush); \
+        else if (mode == kModePrefill) LQ_MAT(D_, K_, kModePrefill); \
         else LQ_MAT(D_, K_, kModeDequant);                       \
     } while (0)
     if (d == 128) {

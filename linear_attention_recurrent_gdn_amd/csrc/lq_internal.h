@@ -112,7 +112,7 @@ struct Fp32DecodeArgs {
     float* o;
 };
 
-enum MatMode : int { kModeInit = 0, kModeFlush = 1, kModeDequant = 2 };
+enum MatMode : int { kModeInit = 0, kModeFlush = 1, kModeDequant = 2, kModePrefill = 3 };
 
 struct MatArgs {
     BlobPtrs blob;
@@ -121,6 +121,14 @@ struct MatArgs {
     const uint8_t* force;     // flush: per-sequence force mask or nullptr
     float* S_out;             // dequant: fp32 output
     int include_buffer;       // dequant: replay the buffered tokens
+    // prefill: the prompt, token-major (layouts as for one decode step, per token)
+    int n_tok;
+    const float* pq;
+    const float* pk;
+    const float* pv;
+    const float* pbeta;
+    const float* pgate;
+    float* po;                // outputs [n_tok][units][d_v], or nullptr
 };
 
 // Host launchers (lq_decode.hip / lq_flush.hip).  Return hipSuccess or the
