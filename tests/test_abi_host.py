@@ -116,6 +116,21 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert lib.lq_window_flush(ctypes.byref(c), None, None, None) == lq.LQ_EINVAL
     assert lib.lq_dequant_state(ctypes.byref(c), ok, None, 0, None) == lq.LQ_EINVAL
     assert lib.lq_read_status(ctypes.byref(c), ok, None, 0, None) == lq.LQ_EINVAL
+    # prefill: a negative prompt length, a missing input for a non-empty prompt,
+    # misaligned pointers; an empty prompt needs no inputs (then it is an init)
+    assert lib.lq_prefill(ctypes.byref(c), ok, None, -1, ok, ok, ok, ok, ok, ok, None) == lq.LQ_EINVAL
+    assert lib.lq_prefill(ctypes.byref(c), None, None, 0, None, None, None, None, None, None, None) == lq.LQ_EINVAL
+    pargs = [ok] * 5
+    for i in range(5):
+        a = list(pargs)
+        a[i] = None
+        assert lib.lq_prefill(ctypes.byref(c), ok, None, 3, *a, ok, None) == lq.LQ_EINVAL
+    a = list(pargs)
+    a[2] = P((1 << 20) + 4)  # v not 16-byte aligned
+    assert lib.lq_prefill(ctypes.byref(c), ok, None, 3, *a, ok, None) == lq.LQ_EINVAL
+    assert lib.lq_prefill(ctypes.byref(c), ok, None, 3, *pargs, P((1 << 20) + 8), None) == lq.LQ_EINVAL
+    big = cfg(n_seq=1 << 15, n_v_heads=64, n_k_heads=64).c()  # 16 tokens of v reach 2^32 elements
+    assert lib.lq_prefill(ctypes.byref(big), ok, None, 3, *pargs, ok, None) == lq.LQ_EUNSUPPORTED
 
 
 def test_strerror_is_static(lib):
