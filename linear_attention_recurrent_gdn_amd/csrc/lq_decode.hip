@@ -118,45 +118,46 @@ template <int EPL, int GE, bool H16>
 struct RingEntry {
     Vec<EPL> k, v;
     Vec<GE> g;
+    float2 ba;  // beta, scalar gate (uniform)
 };
 
 template <int EPL, int GE>
 struct RingEntry<EPL, GE, true> {
     uint32_t k, v;
     Vec<GE> g;
+    float2 ba;
 };
 
-// beta and scalar gate of the whole window, NWB per lane (token i in lane i % 64
-// of register i / 64)
+constexpr int kBufferFlags = 0x00020000;  // raw 32-bit buffer resource word 3 (gfx9 family)
+
+// EPL consecutive fp32 (or packed binary16 when H16) of a buffer resource at
+// a per-lane byte offset plus a uniform (scalar) byte offset.
+template <int EPL>
+__device__ __forceinline__ Vec<EPL> buf_load_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    Vec<EPL> x;
+    if constexpr (EPL == 2) {
+        // the builtin returns a two-element vector of its own (GCC vector) type
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        x.e[0] = __builtin_bit_cast(float, (unsigned int)w[0]);
+        x.e[1] = __builtin_bit_cast(float, (unsigned int)w[1]);
+    } else {
+        x.e[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+    return x;
+}
+
+template <int EPL>
+__device__ __forceinline__ uint32_t buf_load_halves(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    if constexpr (EPL == 2) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    else return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// beta and scalar gate of the whole window as loaded, NWB per lane (token i
+// in lane i % 64 of register i / 64)
 template <int NWB>
 struct WindowRegs {
     float b[NWB], a[NWB];
 };
-
-// beta and scalar gate of buffered token i (uniform): pick the register by
-// compare-and-select (constant indices only), then read the owning lane
-template <int NWB, bool KDA>
-__device__ __forceinline__ float2 window_scalars(WindowRegs<NWB> win, int i) {
-    float bsel = win.b[0], asel = win.a[0];
-#pragma unroll
-    for (int w = 1; w < NWB; ++w) {
-        bsel = (i >= w * kWave) ? win.b[w] : bsel;
-        asel = (i >= w * kWave) ? win.a[w] : asel;
-    }
-    float2 ba;
-    ba.x = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bsel), i & (kWave - 1)));
-    ba.y = 0.f;
-    if constexpr (!KDA)
-        ba.y = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, asel), i & (kWave - 1)));
-    return ba;
-}
-
-template <int EPL>
-__device__ __forceinline__ uint32_t load_half_word(const void* base, size_t off) {
-    const _Float16* p = reinterpret_cast<const _Float16*>(base) + off;
-    if constexpr (EPL == 2) return *reinterpret_cast<const uint32_t*>(p);
-    else return (uint32_t)*reinterpret_cast<const uint16_t*>(p);
-}
 
 template <int EPL>
 __device__ __forceinline__ Vec<EPL> unpack_halves(uint32_t w) {
@@ -181,6 +182,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
 
     __shared__ float lds_x[D];       // s * r, r = A_1..A_n q (all waves read it)
     __shared__ float lds_add[D];     // buffered-token and compensator terms of o
+    __shared__ float2 lds_ba[256];   // wavefront 0: beta and scalar gate of each window slot
 
     const int u = blockIdx.x;
     if (u >= a.dm.n_units) return;
@@ -234,15 +236,25 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         } else {
             cur.g.e[0] = a.gate[u];
         }
+        // the window's entries through buffer resources: a constant per-lane
+        // offset and a scalar per-entry offset, no per-lane address arithmetic
+        constexpr int ESZ = H16 ? 2 : 4;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (char*)a.blob.buf_k + kb0 * ESZ, (short)0, W * D * ESZ, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (char*)a.blob.buf_v + vb0 * ESZ, (short)0, W * D * ESZ, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            bg, (short)0, KDA ? W * D * 4 : 4, kBufferFlags);
+        const int voff = lane * EPL * ESZ;
         auto load_entry = [&](int i, RingEntry<EPL, GE, H16>& en) {
             if constexpr (H16) {
-                en.k = load_half_word<EPL>(a.blob.buf_k, kb0 + (size_t)i * D + lane * EPL);
-                en.v = load_half_word<EPL>(a.blob.buf_v, vb0 + (size_t)i * D + lane * EPL);
+                en.k = buf_load_halves<EPL>(rk, voff, i * D * ESZ);
+                en.v = buf_load_halves<EPL>(rv, voff, i * D * ESZ);
             } else {
-                en.k = load_vec<EPL>(reinterpret_cast<const float*>(a.blob.buf_k) + kb0 + (size_t)i * D + lane * EPL);
-                en.v = load_vec<EPL>(reinterpret_cast<const float*>(a.blob.buf_v) + vb0 + (size_t)i * D + lane * EPL);
+                en.k = buf_load_f32<EPL>(rk, voff, i * D * ESZ);
+                en.v = buf_load_f32<EPL>(rv, voff, i * D * ESZ);
             }
-            if constexpr (KDA) en.g = load_vec<GE>(bg + (size_t)i * D + lane * EPL);
+            if constexpr (KDA) en.g = buf_load_f32<GE>(rg, lane * EPL * 4, i * D * 4);
         };
         RingEntry<EPL, GE, H16> ring[P];
 #pragma unroll
@@ -281,6 +293,16 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         }
         if (h % a.dm.group == 0) store_buf<EPL, H16>(a.blob.buf_k, kb0 + (size_t)j * D + lane * EPL, cur.k);
         store_buf<EPL, H16>(a.blob.buf_v, vb0 + (size_t)j * D + lane * EPL, cur.v);
+        // beta and scalar gate of every buffered slot into LDS, then the ring's
+        // first entries take theirs (uniform reads; later refills read ahead)
+#pragma unroll
+        for (int w = 0; w < NWB; ++w)
+            if (lane + w * kWave < W) lds_ba[lane + w * kWave] = make_float2(win.b[w], win.a[w]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int p = 0; p < P; ++p) ring[p].ba = lds_ba[max(j - 1 - p, 0)];
         if constexpr (KDA) {
             store_vec(bg + (size_t)j * D + lane * EPL, cur.g);
         } else {
@@ -298,7 +320,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         auto step = [&](const Vec<EPL>& ek, const Vec<EPL>& ev, const Vec<GE>& eg, float beta, float alpha) {
             float p = 0.f;
             for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(ek.e[e], r.e[e], p);
-            const float red = wave_sum(p);
+            const float red = wave_sum_all(p);
             const float cr = beta * red;
             if constexpr (KDA) {
                 for (int e = 0; e < EPL; ++e) {
@@ -322,17 +344,21 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
             if constexpr (H16) return unpack_halves<EPL>(ring[p].v);
             else return ring[p].v;
         };
-        for (int s0 = 0; s0 < j; s0 += P) {
+        // whole ring cycles, then the last partial one (no refills needed there)
+        int s0 = 0;
+        for (; s0 + P <= j; s0 += P) {
 #pragma unroll
             for (int p = 0; p < P; ++p) {
                 const int i = j - 1 - (s0 + p);
-                if (i >= 0) {
-                    const float2 ba = window_scalars<NWB, KDA>(win, i);
-                    step(ring_k(p), ring_v(p), ring[p].g, ba.x, ba.y);
-                }
-                load_entry(max(i - P, 0), ring[p]);
+                step(ring_k(p), ring_v(p), ring[p].g, ring[p].ba.x, ring[p].ba.y);
+                const int ir = max(i - P, 0);
+                load_entry(ir, ring[p]);
+                ring[p].ba = lds_ba[ir];
             }
         }
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            if (s0 + p < j) step(ring_k(p), ring_v(p), ring[p].g, ring[p].ba.x, ring[p].ba.y);
         if constexpr (!KDA)
             for (int e = 0; e < EPL; ++e) r.e[e] *= sc;
 
@@ -495,17 +521,19 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
     }
 }
 
+// register-ring depths (buffered tokens in flight per unit), from sweeps on
+// the decode workloads
 #ifndef LQ_RING_GDN
-#define LQ_RING_GDN 4
+#define LQ_RING_GDN 6
 #endif
 #ifndef LQ_RING_KDA
-#define LQ_RING_KDA 6
+#define LQ_RING_KDA 8
 #endif
 #ifndef LQ_RING_GDN_H16
 #define LQ_RING_GDN_H16 6
 #endif
 #ifndef LQ_RING_KDA_H16
-#define LQ_RING_KDA_H16 6
+#define LQ_RING_KDA_H16 4
 #endif
 
 template <int NWB, int FMT, bool H16>

@@ -196,6 +196,22 @@ __device__ __forceinline__ float wave_sum(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
+// Sum over the whole wavefront, left in every lane (no scalar round trip):
+// four DPP stages inside each 16-lane row, then the gfx950 row swaps
+// (v_permlane16_swap, v_permlane32_swap) add the rows pairwise.
+__device__ __forceinline__ float wave_sum_all(float x) {
+    x += dpp_f32<kDppQuadXor1>(x);
+    x += dpp_f32<kDppQuadXor2>(x);
+    x += dpp_f32<kDppRowHalfMirror>(x);
+    x += dpp_f32<kDppRowMirror>(x);
+    const int b = __builtin_bit_cast(int, x);
+    const auto p16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    x = __builtin_bit_cast(float, (int)p16[0]) + __builtin_bit_cast(float, (int)p16[1]);
+    const int c = __builtin_bit_cast(int, x);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+    return __builtin_bit_cast(float, (int)p32[0]) + __builtin_bit_cast(float, (int)p32[1]);
+}
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences global
