@@ -36,8 +36,9 @@
 //      a unit lower-triangular 16x16 matrix shared by all rows.  Both
 //      d_v x d_k x 16 products and C run on the FP64 matrix cores; L is
 //      assembled from per-wavefront partial products over column slices, and
-//      M is solved by forward substitution in one wavefront while the others
-//      form A;
+//      M^T is solved by back substitution in one wavefront (all 64 lanes, each
+//      holding four entries in the accumulator layout, finished rows broadcast
+//      across row groups with the gfx950 permlane swaps) while the others form A;
 //   C  quantizer, in the same workgroup (readings; the pages print no
 //      formula): line scores = squared L2 norms of rows and columns; the
 //      n_comp best lines (ties to the lower candidate index, rows before
@@ -133,6 +134,27 @@ __device__ __forceinline__ int reduce_columns(double (&v)[NV], int m) {
         rs_stage<2, kDppRowRor8, MAX>(v, (m & 8) != 0);
         return 8 * ((m >> 2) & 1) + 4 * (m & 1) + 2 * ((m >> 1) & 1) + ((m >> 3) & 1);
     }
+}
+
+// The value that lane m of row group g (lanes 16g .. 16g + 15) holds, in lane
+// m of every row group (g uniform): v_permlane32_swap replicates the half
+// that holds g, v_permlane16_swap then the row of that half.
+__device__ __forceinline__ double group_bcast(double x, int g) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
+    {
+        const auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+        const auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+        lo = (g & 2) ? (int)pl[1] : (int)pl[0];
+        hi = (g & 2) ? (int)ph[1] : (int)ph[0];
+    }
+    {
+        const auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+        const auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+        lo = (g & 1) ? (int)pl[1] : (int)pl[0];
+        hi = (g & 1) ? (int)ph[1] : (int)ph[0];
+    }
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
 __device__ __forceinline__ double shfl_xor_f64(double x, int m) {
@@ -274,7 +296,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     __shared__ double lds_fold[KDA ? D : 1];                // channel gate: fold factor per column
     __shared__ int lds_anyfold;                             // channel gate: some column folded
     __shared__ double lds_gram[NW][EB][EB];                 // partial kf . kb over column slices
-    __shared__ double lds_N[EB][EB];                        // Diag(beta) L
+    __shared__ double lds_N[EB][4][4];                      // Diag(beta) L, [e2][q][r] = N[e2][4r + q]
     // prefill outputs: queries as fetched and scaled, qf . kb, its future part
     __shared__ float lds_qraw[PF ? 2 : 1][PF ? EB : 1][PF ? D : 1];  // double buffer by chunk parity
     __shared__ double lds_qf[PF ? EB : 1][PF ? KP : 1];
@@ -589,7 +611,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                     double sum = 0.0;
 #pragma unroll
                     for (int w = 0; w < NW; ++w) sum += lds_gram[w][e][e2];
-                    lds_N[e][e2] = e2 < e ? (double)lds_b[e] * sum : 0.0;
+                    lds_N[e][e2 & 3][e2 >> 2] = e2 < e ? (double)lds_b[e] * sum : 0.0;
                     if constexpr (PF) {
                         double sq = 0.0;
 #pragma unroll
@@ -600,19 +622,24 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                // M = (I + N)^-1 by forward substitution, one column per lane
-                if (lane < EB) {
-                    double x[EB];
+                // Y = M^T = (I + N^T)^-1 with all 64 lanes, right-looking back
+                // substitution: lane (q, m), register r holds Y[4r + q][m].  Row e2
+                // is final once the rows below it have been folded in; it is then
+                // broadcast to the four row groups and folded into every row
+                // above it (N[e2][e] is zero for e >= e2, so no masking).
+                v4d Y;
 #pragma unroll
-                    for (int e = 0; e < EB; ++e) {
-                        double t = (e == lane) ? 1.0 : 0.0;
+                for (int r = 0; r < 4; ++r) Y[r] = (4 * r + q == m) ? 1.0 : 0.0;
 #pragma unroll
-                        for (int e2 = 0; e2 < e; ++e2) t = __builtin_fma(-lds_N[e][e2], x[e2], t);
-                        x[e] = t;
-                    }
+                for (int e2 = EB - 1; e2 >= 1; --e2) {
+                    const double y = group_bcast(Y[e2 >> 2], e2 & 3);
+                    const double* nrow = &lds_N[e2][q][0];
 #pragma unroll
-                    for (int e = 0; e < EB; ++e) lds_M[e][lane] = x[e];
+                    for (int r = 0; r < 4; ++r) Y[r] = __builtin_fma(-nrow[r], y, Y[r]);
                 }
+                // Y[4r + q][m] = M[m][4r + q]
+#pragma unroll
+                for (int r = 0; r < 4; ++r) lds_M[m][4 * r + q] = Y[r];
             }
             __syncthreads();
             if (wave == 0) A4 = gemm_a();
