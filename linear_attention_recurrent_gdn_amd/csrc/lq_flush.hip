@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     __shared__ float lds_al[EB];                            // scalar gate: gates as fetched
     __shared__ double lds_ig[EB];                           // scalar gate: 1 / g_e
     __shared__ double lds_gs[2];                            // scalar gate: fold factor, new g
-    __shared__ double lds_G[KDA ? D : 1];                   // channel gate: running G per column
+    __shared__ double lds_G[2][KDA ? D : 1];                // channel gate: running G per column (by chunk parity)
     __shared__ double lds_fold[KDA ? D : 1];                // channel gate: fold factor per column
     __shared__ int lds_anyfold;                             // channel gate: some column folded
     __shared__ double lds_gram[NW][EB][EB];                 // partial kf . kb over column slices
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
         }
         double gam = 1.0;  // scalar gate: g of the last replayed token (uniform)
         if constexpr (KDA) {
-            if (tid < D) lds_G[tid] = 1.0;
+            if (tid < D) lds_G[0][tid] = 1.0;
         }
         Stage<KDA> pf{};
         if (n_replay > 0) {
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
         }
         for (int i0 = 0; i0 < n_replay; i0 += EB) {
             const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
-            const int qb = (i0 / EB) & 1;  // prefill: this chunk's query buffer
+            const int qb = (i0 / EB) & 1;  // chunk parity: query buffer (prefill), running gate (channel)
             if constexpr (PF) __builtin_amdgcn_s_waitcnt(0);  // this chunk's queries are in LDS
             __syncthreads();  // the previous chunk is done with LDS
             {
@@ -490,21 +490,31 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 if constexpr (PF) fetch_q_to_lds<D>(bq, ts.k, i0 + EB, n_replay, tid, &lds_qraw[qb ^ 1][0][0]);
             }
             if constexpr (KDA) {
-                // one thread per column: fold G into T if the chunk could take it
-                // below the threshold, then the key scaled both ways
-                if (tid < D) {
-                    const int c = tid;
-                    double G = lds_G[c];
-                    double P = 1.0;
-                    for (int e = 0; e < ne; ++e) P *= fmax((double)lds_graw[e][c], kMinGate);
-                    const bool fold = G * P < kRescaleBelow;
-                    lds_fold[c] = fold ? G : 1.0;
-                    if (fold) {
-                        G = 1.0;
-                        lds_anyfold = 1;  // every writer stores the same value
-                    }
+                // four threads per column, four tokens each: fold G into T if the
+                // chunk could take it below the threshold, then the keys (and
+                // queries) scaled by the running gate product, both ways
+                static_assert(NT == 4 * D, "four threads per column");
+                {
+                    const int c = tid % D, seg = tid / D;
+                    double pre = 1.0, P = 1.0;  // product before this thread's tokens, whole chunk
 #pragma unroll
                     for (int e = 0; e < EB; ++e) {
+                        const double al = e < ne ? fmax((double)lds_graw[e][c], kMinGate) : 1.0;
+                        if (e < 4 * seg) pre *= al;
+                        P *= al;
+                    }
+                    // read this chunk's G, write the next chunk's: no thread of
+                    // the column overwrites what another still has to read
+                    const double G0 = lds_G[qb][c];
+                    const bool fold = G0 * P < kRescaleBelow;  // the same in the column's four threads
+                    if (seg == 0) {
+                        lds_fold[c] = fold ? G0 : 1.0;
+                        if (fold) lds_anyfold = 1;  // every writer stores the same value
+                    }
+                    double G = (fold ? 1.0 : G0) * pre;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 4 * seg + i;
                         double kf = 0.0, kbk = 0.0, qf = 0.0;
                         if (e < ne) {
                             G *= fmax((double)lds_graw[e][c], kMinGate);
@@ -517,7 +527,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                         lds_kb[e][c] = kbk;
                         if constexpr (PF) lds_qf[e][c] = qf;
                     }
-                    lds_G[c] = G;
+                    if (seg == 3) lds_G[qb ^ 1][c] = (fold ? 1.0 : G0) * P;
                 }
             }
             if constexpr (PF && !KDA) {
@@ -690,7 +700,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) T[b][r] *= lds_G[16 * b + 4 * q + r];
+                    for (int r = 0; r < 4; ++r) T[b][r] *= lds_G[((n_replay + EB - 1) / EB) & 1][16 * b + 4 * q + r];
             }
         } else {
 #pragma unroll
