@@ -236,3 +236,39 @@ def test_repeatable_bitwise():
     assert torch.equal(runs[0][0], runs[1][0])
     for key in ("fill", "codes", "sigma", "smooth", "comp_idx", "comp_vec"):
         assert torch.equal(runs[0][1][key], runs[1][1][key]), key
+
+
+@pytest.mark.parametrize("buffer", ["fp32", "fp16"])
+def test_checkpoint_mid_window_resumes_bitwise(buffer):
+    # the blob is self-contained: copied to the host in the middle of a window
+    # and restored into a fresh allocation, it continues exactly as the original
+    # (GQA, so the shared key buffer travels too)
+    wl = small("gdn_decode", name="ckpt", n_seq=2, n_v_heads=4, n_k_heads=2, window=8, n_comp=3, prefill=0,
+               buffer_format=buffer)
+    cfg = _cfg(wl)
+    S0 = torch.randn(wl.n_units, wl.d, wl.d, device="cuda", generator=torch.Generator("cuda").manual_seed(2))
+    st = lq.new_state(cfg)
+    lq.lq_state_init(cfg, st, S0)
+    o = torch.empty(wl.n_units * wl.d, device="cuda")
+    toks = [{k: torch.from_numpy(v).cuda() for k, v in I.token(wl, t).items()} for t in range(20)]
+
+    def run(state, t0, t1):
+        out = []
+        for t in range(t0, t1):
+            x = toks[t]
+            lq.lq_decode_step(cfg, state, x["q"], x["k"], x["v"], x["beta"], x["gate"], o)
+            out.append(o.clone())
+            if (t + 1) % wl.window == 0:
+                lq.lq_window_flush(cfg, state, None)
+        return torch.stack(out)
+
+    run(st, 0, 11)  # one flush behind, three tokens into the next window
+    saved = st.cpu()
+    a = run(st, 11, 20)
+    restored = lq.new_state(cfg)
+    restored.copy_(saved)
+    b = run(restored, 11, 20)
+    assert torch.equal(a, b)
+    va, vb = lq.state_views(cfg, st), lq.state_views(cfg, restored)
+    for key in ("fill", "codes", "sigma", "smooth", "comp_idx", "comp_vec", "buf_k", "buf_v"):
+        assert torch.equal(va[key], vb[key]), key
