@@ -157,12 +157,53 @@ __device__ __forceinline__ double group_bcast(double x, int g) {
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-__device__ __forceinline__ double shfl_xor_f64(double x, int m) {
-    const uint64_t b = __builtin_bit_cast(uint64_t, x);
-    const int src = (lane_id() ^ m) << 2;
-    const int lo = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)b);
-    const int hi = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(b >> 32));
-    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+// Wavefront argmax of (value, candidate index), larger value first, equal
+// values to the lower index; the result in every lane.  Lanes are paired by
+// DPP inside each 16-lane row (quad swaps, then the half-row and row
+// mirrors), then the rows by the gfx950 row swaps, which hand every lane both
+// values of its pair: no LDS round trips.
+struct Cand {
+    double v;
+    int i;
+};
+
+__device__ __forceinline__ Cand better(Cand a, Cand b) {
+    return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+}
+
+template <int CTRL>
+__device__ __forceinline__ Cand argmax_dpp(Cand a) {
+    Cand b;
+    b.v = dpp_f64<CTRL>(a.v);
+    b.i = __builtin_amdgcn_update_dpp(0, a.i, CTRL, 0xF, 0xF, false);
+    return better(a, b);
+}
+
+template <bool WIDE>
+__device__ __forceinline__ Cand argmax_swap(Cand a) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, a.v);
+    const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+    const auto pl = WIDE ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                         : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto ph = WIDE ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                         : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const auto pi = WIDE ? __builtin_amdgcn_permlane32_swap(a.i, a.i, false, false)
+                         : __builtin_amdgcn_permlane16_swap(a.i, a.i, false, false);
+    Cand x, y;
+    x.v = __builtin_bit_cast(double, ((uint64_t)(uint32_t)ph[0] << 32) | (uint32_t)pl[0]);
+    x.i = (int)pi[0];
+    y.v = __builtin_bit_cast(double, ((uint64_t)(uint32_t)ph[1] << 32) | (uint32_t)pl[1]);
+    y.i = (int)pi[1];
+    return better(x, y);
+}
+
+__device__ __forceinline__ Cand wave_argmax(Cand a) {
+    a = argmax_dpp<kDppQuadXor1>(a);
+    a = argmax_dpp<kDppQuadXor2>(a);
+    a = argmax_dpp<kDppRowHalfMirror>(a);
+    a = argmax_dpp<kDppRowMirror>(a);
+    a = argmax_swap<false>(a);
+    return argmax_swap<true>(a);
 }
 
 // E4M3 byte of x (FP64): the nearest value of the 8-bit float format with
@@ -767,13 +808,9 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                         bv_ = val[i];
                         bi = lane * CPL + i;
                     }
-                for (int mm = 1; mm < kWave; mm <<= 1) {
-                    const double ov = shfl_xor_f64(bv_, mm);
-                    const int oi = __shfl_xor(bi, mm);
-                    if (ov > bv_ || (ov == bv_ && oi < bi)) {
-                        bv_ = ov;
-                        bi = oi;
-                    }
+                {
+                    const Cand best = wave_argmax(Cand{bv_, bi});
+                    bi = best.i;
                 }
 #pragma unroll
                 for (int i = 0; i < CPL; ++i)
