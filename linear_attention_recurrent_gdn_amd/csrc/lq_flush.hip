@@ -376,6 +376,37 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
         }
         if constexpr (PF) n_replay = a.n_tok;
 
+        // the replayed tokens (window buffer, or the prompt): the first chunk is
+        // requested before the window-start state so the two latencies overlap
+        bool h16 = a.dm.buffer_format == LQ_BUFFER_FP16;
+        const size_t esz = h16 ? 2 : 4;
+        const void* bk = (const char*)a.blob.buf_k + kvec * (size_t)W * D * esz;
+        const void* bv = (const char*)a.blob.buf_v + (size_t)u * W * D * esz;
+        const float* bb = a.blob.buf_beta + (size_t)u * W;
+        const float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
+        const float* bq = nullptr;
+        TokStrides ts{(size_t)D, (size_t)D, 1, KDA ? (size_t)D : 1};
+        if constexpr (PF) {
+            const size_t U = (size_t)a.dm.n_units;
+            const size_t KU = U / a.dm.n_v_heads * a.dm.n_k_heads;  // key-head rows per token
+            h16 = false;
+            bk = a.pk + kvec * D;
+            bq = a.pq + kvec * D;
+            bv = a.pv + (size_t)u * D;
+            bb = a.pbeta + u;
+            bg = a.pgate + (size_t)u * (KDA ? D : 1);
+            ts = TokStrides{KU * D, U * D, U, U * (KDA ? D : 1)};
+        }
+        double gam = 1.0;  // scalar gate: g of the last replayed token (uniform)
+        if constexpr (KDA) {
+            if (tid < D) lds_G[0][tid] = 1.0;
+        }
+        Stage<KDA> pf{};
+        if (n_replay > 0) {
+            pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, ts, 0, n_replay, tid);
+            if constexpr (PF) fetch_q_to_lds<D>(bq, ts.k, 0, n_replay, tid, &lds_qraw[0][0][0]);
+        }
+
         // ---------------- A: the window-start state; T[b][r] = S[n][16b + 4q + r]
         v4d T[NB];
         if constexpr (MODE == kModeInit || PF) {
@@ -447,34 +478,6 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
         }
 
         // ---------------- B: forward replay of the buffered tokens (or the prompt), 16 per chunk
-        bool h16 = a.dm.buffer_format == LQ_BUFFER_FP16;
-        const size_t esz = h16 ? 2 : 4;
-        const void* bk = (const char*)a.blob.buf_k + kvec * (size_t)W * D * esz;
-        const void* bv = (const char*)a.blob.buf_v + (size_t)u * W * D * esz;
-        const float* bb = a.blob.buf_beta + (size_t)u * W;
-        const float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
-        const float* bq = nullptr;
-        TokStrides ts{(size_t)D, (size_t)D, 1, KDA ? (size_t)D : 1};
-        if constexpr (PF) {
-            const size_t U = (size_t)a.dm.n_units;
-            const size_t KU = U / a.dm.n_v_heads * a.dm.n_k_heads;  // key-head rows per token
-            h16 = false;
-            bk = a.pk + kvec * D;
-            bq = a.pq + kvec * D;
-            bv = a.pv + (size_t)u * D;
-            bb = a.pbeta + u;
-            bg = a.pgate + (size_t)u * (KDA ? D : 1);
-            ts = TokStrides{KU * D, U * D, U, U * (KDA ? D : 1)};
-        }
-        double gam = 1.0;  // scalar gate: g of the last replayed token (uniform)
-        if constexpr (KDA) {
-            if (tid < D) lds_G[0][tid] = 1.0;
-        }
-        Stage<KDA> pf{};
-        if (n_replay > 0) {
-            pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, ts, 0, n_replay, tid);
-            if constexpr (PF) fetch_q_to_lds<D>(bq, ts.k, 0, n_replay, tid, &lds_qraw[0][0][0]);
-        }
         for (int i0 = 0; i0 < n_replay; i0 += EB) {
             const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
             const int qb = (i0 / EB) & 1;  // chunk parity: query buffer (prefill), running gate (channel)
