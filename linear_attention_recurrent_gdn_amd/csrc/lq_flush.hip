@@ -344,7 +344,6 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     __shared__ double lds_gq[PF ? EB : 1];                  // scalar gate: g_e
     __shared__ double lds_gramq[PF ? NW : 1][PF ? EB : 1][PF ? EB : 1];
     __shared__ double lds_P[PF ? EB : 1][PF ? EB : 1];      // (e' <= e) qf_e . kb_e'
-    __shared__ double lds_M[EB][EB];                        // (I + N)^-1
     __shared__ double lds_score[2 * D];
     __shared__ double lds_part[NW][D];
     __shared__ float lds_smooth[D];
@@ -627,76 +626,114 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 }
             }
             __syncthreads();
-            // A = T Kf^T (wavefronts 1..), M (wavefront 0), then A for wavefront 0
-            // prefill: Aq = T Qf^T in the same pass (register r: token 4r + q, row n)
+            // N = Diag(beta) L (strictly lower), and for the prefill P, each
+            // element summed over the slices in a fixed order, shared out over
+            // the whole block
+            {
+                constexpr int NEL = (PF ? 2 : 1) * EB * EB;
+#pragma unroll
+                for (int t = 0; t < (NEL + NT - 1) / NT; ++t) {
+                    const int idx = tid + NT * t;
+                    if (NEL % NT != 0 && idx >= NEL) break;
+                    const int j = idx % (EB * EB);
+                    const int e = j / EB, e2 = j % EB;
+                    double sum = 0.0;
+                    if (!PF || idx < EB * EB) {
+#pragma unroll
+                        for (int w = 0; w < NW; ++w) sum += lds_gram[w][e][e2];
+                        lds_N[e][e2 & 3][e2 >> 2] = e2 < e ? (double)lds_b[e] * sum : 0.0;
+                    } else if constexpr (PF) {
+#pragma unroll
+                        for (int w = 0; w < NW; ++w) sum += lds_gramq[w][e][e2];
+                        lds_P[e][e2] = e2 <= e ? sum : 0.0;
+                    }
+                }
+            }
+            __syncthreads();
+            // every wavefront: A = T Kf^T (prefill: also Aq = T Qf^T, register r:
+            // token 4r + q, row n) on the matrix pipe, and between its products
+            // its own copy of Y = M^T = (I + N^T)^-1 on the vector ALU, by
+            // right-looking back substitution: lane (q, m), register r holds
+            // Y[4r + q][m].  Row e2 is final once the rows below it have been
+            // folded in; it is then broadcast to the four row groups and folded
+            // into every row above it (N[e2][e] is zero for e >= e2, so no
+            // masking).  Y[r] in lane (q, m) is M[m][4r + q]: the left operand of
+            // C = M R as the matrix pipe takes it.  The keys of block b + 1 are
+            // requested before the products of block b; the scheduling barriers
+            // keep that order.
             v4d Aq4 = {0.0, 0.0, 0.0, 0.0};
-            auto gemm_a = [&]() {
-                // four independent accumulators keep the matrix pipe busy
+            v4d A4;
+            v4d Y;
+            {
+                constexpr int SPB = (EB - 2 + NB) / NB;  // substitution steps per key block
                 v4d acc[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] = v4d{0.0, 0.0, 0.0, 0.0};
-                if constexpr (PF) {
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            acc[r & 1] = mfma(lds_kf[m][16 * b + 4 * q + r], T[b][r], acc[r & 1]);
-                            acc[2 + (r & 1)] = mfma(lds_qf[m][16 * b + 4 * q + r], T[b][r], acc[2 + (r & 1)]);
-                        }
-                    Aq4 = acc[2] + acc[3];
-                    return acc[0] + acc[1];
-                } else {
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[r] = mfma(lds_kf[m][16 * b + 4 * q + r], T[b][r], acc[r]);
-                    return (acc[0] + acc[1]) + (acc[2] + acc[3]);  // register r: A[token 4r + q][row n]
-                }
-            };
-            v4d A4;
-            if (wave != 0) {
-                A4 = gemm_a();
-            } else {
-                // N = Diag(beta) L (strictly lower), summed over the slices in a fixed order
-#pragma unroll
-                for (int t = 0; t < EB * EB / kWave; ++t) {
-                    const int idx = lane + kWave * t;
-                    const int e = idx / EB, e2 = idx % EB;
-                    double sum = 0.0;
-#pragma unroll
-                    for (int w = 0; w < NW; ++w) sum += lds_gram[w][e][e2];
-                    lds_N[e][e2 & 3][e2 >> 2] = e2 < e ? (double)lds_b[e] * sum : 0.0;
-                    if constexpr (PF) {
-                        double sq = 0.0;
-#pragma unroll
-                        for (int w = 0; w < NW; ++w) sq += lds_gramq[w][e][e2];
-                        lds_P[e][e2] = e2 <= e ? sq : 0.0;
-                    }
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                // Y = M^T = (I + N^T)^-1 with all 64 lanes, right-looking back
-                // substitution: lane (q, m), register r holds Y[4r + q][m].  Row e2
-                // is final once the rows below it have been folded in; it is then
-                // broadcast to the four row groups and folded into every row
-                // above it (N[e2][e] is zero for e >= e2, so no masking).
-                v4d Y;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Y[r] = (4 * r + q == m) ? 1.0 : 0.0;
+                // prefill: the queries of block b are requested with the keys of
+                // block b + 1 (one buffer, the products on keys go first)
+                double kc[2][4], qc[4];
+                auto load_keys = [&](int b, double* kd) {
 #pragma unroll
-                for (int e2 = EB - 1; e2 >= 1; --e2) {
-                    const double y = group_bcast(Y[e2 >> 2], e2 & 3);
-                    const double* nrow = &lds_N[e2][q][0];
+                    for (int r = 0; r < 4; ++r) kd[r] = lds_kf[m][16 * b + 4 * q + r];
+                };
+                load_keys(0, kc[0]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) Y[r] = __builtin_fma(-nrow[r], y, Y[r]);
+                for (int b = 0; b < NB; ++b) {
+                    const int cur = b & 1;
+                    if (b + 1 < NB) load_keys(b + 1, kc[cur ^ 1]);
+                    if constexpr (PF) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) qc[r] = lds_qf[m][16 * b + 4 * q + r];
+                    }
+                    double nr[SPB][4];
+#pragma unroll
+                    for (int s = 0; s < SPB; ++s) {
+                        const int e2 = EB - 1 - (SPB * b + s);
+                        if (e2 >= 1) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) nr[s][r] = lds_N[e2][q][r];
+                        }
+                    }
+                    if constexpr (PF) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[0] = mfma(kc[cur][r], T[b][r], acc[0]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[2] = mfma(qc[r], T[b][r], acc[2]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[r] = mfma(kc[cur][r], T[b][r], acc[r]);
+                    }
+#pragma unroll
+                    for (int s = 0; s < SPB; ++s) {
+                        const int e2 = EB - 1 - (SPB * b + s);
+                        if (e2 >= 1) {
+                            const double y = group_bcast(Y[e2 >> 2], e2 & 3);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) Y[r] = __builtin_fma(-nr[s][r], y, Y[r]);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                // Y[4r + q][m] = M[m][4r + q]
-#pragma unroll
-                for (int r = 0; r < 4; ++r) lds_M[m][4 * r + q] = Y[r];
+                if constexpr (PF) {
+                    // one accumulator each for keys and queries (registers are
+                    // short here; the matrix pipe forwards a dependent accumulator)
+                    Aq4 = acc[2];
+                    A4 = acc[0];
+                } else {
+                    A4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);  // register r: A[token 4r + q][row n]
+                }
             }
-            __syncthreads();
-            if (wave == 0) A4 = gemm_a();
+            // keys of the update T += C Kb, token group 0 requested ahead
+            const double(*kb)[KP] = KDA ? (const double(*)[KP])lds_kb : (const double(*)[KP])lds_kf;
+            const int colm = 4 * (m & 3) + (m >> 2);  // column of block b held by result row m
+            double kv[2][NB];
+            auto load_kb = [&](int r, double* dst) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) dst[b] = kb[4 * r + q][16 * b + colm];
+            };
+            load_kb(0, kv[0]);
             // R = (v' - A) Diag(beta): register r -> token 4r + q, row n
             v4d R4;
 #pragma unroll
@@ -707,10 +744,10 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             }
             // C = M R (per row): register r -> token 4r + q, row n
             v4d C4a = {0.0, 0.0, 0.0, 0.0}, C4b = {0.0, 0.0, 0.0, 0.0};
-            C4a = mfma(lds_M[m][q], R4[0], C4a);
-            C4b = mfma(lds_M[m][4 + q], R4[1], C4b);
-            C4a = mfma(lds_M[m][8 + q], R4[2], C4a);
-            C4b = mfma(lds_M[m][12 + q], R4[3], C4b);
+            C4a = mfma(Y[0], R4[0], C4a);
+            C4b = mfma(Y[1], R4[1], C4b);
+            C4a = mfma(Y[2], R4[2], C4a);
+            C4b = mfma(Y[3], R4[3], C4b);
             const v4d C4 = C4a + C4b;
             if constexpr (PF) {
                 // outputs of the chunk's tokens: o_e = T qf_e + sum_{e' <= e} C_e' (kb_e' . qf_e)
@@ -727,14 +764,17 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                     }
                 }
             }
-            // T += C Kb: block b of S^T, token group r
+            // T += C Kb: block b of S^T, token group r; the keys of token group
+            // r + 1 are requested before the products of group r
             {
-                const double(*kb)[KP] = KDA ? (const double(*)[KP])lds_kb : (const double(*)[KP])lds_kf;
-                const int colm = 4 * (m & 3) + (m >> 2);  // column of block b held by result row m
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+                for (int r = 0; r < 4; ++r) {
+                    const int cur = r & 1;
+                    if (r + 1 < 4) load_kb(r + 1, kv[cur ^ 1]);
 #pragma unroll
-                    for (int b = 0; b < NB; ++b) T[b] = mfma(kb[4 * r + q][16 * b + colm], C4[r], T[b]);
+                    for (int b = 0; b < NB; ++b) T[b] = mfma(kv[cur][b], C4[r], T[b]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
         // back to S
