@@ -75,6 +75,18 @@ __device__ __forceinline__ void store_vec(float* p, const Vec<EPL>& v) {
 
 __device__ __forceinline__ bool finite(float x) { return __builtin_isfinite(x); }
 
+// A zero the compiler cannot see through: an index built from it is taken as
+// varying across lanes, so the load is a vector load.
+__device__ __forceinline__ int vgpr_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Stores values that are already binary16-representable when H16.
@@ -203,18 +215,20 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     uint4 tw[NLW];
     float sg_row;
 
-    // tokens already in the window (uniform: every branch below is scalar)
-    const int j = __builtin_amdgcn_readfirstlane(a.blob.fill[u]);
-    if (j >= W) {
-        if (cg < NLW) a.o[(size_t)u * D + my_row] = __builtin_nanf("");
-        if (wave == 0 && lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_WINDOW_OVERFLOW);
-        return;
-    }
+    // tokens already in the window (uniform: every branch below is scalar).
+    // Only the window's own entries need it: every other load is requested
+    // before the wait for it, so the count and those loads share one trip.  A
+    // full window (no flush since W tokens) runs as an empty one with no
+    // stores to the window and NaN outputs; there is no early return, which
+    // would let the compiler move the loads below the wait.
+    const int j_ld = a.blob.fill[u];
+    int j;
 
     if (wave != 0) {
 #pragma unroll
         for (int t = 0; t < NLW; ++t) tw[t] = tile[t * kWave + lane];
         sg_row = a.blob.sigma[(size_t)u * D + my_row];
+        j = __builtin_amdgcn_readfirstlane(j_ld);
     } else {
         const size_t kb0 = kvec * (size_t)W * D;  // element offsets of this unit's k and v entries
         const size_t vb0 = (size_t)u * W * D;
@@ -222,51 +236,30 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         float* bg = a.blob.buf_gate + (size_t)u * W * (KDA ? D : 1);
 
         // loads in the order they are consumed (vector loads return in order):
-        // the current token, the newest P buffered tokens (a ring refilled P
-        // tokens ahead of use; indices below 0 are clamped to entry 0 and not
-        // used), beta and the scalar gate of the whole window (NWB per lane,
-        // window <= 64 NWB), smoothing and compensators
+        // the current token, beta and the scalar gate of the whole window (NWB
+        // per lane, window <= 64 NWB), this wave's tile quarter, smoothing and
+        // compensators; then, once the count is in, the newest P buffered
+        // tokens (a ring refilled P tokens ahead of use)
         const Vec<EPL> qv = load_vec<EPL>(a.q + kvec * D + lane * EPL);
         Entry<EPL, GE> cur;
         cur.k = load_vec<EPL>(a.k + kvec * D + lane * EPL);
         cur.v = load_vec<EPL>(a.v + (size_t)u * D + lane * EPL);
-        cur.beta = a.beta[u];
+        // beta and the scalar gate through the vector path, in order with the
+        // token's other loads (a scalar load would be issued, and waited for,
+        // on its own)
+        const float bgv = (KDA || lane == 0 ? a.beta : a.gate)[u + vgpr_zero()];
+        cur.beta = lane_value(bgv, 0);
         if constexpr (KDA) {
             cur.g = load_vec<GE>(a.gate + (size_t)u * D + lane * EPL);
         } else {
-            cur.g.e[0] = a.gate[u];
+            cur.g.e[0] = lane_value(bgv, 1);
         }
-        // the window's entries through buffer resources: a constant per-lane
-        // offset and a scalar per-entry offset, no per-lane address arithmetic
-        constexpr int ESZ = H16 ? 2 : 4;
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            (char*)a.blob.buf_k + kb0 * ESZ, (short)0, W * D * ESZ, kBufferFlags);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (char*)a.blob.buf_v + vb0 * ESZ, (short)0, W * D * ESZ, kBufferFlags);
-        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-            bg, (short)0, KDA ? W * D * 4 : 4, kBufferFlags);
-        const int voff = lane * EPL * ESZ;
-        auto load_entry = [&](int i, RingEntry<EPL, GE, H16>& en) {
-            if constexpr (H16) {
-                en.k = buf_load_halves<EPL>(rk, voff, i * D * ESZ);
-                en.v = buf_load_halves<EPL>(rv, voff, i * D * ESZ);
-            } else {
-                en.k = buf_load_f32<EPL>(rk, voff, i * D * ESZ);
-                en.v = buf_load_f32<EPL>(rv, voff, i * D * ESZ);
-            }
-            if constexpr (KDA) en.g = buf_load_f32<GE>(rg, lane * EPL * 4, i * D * 4);
-        };
-        RingEntry<EPL, GE, H16> ring[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) load_entry(max(j - 1 - p, 0), ring[p]);
         WindowRegs<NWB> win;
 #pragma unroll
         for (int w = 0; w < NWB; ++w) {
             win.b[w] = bb[min(lane + w * kWave, W - 1)];
             win.a[w] = KDA ? 0.f : bg[min(lane + w * kWave, W - 1)];
         }
-        // this wave's tile quarter, smoothing and compensators come after the
-        // data the reverse pass needs first
 #pragma unroll
         for (int t = 0; t < NLW; ++t) tw[t] = tile[t * kWave + lane];
         sg_row = a.blob.sigma[(size_t)u * D + my_row];
@@ -276,6 +269,42 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < NCP; ++c)
             cvec[c] = load_vec<EPL>(a.blob.comp_vec + ((size_t)u * nc + min(c, max(nc - 1, 0))) * D + lane * EPL);
+
+        j = __builtin_amdgcn_readfirstlane(j_ld);
+        const bool over = j >= W;
+        const int jr = over ? 0 : j;  // entries replayed
+        // the window's entries through buffer resources: a constant per-lane
+        // offset and a scalar per-entry offset, no per-lane address arithmetic.
+        // Ring slots with no entry left (index below 0) load through a
+        // resource of zero size: out of range, the load returns zeros without
+        // a memory access.  So every slot is loaded unconditionally (the
+        // compiler's wait counts stay exact) and the unused loads cost no
+        // memory trip to wait for.
+        constexpr int ESZ = H16 ? 2 : 4;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (char*)a.blob.buf_k + kb0 * ESZ, (short)0, W * D * ESZ, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (char*)a.blob.buf_v + vb0 * ESZ, (short)0, W * D * ESZ, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            bg, (short)0, KDA ? W * D * 4 : 4, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rnone =
+            __builtin_amdgcn_make_buffer_rsrc((char*)a.blob.buf_k, (short)0, 0, kBufferFlags);
+        const int voff = lane * EPL * ESZ;
+        auto load_entry = [&](int i, RingEntry<EPL, GE, H16>& en) {
+            const bool live = i >= 0;  // uniform
+            const int ie = live ? i : 0;
+            if constexpr (H16) {
+                en.k = buf_load_halves<EPL>(live ? rk : rnone, voff, ie * D * ESZ);
+                en.v = buf_load_halves<EPL>(live ? rv : rnone, voff, ie * D * ESZ);
+            } else {
+                en.k = buf_load_f32<EPL>(live ? rk : rnone, voff, ie * D * ESZ);
+                en.v = buf_load_f32<EPL>(live ? rv : rnone, voff, ie * D * ESZ);
+            }
+            if constexpr (KDA) en.g = buf_load_f32<GE>(live ? rg : rnone, lane * EPL * 4, ie * D * 4);
+        };
+        RingEntry<EPL, GE, H16> ring[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) load_entry(jr - 1 - p, ring[p]);
 
         // check the current token and append it to the window buffer
         bool ok = finite(cur.beta);
@@ -291,8 +320,10 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
             }
             if (__any(sat) && lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_BUFFER_SATURATED);
         }
-        if (h % a.dm.group == 0) store_buf<EPL, H16>(a.blob.buf_k, kb0 + (size_t)j * D + lane * EPL, cur.k);
-        store_buf<EPL, H16>(a.blob.buf_v, vb0 + (size_t)j * D + lane * EPL, cur.v);
+        if (!over) {
+            if (h % a.dm.group == 0) store_buf<EPL, H16>(a.blob.buf_k, kb0 + (size_t)j * D + lane * EPL, cur.k);
+            store_buf<EPL, H16>(a.blob.buf_v, vb0 + (size_t)j * D + lane * EPL, cur.v);
+        }
         // beta and scalar gate of every buffered slot into LDS, then the ring's
         // first entries take theirs (uniform reads; later refills read ahead)
 #pragma unroll
@@ -302,13 +333,15 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int p = 0; p < P; ++p) ring[p].ba = lds_ba[max(j - 1 - p, 0)];
-        if constexpr (KDA) {
-            store_vec(bg + (size_t)j * D + lane * EPL, cur.g);
-        } else {
-            if (lane == 0) bg[j] = cur.g.e[0];
+        for (int p = 0; p < P; ++p) ring[p].ba = lds_ba[max(jr - 1 - p, 0)];
+        if (!over) {
+            if constexpr (KDA) {
+                store_vec(bg + (size_t)j * D + lane * EPL, cur.g);
+            } else {
+                if (lane == 0) bg[j] = cur.g.e[0];
+            }
+            if (lane == 0) bb[j] = cur.beta;
         }
-        if (lane == 0) bb[j] = cur.beta;
 
         // reverse pass over the window, newest token first.  With a scalar
         // gate the running gate product sc stays off the dependent chain:
@@ -344,21 +377,21 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
             if constexpr (H16) return unpack_halves<EPL>(ring[p].v);
             else return ring[p].v;
         };
-        // whole ring cycles, then the last partial one (no refills needed there)
+        // whole ring cycles, then the last partial one (no refills needed
+        // there)
         int s0 = 0;
-        for (; s0 + P <= j; s0 += P) {
+        for (; s0 + P <= jr; s0 += P) {
 #pragma unroll
             for (int p = 0; p < P; ++p) {
-                const int i = j - 1 - (s0 + p);
+                const int i = jr - 1 - (s0 + p);
                 step(ring_k(p), ring_v(p), ring[p].g, ring[p].ba.x, ring[p].ba.y);
-                const int ir = max(i - P, 0);
-                load_entry(ir, ring[p]);
-                ring[p].ba = lds_ba[ir];
+                load_entry(i - P, ring[p]);
+                ring[p].ba = lds_ba[max(i - P, 0)];
             }
         }
 #pragma unroll
         for (int p = 0; p < P; ++p)
-            if (s0 + p < j) step(ring_k(p), ring_v(p), ring[p].g, ring[p].ba.x, ring[p].ba.y);
+            if (s0 + p < jr) step(ring_k(p), ring_v(p), ring[p].g, ring[p].ba.x, ring[p].ba.y);
         if constexpr (!KDA)
             for (int e = 0; e < EPL; ++e) r.e[e] *= sc;
 
@@ -438,9 +471,13 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         else p = sum4(p);
         if (t == cg) mine = p;
     }
+    const bool over = j >= W;
     if (cg < NLW)
-        a.o[(size_t)u * D + my_row] = __builtin_fmaf(sg_row, mine, lds_add[my_row]);
-    if (wave == 0 && lane == 0) a.blob.fill[u] = j + 1;
+        a.o[(size_t)u * D + my_row] = over ? __builtin_nanf("") : __builtin_fmaf(sg_row, mine, lds_add[my_row]);
+    if (wave == 0 && lane == 0) {
+        if (over) atomicOr(a.blob.status, (uint32_t)LQ_DEV_WINDOW_OVERFLOW);
+        else a.blob.fill[u] = j + 1;
+    }
 }
 
 template <int D, bool KDA>
