@@ -83,6 +83,22 @@ __device__ __forceinline__ int vgpr_zero() {
     return z;
 }
 
+// Unit of a workgroup.  The dispatcher hands workgroup b to XCD b % 8, and
+// each XCD has its own L2.  With grouped heads (G value heads per key head)
+// the G units that read the same key vectors (the buffered k and the token's
+// q, k) are given workgroups b, b + 8, ..., on one XCD and next to each other
+// in dispatch order, so the shared keys come from that XCD's L2 after the
+// first read.  Needs the unit count to be a multiple of 8 G; otherwise
+// workgroup b runs unit b.
+__device__ __forceinline__ int unit_of_block(int b, const Dims& dm) {
+    constexpr int kXcds = 8;
+    const int G = dm.group;
+    if (G <= 1 || dm.n_units % (kXcds * G) != 0) return b;
+    const int slot = b / kXcds;
+    const int kvec = (slot / G) * kXcds + b % kXcds;
+    return kvec * G + slot % G;
+}
+
 __device__ __forceinline__ float lane_value(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
@@ -196,8 +212,8 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     __shared__ float lds_add[D];     // buffered-token and compensator terms of o
     __shared__ float2 lds_ba[256];   // wavefront 0: beta and scalar gate of each window slot
 
-    const int u = blockIdx.x;
-    if (u >= a.dm.n_units) return;
+    if ((int)blockIdx.x >= a.dm.n_units) return;
+    const int u = unit_of_block(blockIdx.x, a.dm);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = lane_id();
     const int W = a.dm.window;
@@ -487,8 +503,8 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
     constexpr int ROWS = D / 4;       // rows per wave (four waves per unit)
     constexpr int NP = ROWS / RPP;    // passes
 
-    const int u = blockIdx.x;
-    if (u >= a.dm.n_units) return;
+    if ((int)blockIdx.x >= a.dm.n_units) return;
+    const int u = unit_of_block(blockIdx.x, a.dm);
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int cg = lane % LPR;

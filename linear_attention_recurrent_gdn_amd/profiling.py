@@ -22,9 +22,12 @@ Three commands:
 
   hbm
       Practical memory bandwidth of this device for plain streaming kernels:
-      a 1 GiB device-to-device copy (read + write) and a 1 GiB read (sum),
-      each timed with HIP events over repeated launches, and the same read
-      over 64 MiB (a working set that stays in the 256 MB last-level cache).
+      the stream_read yardstick (probe/stream_read.hip: 16-byte loads,
+      grid-stride, nothing else) over the decode launches' own byte counts
+      (56.4 MB, 379 MB, 506 MB and 902 MB per launch for gdn_decode,
+      hybrid_stack, kda_decode and gdn_serving) and 4 GiB, then torch's 1 GiB
+      device-to-device copy (read + write) and read (sum) and the same over
+      64 MiB; every figure timed with HIP events over repeated launches.
 """
 from __future__ import annotations
 
@@ -94,11 +97,24 @@ def run_window(workload: str, fmt: str = "int8", buffer: str = "fp32") -> None:
         sys.exit(1)
 
 
+STREAM_BYTES = (56397824, 378830848, 505602048, 902365184, 4 << 30)
+
+
 def hbm() -> dict:
+    import subprocess
+
+    from linear_attention_recurrent_gdn_amd import _build
+
+    if not os.path.exists(_build.PROBE):
+        raise SystemExit(f"{_build.PROBE} is missing: build it first (python -m linear_attention_recurrent_gdn_amd._build)")
+    r = subprocess.run([_build.PROBE, *map(str, STREAM_BYTES)], capture_output=True, text=True)
+    sys.stdout.write(r.stdout)
+    if r.returncode != 0:
+        raise SystemExit(f"stream_read failed: {r.stderr.strip()}")
+    out = {"stream_read": [json.loads(l) for l in r.stdout.splitlines() if l.startswith("{")]}
     import torch
 
     dev = torch.device("cuda", 0)
-    out = {}
     for label, nbytes in (("1GiB", 1 << 30), ("64MiB", 64 << 20)):
         x = torch.ones(nbytes // 4, device=dev)
         y = torch.empty_like(x)
@@ -211,7 +227,8 @@ def main(argv=None):
     b.add_argument("--write", required=True)
     b.add_argument("--out", required=True)
     b.add_argument("--command", default="")
-    sub.add_parser("hbm")
+    h = sub.add_parser("hbm")
+    h.add_argument("--out", default=None, help="also write a text summary here")
     c = sub.add_parser("stats")
     c.add_argument("--csv", required=True)
     c.add_argument("--command", default="")
@@ -220,7 +237,16 @@ def main(argv=None):
     if args.cmd == "window":
         run_window(args.workload, args.format, args.buffer)
     elif args.cmd == "hbm":
-        hbm()
+        res = hbm()
+        if args.out:
+            lines = ["# streaming bandwidth of this device (plain kernels, HIP events)",
+                     "# command: python -m linear_attention_recurrent_gdn_amd.profiling hbm --out " + args.out,
+                     "#", "# stream_read (probe/stream_read.hip): bytes read per launch, grid, mean us, TB/s"]
+            for r in res["stream_read"]:
+                lines.append(f"  {r['bytes']:>12d} {r['grid']:6d} {r['us']:10.2f} {r['TBps']:7.3f}")
+            lines.append("# torch: " + ", ".join(f"{k} {v}" for k, v in res.items() if k != "stream_read"))
+            with open(args.out, "w") as f:
+                f.write("\n".join(lines) + "\n")
     elif args.cmd == "traffic":
         print(json.dumps(traffic(args.workload, args.fetch, args.write, args.out, args.command), indent=1))
     else:

@@ -71,6 +71,12 @@ CASES = {
     "gqa_d64_h16_e4m3": (small("gdn_decode", name="gqa_d64_h16_e4m3", n_seq=2, n_v_heads=4, n_k_heads=2, d=64,
                                prefill=40, decode=70, window=32, n_comp=3, code_format="e4m3",
                                buffer_format="fp16"), dict(dequant_every=23)),
+    # grouped heads with a unit count that is a multiple of 8 G: the units that
+    # share a key head run in workgroups b, b + 8, ... (one XCD each)
+    "gqa4_xcd": (small("gdn_decode", name="gqa4_xcd", n_seq=2, n_v_heads=16, n_k_heads=4, d=64,
+                       prefill=24, decode=40, window=16, n_comp=2), dict(dequant_every=17)),
+    "kda_gqa_xcd": (small("kda_decode", name="kda_gqa_xcd", n_seq=2, n_v_heads=8, n_k_heads=4,
+                          prefill=24, decode=40, window=16, n_comp=3), dict(dequant_every=19)),
     # zero start state (no prefill) with the channel gate at d=128
     "kda_zero_start": (small("kda_decode", name="kda_zero_start", n_seq=1, n_v_heads=2,
                              n_k_heads=2, prefill=0, decode=20, window=8, n_comp=4), dict()),
@@ -163,7 +169,9 @@ def test_forced_flush_of_empty_window_is_a_no_op():
 def test_fp32_state_kernel_matches_oracle(gate, d):
     # the FP32-state comparison kernel against the oracle's plain recurrence
     base = "gdn_decode" if gate == "scalar" else "kda_decode"
-    wl = small(base, name=f"fp32_{gate}_{d}", n_seq=3, n_v_heads=4, n_k_heads=2, d=d, prefill=0,
+    # four sequences: 16 units of two heads per key head, so the workgroups
+    # take the XCD-grouped unit order
+    wl = small(base, name=f"fp32_{gate}_{d}", n_seq=4, n_v_heads=4, n_k_heads=2, d=d, prefill=0,
                outlier_rows=0, outlier_cols=0)
     cfg = _cfg(wl)
     U = wl.n_units
