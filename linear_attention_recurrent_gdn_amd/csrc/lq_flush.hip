@@ -324,8 +324,10 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     constexpr int CPL = 2 * D / kWave;  // selection candidates per lane
     constexpr bool PF = MODE == kModePrefill;
 
-    __shared__ double lds_kf[EB][KP];                       // forward-scaled keys of the chunk
-    __shared__ double lds_kb[KDA ? EB : 1][KDA ? KP : 1];  // back-scaled keys (channel gate)
+    // keys of the chunk: forward-scaled (kf), back-scaled (kb, channel gate);
+    // the keys the update of T reads are double-buffered by chunk parity
+    __shared__ double lds_kf[KDA ? 1 : 2][EB][KP];
+    __shared__ double lds_kb[KDA ? 2 : 1][KDA ? EB : 1][KDA ? KP : 1];
     __shared__ float lds_v[EB][D];                          // values as fetched
     __shared__ float lds_kraw[KDA ? EB : 1][KDA ? D : 1];  // channel gate: keys as fetched
     __shared__ float lds_graw[KDA ? EB : 1][KDA ? D : 1];  // channel gate: gates as fetched
@@ -440,21 +442,33 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 for (int r = 0; r < 4; ++r) T[b][r] = sgr * (double)cv[r] * (double)pick4(s4, r);
             }
             // compensator lines: a row slot adds its line to the four lanes of
-            // that row, a column slot adds one value per row; every load is
-            // issued before any is used
+            // that row, a column slot adds one value per row.  The unit's lines
+            // (at most 16 d floats) go to LDS, into the partial-gram space that
+            // the replay only uses later, in the same trip as the slot indices:
+            // no load waits for another
             if (nc > 0) {
                 const int* ci = a.blob.comp_idx + (size_t)u * nc;
                 const float* cv = a.blob.comp_vec + (size_t)u * nc * D;
+                float* lds_cv = reinterpret_cast<float*>(&lds_gram[0][0][0]);
+                static_assert(sizeof(lds_gram) >= 16 * D * sizeof(float) && NT * 4 >= 16 * D, "room for 16 lines");
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(cv + min(4 * tid, nc * D - 4)),
+                    (void __attribute__((address_space(3)))*)(lds_cv + 4 * kWave * wave), 16, 0, 0);
+                // the slot indices in one vector load (lane c holds slot c), not
+                // one scalar load and wait per slot
+                const int cil = ci[min(lane, nc - 1)];
                 int my_slot = -1;  // the row slot holding this lane's row, if any
                 for (int c = 0; c < nc; ++c)
-                    if (ci[c] == n) my_slot = c;
+                    if (__builtin_amdgcn_readlane(cil, c) == n) my_slot = c;
+                __builtin_amdgcn_s_waitcnt(0);  // this thread's lines are in LDS
+                __syncthreads();
                 float4 rowv[NB];
-                const float* rv = cv + (size_t)max(my_slot, 0) * D;
+                const float* rv = lds_cv + max(my_slot, 0) * D;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) rowv[b] = *reinterpret_cast<const float4*>(rv + 16 * b + 4 * q);
                 float colv[16];
 #pragma unroll
-                for (int c = 0; c < 16; ++c) colv[c] = cv[(size_t)min(c, nc - 1) * D + n];
+                for (int c = 0; c < 16; ++c) colv[c] = lds_cv[min(c, nc - 1) * D + n];
                 if (my_slot >= 0) {
 #pragma unroll
                     for (int b = 0; b < NB; ++b)
@@ -464,37 +478,68 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
                     if (c >= nc) break;
-                    const int col = ci[c] - D;
+                    const int col = __builtin_amdgcn_readlane(cil, c) - D;
                     if (col >= 0) {
+                        // the column's block and register are uniform (a scalar
+                        // branch picks them); its quad is the lane mask
+                        const int cb = col >> 4, cr = col & 3;
+                        const bool mine = q == ((col >> 2) & 3);
 #pragma unroll
                         for (int b = 0; b < NB; ++b)
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
-                                if (16 * b + 4 * q + r == col) T[b][r] += (double)colv[c];
+                                if (b == cb && r == cr && mine) T[b][r] += (double)colv[c];
                     }
                 }
             }
         }
 
         // ---------------- B: forward replay of the buffered tokens (or the prompt), 16 per chunk
-        for (int i0 = 0; i0 < n_replay; i0 += EB) {
+        //
+        // Software-pipelined over chunks.  Chunk c+1 is staged while chunk c
+        // finishes, so the products the next chunk needs first (its partial
+        // grams) enter the matrix pipe ahead of chunk c's update of T, and the
+        // reduction to N runs while that update executes:
+        //   gemm_a(c) with M(c) | R(c), C(c) | barrier | stage(c+1) | grams(c+1)
+        //   | T += C Kb for chunk c, with the gram write, a barrier, the
+        //     reduction to N(c+1) and a barrier between its four token groups
+        // The keys T += C Kb reads (kb, which is kf with a scalar gate) are
+        // double-buffered by chunk parity; everything else a chunk stages is
+        // read before the barrier that precedes the next stage.
+        const int n_chunks = (n_replay + EB - 1) / EB;
+        auto kf_of = [&](int par) -> const double(*)[KP] {
+            return (const double(*)[KP])lds_kf[KDA ? 0 : par];
+        };
+        auto kb_of = [&](int par) -> const double(*)[KP] {
+            if constexpr (KDA) return (const double(*)[KP])lds_kb[par];
+            else return (const double(*)[KP])lds_kf[par];
+        };
+        // stage chunk c from the fetched registers into LDS, then request chunk
+        // c + 1; ends with a barrier after which the chunk's data is readable
+        auto stage = [&](int c) {
+            // the thread index through an opaque copy: the address arithmetic
+            // below is redone at each call instead of being kept live across the
+            // replay (registers are short)
+            int tid = threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            const int i0 = c * EB;
             const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
-            const int qb = (i0 / EB) & 1;  // chunk parity: query buffer (prefill), running gate (channel)
+            const int qb = c & 1;  // chunk parity: keys, queries (prefill), running gate (channel)
             if constexpr (PF) __builtin_amdgcn_s_waitcnt(0);  // this chunk's queries are in LDS
-            __syncthreads();  // the previous chunk is done with LDS
             {
                 const int x = 4 * tid;
-                const int e = x / D, c = x % D;
+                const int e = x / D, col = x % D;
                 const bool live = e < ne;  // padding tokens: zero key, zero beta
-                *reinterpret_cast<float4*>(&lds_v[e][c]) = pf.v;
+                *reinterpret_cast<float4*>(&lds_v[e][col]) = pf.v;
                 if constexpr (KDA) {
-                    *reinterpret_cast<float4*>(&lds_kraw[e][c]) = pf.k;
-                    *reinterpret_cast<float4*>(&lds_graw[e][c]) = pf.g;
+                    *reinterpret_cast<float4*>(&lds_kraw[e][col]) = pf.k;
+                    *reinterpret_cast<float4*>(&lds_graw[e][col]) = pf.g;
                 } else {
-                    lds_kf[e][c + 0] = live ? (double)pf.k.x : 0.0;
-                    lds_kf[e][c + 1] = live ? (double)pf.k.y : 0.0;
-                    lds_kf[e][c + 2] = live ? (double)pf.k.z : 0.0;
-                    lds_kf[e][c + 3] = live ? (double)pf.k.w : 0.0;
+                    double* kd = &lds_kf[qb][e][col];
+                    kd[0] = live ? (double)pf.k.x : 0.0;
+                    kd[1] = live ? (double)pf.k.y : 0.0;
+                    kd[2] = live ? (double)pf.k.z : 0.0;
+                    kd[3] = live ? (double)pf.k.w : 0.0;
                 }
                 if (tid < EB) {
                     lds_b[tid] = tid < ne ? pf.b : 0.f;
@@ -528,7 +573,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 }
             }
             __syncthreads();
-            if (i0 + EB < n_replay) {  // in flight during this chunk
+            if (i0 + EB < n_replay) {  // in flight until the next stage
                 pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, ts, i0 + EB, n_replay, tid);
                 if constexpr (PF) fetch_q_to_lds<D>(bq, ts.k, i0 + EB, n_replay, tid, &lds_qraw[qb ^ 1][0][0]);
             }
@@ -538,50 +583,117 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 // queries) scaled by the running gate product, both ways
                 static_assert(NT == 4 * D, "four threads per column");
                 {
-                    const int c = tid % D, seg = tid / D;
+                    const int col = tid % D, seg = tid / D;
                     double pre = 1.0, P = 1.0;  // product before this thread's tokens, whole chunk
 #pragma unroll
                     for (int e = 0; e < EB; ++e) {
-                        const double al = e < ne ? fmax((double)lds_graw[e][c], kMinGate) : 1.0;
+                        const double al = e < ne ? fmax((double)lds_graw[e][col], kMinGate) : 1.0;
                         if (e < 4 * seg) pre *= al;
                         P *= al;
                     }
                     // read this chunk's G, write the next chunk's: no thread of
                     // the column overwrites what another still has to read
-                    const double G0 = lds_G[qb][c];
+                    const double G0 = lds_G[qb][col];
                     const bool fold = G0 * P < kRescaleBelow;  // the same in the column's four threads
                     if (seg == 0) {
-                        lds_fold[c] = fold ? G0 : 1.0;
+                        lds_fold[col] = fold ? G0 : 1.0;
                         if (fold) lds_anyfold = 1;  // every writer stores the same value
                     }
                     double G = (fold ? 1.0 : G0) * pre;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int e = 4 * seg + i;
-                        double kf = 0.0, kbk = 0.0, qf = 0.0;
+                        double kfv = 0.0, kbv = 0.0, qfv = 0.0;
                         if (e < ne) {
-                            G *= fmax((double)lds_graw[e][c], kMinGate);
-                            const double kc = (double)lds_kraw[e][c];
-                            kf = G * kc;
-                            kbk = kc / G;
-                            if constexpr (PF) qf = G * (double)lds_qraw[qb][e][c];
+                            G *= fmax((double)lds_graw[e][col], kMinGate);
+                            const double kc = (double)lds_kraw[e][col];
+                            kfv = G * kc;
+                            kbv = kc / G;
+                            if constexpr (PF) qfv = G * (double)lds_qraw[qb][e][col];
                         }
-                        lds_kf[e][c] = kf;
-                        lds_kb[e][c] = kbk;
-                        if constexpr (PF) lds_qf[e][c] = qf;
+                        lds_kf[0][e][col] = kfv;
+                        lds_kb[qb][e][col] = kbv;
+                        if constexpr (PF) lds_qf[e][col] = qfv;
                     }
-                    if (seg == 3) lds_G[qb ^ 1][c] = (fold ? 1.0 : G0) * P;
+                    if (seg == 3) lds_G[qb ^ 1][col] = (fold ? 1.0 : G0) * P;
                 }
             }
             if constexpr (PF && !KDA) {
                 // queries scaled by the running gate: qf_e = g_e q_e
                 const int x = 4 * tid;
-                const int e = x / D, c = x % D;
+                const int e = x / D, col = x % D;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) lds_qf[e][c + i] = lds_gq[e] * (double)lds_qraw[qb][e][c + i];
+                for (int i = 0; i < 4; ++i) lds_qf[e][col + i] = lds_gq[e] * (double)lds_qraw[qb][e][col + i];
             }
             if constexpr (KDA || PF) __syncthreads();
-            // folds into T
+        };
+        // partial L of chunk c over this wavefront's 16-column slice: lane (q, m),
+        // register r -> sum_k kf[4r + q][k] kb[m][k]; prefill also qf . kb
+        // (one accumulator each: the matrix pipe forwards a dependent accumulator)
+        v4d gr, grq;
+        auto gram_issue = [&](int c) {
+            const double(*kf)[KP] = kf_of(c & 1);
+            const double(*kb)[KP] = kb_of(c & 1);
+            gr = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int k = 16 * wave + 4 * t + q;
+                gr = mfma(kf[m][k], kb[m][k], gr);
+            }
+            if constexpr (PF) {
+                // partial qf . kb: lane (q, m), register r -> qf[4r + q] . kb[m]
+                grq = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int k = 16 * wave + 4 * t + q;
+                    grq = mfma(lds_qf[m][k], kb[m][k], grq);
+                }
+            }
+        };
+        auto gram_write = [&]() {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lds_gram[wave][4 * r + q][m] = gr[r];
+            if constexpr (PF) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) lds_gramq[wave][4 * r + q][m] = grq[r];
+            }
+        };
+        // N = Diag(beta) L (strictly lower), and for the prefill P, each
+        // element summed over the slices in a fixed order, shared out over the
+        // whole block
+        auto n_reduce = [&]() {
+            constexpr int NEL = (PF ? 2 : 1) * EB * EB;
+#pragma unroll
+            for (int t = 0; t < (NEL + NT - 1) / NT; ++t) {
+                const int idx = tid + NT * t;
+                if (NEL % NT != 0 && idx >= NEL) break;
+                const int j = idx % (EB * EB);
+                const int e = j / EB, e2 = j % EB;
+                double sum = 0.0;
+                if (!PF || idx < EB * EB) {
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) sum += lds_gram[w][e][e2];
+                    lds_N[e][e2 & 3][e2 >> 2] = e2 < e ? (double)lds_b[e] * sum : 0.0;
+                } else if constexpr (PF) {
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) sum += lds_gramq[w][e][e2];
+                    lds_P[e][e2] = e2 <= e ? sum : 0.0;
+                }
+            }
+        };
+        if (n_chunks > 0) {
+            stage(0);
+            gram_issue(0);
+            gram_write();
+            __syncthreads();
+            n_reduce();
+            __syncthreads();
+        }
+        for (int c = 0; c < n_chunks; ++c) {
+            const int i0 = c * EB;
+            const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
+            const bool more = c + 1 < n_chunks;  // uniform
+            // folds into T (decided when the chunk was staged)
             if constexpr (KDA) {
                 if (lds_anyfold) {  // uniform, rare
 #pragma unroll
@@ -597,59 +709,6 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 }
                 gam = lds_gs[1];
             }
-            // partial L over this wavefront's 16-column slice: lane (q, m),
-            // register r -> sum_k kf[4r + q][k] kb[m][k]
-            {
-                const double(*kb)[KDA ? KP : KP] = KDA ? (const double(*)[KP])lds_kb : (const double(*)[KP])lds_kf;
-                v4d g4a = {0.0, 0.0, 0.0, 0.0}, g4b = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-                for (int t = 0; t < 4; t += 2) {
-                    const int k = 16 * wave + 4 * t + q;
-                    g4a = mfma(lds_kf[m][k], kb[m][k], g4a);
-                    g4b = mfma(lds_kf[m][k + 4], kb[m][k + 4], g4b);
-                }
-                const v4d g4 = g4a + g4b;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) lds_gram[wave][4 * r + q][m] = g4[r];
-                if constexpr (PF) {
-                    // partial qf . kb: lane (q, m), register r -> qf[4r + q] . kb[m]
-                    v4d h4a = {0.0, 0.0, 0.0, 0.0}, h4b = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-                    for (int t = 0; t < 4; t += 2) {
-                        const int k = 16 * wave + 4 * t + q;
-                        h4a = mfma(lds_qf[m][k], kb[m][k], h4a);
-                        h4b = mfma(lds_qf[m][k + 4], kb[m][k + 4], h4b);
-                    }
-                    const v4d h4 = h4a + h4b;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) lds_gramq[wave][4 * r + q][m] = h4[r];
-                }
-            }
-            __syncthreads();
-            // N = Diag(beta) L (strictly lower), and for the prefill P, each
-            // element summed over the slices in a fixed order, shared out over
-            // the whole block
-            {
-                constexpr int NEL = (PF ? 2 : 1) * EB * EB;
-#pragma unroll
-                for (int t = 0; t < (NEL + NT - 1) / NT; ++t) {
-                    const int idx = tid + NT * t;
-                    if (NEL % NT != 0 && idx >= NEL) break;
-                    const int j = idx % (EB * EB);
-                    const int e = j / EB, e2 = j % EB;
-                    double sum = 0.0;
-                    if (!PF || idx < EB * EB) {
-#pragma unroll
-                        for (int w = 0; w < NW; ++w) sum += lds_gram[w][e][e2];
-                        lds_N[e][e2 & 3][e2 >> 2] = e2 < e ? (double)lds_b[e] * sum : 0.0;
-                    } else if constexpr (PF) {
-#pragma unroll
-                        for (int w = 0; w < NW; ++w) sum += lds_gramq[w][e][e2];
-                        lds_P[e][e2] = e2 <= e ? sum : 0.0;
-                    }
-                }
-            }
-            __syncthreads();
             // every wavefront: A = T Kf^T (prefill: also Aq = T Qf^T, register r:
             // token 4r + q, row n) on the matrix pipe, and between its products
             // its own copy of Y = M^T = (I + N^T)^-1 on the vector ALU, by
@@ -665,6 +724,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             v4d A4;
             v4d Y;
             {
+                const double(*kf)[KP] = kf_of(c & 1);
                 constexpr int SPB = (EB - 2 + NB) / NB;  // substitution steps per key block
                 v4d acc[4];
 #pragma unroll
@@ -676,7 +736,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 double kc[2][4], qc[4];
                 auto load_keys = [&](int b, double* kd) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) kd[r] = lds_kf[m][16 * b + 4 * q + r];
+                    for (int r = 0; r < 4; ++r) kd[r] = kf[m][16 * b + 4 * q + r];
                 };
                 load_keys(0, kc[0]);
 #pragma unroll
@@ -725,15 +785,6 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                     A4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);  // register r: A[token 4r + q][row n]
                 }
             }
-            // keys of the update T += C Kb, token group 0 requested ahead
-            const double(*kb)[KP] = KDA ? (const double(*)[KP])lds_kb : (const double(*)[KP])lds_kf;
-            const int colm = 4 * (m & 3) + (m >> 2);  // column of block b held by result row m
-            double kv[2][NB];
-            auto load_kb = [&](int r, double* dst) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b) dst[b] = kb[4 * r + q][16 * b + colm];
-            };
-            load_kb(0, kv[0]);
             // R = (v' - A) Diag(beta): register r -> token 4r + q, row n
             v4d R4;
 #pragma unroll
@@ -749,33 +800,56 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             C4a = mfma(Y[2], R4[2], C4a);
             C4b = mfma(Y[3], R4[3], C4b);
             const v4d C4 = C4a + C4b;
+            // prefill outputs of the chunk's tokens: o_e = T qf_e + sum_{e' <= e} C_e' (kb_e' . qf_e)
+            const bool outs = PF && a.po != nullptr;
             if constexpr (PF) {
-                // outputs of the chunk's tokens: o_e = T qf_e + sum_{e' <= e} C_e' (kb_e' . qf_e)
-                if (a.po != nullptr) {
+                if (outs) {
                     Aq4 = mfma(lds_P[m][q], C4[0], Aq4);
                     Aq4 = mfma(lds_P[m][4 + q], C4[1], Aq4);
                     Aq4 = mfma(lds_P[m][8 + q], C4[2], Aq4);
                     Aq4 = mfma(lds_P[m][12 + q], C4[3], Aq4);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int e = 4 * r + q;
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int e = 4 * rr + q;
                         float* o0 = a.po + ((size_t)i0 * a.dm.n_units + u) * D;  // uniform
-                        if (e < ne) o0[(uint32_t)e * (uint32_t)a.dm.n_units * D + n] = (float)Aq4[r];
+                        if (e < ne) o0[(uint32_t)e * (uint32_t)a.dm.n_units * D + n] = (float)Aq4[rr];
                     }
                 }
             }
             // T += C Kb: block b of S^T, token group r; the keys of token group
-            // r + 1 are requested before the products of group r
-            {
+            // r + 1 are requested before the products of group r.  Between the
+            // groups (when `tasks`): chunk c+1's partial grams to LDS, a
+            // barrier, its N, a barrier
+            auto t_update = [&](bool tasks) {
+                const double(*kb)[KP] = kb_of(c & 1);
+                const int colm = 4 * (m & 3) + (m >> 2);  // column of block b held by result row m
+                double kv[2][NB];
+                auto load_kb = [&](int r, double* dst) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) dst[b] = kb[4 * r + q][16 * b + colm];
+                };
+                load_kb(0, kv[0]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int cur = r & 1;
                     if (r + 1 < 4) load_kb(r + 1, kv[cur ^ 1]);
 #pragma unroll
                     for (int b = 0; b < NB; ++b) T[b] = mfma(kv[cur][b], C4[r], T[b]);
+                    if (tasks) {
+                        if (r == 0) gram_write();
+                        if (r == 1) __syncthreads();
+                        if (r == 2) n_reduce();
+                        if (r == 3) __syncthreads();
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
+            };
+            if (more) {
+                __syncthreads();  // chunk c's staged data, keys aside, is read
+                stage(c + 1);
+                gram_issue(c + 1);
             }
+            t_update(more);
         }
         // back to S
         if constexpr (KDA) {
