@@ -292,23 +292,17 @@ __device__ __forceinline__ Stage<KDA> fetch_stage(const void* bk, const void* bv
     return st;
 }
 
-// The chunk's queries straight into LDS (no registers): thread t copies 16
-// bytes of token-major [16][D] fp32 to byte 16 t of dst; a wavefront's 64
-// copies land consecutively from its base (the LDS address of
-// global_load_lds_dwordx4 is M0 + 16 * lane).  Completion is counted by
-// vmcnt: wait for it, then a barrier, before reading dst.
+// The chunk's queries, four consecutive fp32 per thread of token-major
+// [16][D] (like the keys), fetched into registers a stage ahead.  (A copy
+// straight into LDS would make every barrier after it wait for the copy.)
 template <int D>
-__device__ __forceinline__ void fetch_q_to_lds(const float* bq, size_t stride, int i0, int n_replay, int tid,
-                                               float* dst) {
+__device__ __forceinline__ float4 fetch_q(const float* bq, size_t stride, int i0, int n_replay, int tid) {
     constexpr int EB = 16;
     const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
     const int x = 4 * tid;
     const uint32_t e = (uint32_t)min(x / D, ne - 1), c = (uint32_t)(x % D);
-    const int wave = tid / kWave;
     const float* q0 = bq + (size_t)i0 * stride;
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(q0 + (e * (uint32_t)stride + c)),
-        (void __attribute__((address_space(3)))*)(dst + 4 * kWave * wave), 16, 0, 0);
+    return *reinterpret_cast<const float4*>(q0 + (e * (uint32_t)stride + c));
 }
 
 }  // namespace
@@ -338,14 +332,17 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     __shared__ double lds_G[2][KDA ? D : 1];                // channel gate: running G per column (by chunk parity)
     __shared__ double lds_fold[KDA ? D : 1];                // channel gate: fold factor per column
     __shared__ int lds_anyfold;                             // channel gate: some column folded
-    __shared__ double lds_gram[NW][EB][EB];                 // partial kf . kb over column slices
+    // small [16][16] matrices padded to 17 columns: a column read across the
+    // 16 rows (a matrix-pipe operand) would otherwise hit one LDS bank
+    __shared__ double lds_gram[NW][EB][EB + 1];             // partial kf . kb over column slices
     __shared__ double lds_N[EB][4][4];                      // Diag(beta) L, [e2][q][r] = N[e2][4r + q]
+    __shared__ double lds_M[EB][EB + 1];                    // (I + N)^-1
     // prefill outputs: queries as fetched and scaled, qf . kb, its future part
-    __shared__ float lds_qraw[PF ? 2 : 1][PF ? EB : 1][PF ? D : 1];  // double buffer by chunk parity
+    __shared__ float lds_qraw[PF ? EB : 1][PF ? D : 1];
     __shared__ double lds_qf[PF ? EB : 1][PF ? KP : 1];
     __shared__ double lds_gq[PF ? EB : 1];                  // scalar gate: g_e
-    __shared__ double lds_gramq[PF ? NW : 1][PF ? EB : 1][PF ? EB : 1];
-    __shared__ double lds_P[PF ? EB : 1][PF ? EB : 1];      // (e' <= e) qf_e . kb_e'
+    __shared__ double lds_gramq[PF ? NW : 1][PF ? EB : 1][PF ? EB + 1 : 1];
+    __shared__ double lds_P[PF ? EB : 1][PF ? EB + 1 : 1];  // (e' <= e) qf_e . kb_e'
     __shared__ double lds_score[2 * D];
     __shared__ double lds_part[NW][D];
     __shared__ float lds_smooth[D];
@@ -403,9 +400,10 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             if (tid < D) lds_G[0][tid] = 1.0;
         }
         Stage<KDA> pf{};
+        float4 pfq = make_float4(0.f, 0.f, 0.f, 0.f);  // prefill: the staged chunk's queries
         if (n_replay > 0) {
             pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, ts, 0, n_replay, tid);
-            if constexpr (PF) fetch_q_to_lds<D>(bq, ts.k, 0, n_replay, tid, &lds_qraw[0][0][0]);
+            if constexpr (PF) pfq = fetch_q<D>(bq, ts.k, 0, n_replay, tid);
         }
 
         // ---------------- A: the window-start state; T[b][r] = S[n][16b + 4q + r]
@@ -516,7 +514,13 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
         };
         // stage chunk c from the fetched registers into LDS, then request chunk
         // c + 1; ends with a barrier after which the chunk's data is readable
-        auto stage = [&](int c) {
+        // (with live false: only the caller's work and a barrier)
+        auto stage = [&](int c, bool live, auto&& mid) {
+            if (!live) {
+                mid();
+                __syncthreads();
+                return;
+            }
             // the thread index through an opaque copy: the address arithmetic
             // below is redone at each call instead of being kept live across the
             // replay (registers are short)
@@ -525,12 +529,12 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             const int i0 = c * EB;
             const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
             const int qb = c & 1;  // chunk parity: keys, queries (prefill), running gate (channel)
-            if constexpr (PF) __builtin_amdgcn_s_waitcnt(0);  // this chunk's queries are in LDS
             {
                 const int x = 4 * tid;
                 const int e = x / D, col = x % D;
                 const bool live = e < ne;  // padding tokens: zero key, zero beta
                 *reinterpret_cast<float4*>(&lds_v[e][col]) = pf.v;
+                if constexpr (PF) *reinterpret_cast<float4*>(&lds_qraw[e][col]) = pfq;
                 if constexpr (KDA) {
                     *reinterpret_cast<float4*>(&lds_kraw[e][col]) = pf.k;
                     *reinterpret_cast<float4*>(&lds_graw[e][col]) = pf.g;
@@ -572,11 +576,8 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                     }
                 }
             }
+            mid();  // work of the caller that overlaps the stage (no LDS it writes)
             __syncthreads();
-            if (i0 + EB < n_replay) {  // in flight until the next stage
-                pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, ts, i0 + EB, n_replay, tid);
-                if constexpr (PF) fetch_q_to_lds<D>(bq, ts.k, i0 + EB, n_replay, tid, &lds_qraw[qb ^ 1][0][0]);
-            }
             if constexpr (KDA) {
                 // four threads per column, four tokens each: fold G into T if the
                 // chunk could take it below the threshold, then the keys (and
@@ -609,7 +610,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                             const double kc = (double)lds_kraw[e][col];
                             kfv = G * kc;
                             kbv = kc / G;
-                            if constexpr (PF) qfv = G * (double)lds_qraw[qb][e][col];
+                            if constexpr (PF) qfv = G * (double)lds_qraw[e][col];
                         }
                         lds_kf[0][e][col] = kfv;
                         lds_kb[qb][e][col] = kbv;
@@ -623,7 +624,12 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 const int x = 4 * tid;
                 const int e = x / D, col = x % D;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) lds_qf[e][col + i] = lds_gq[e] * (double)lds_qraw[qb][e][col + i];
+                for (int i = 0; i < 4; ++i) lds_qf[e][col + i] = lds_gq[e] * (double)lds_qraw[e][col + i];
+            }
+            // the next chunk, in flight until the next stage
+            if (i0 + EB < n_replay) {
+                pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, ts, i0 + EB, n_replay, tid);
+                if constexpr (PF) pfq = fetch_q<D>(bq, ts.k, i0 + EB, n_replay, tid);
             }
             if constexpr (KDA || PF) __syncthreads();
         };
@@ -682,7 +688,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             }
         };
         if (n_chunks > 0) {
-            stage(0);
+            stage(0, true, [] {});
             gram_issue(0);
             gram_write();
             __syncthreads();
@@ -710,51 +716,31 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 gam = lds_gs[1];
             }
             // every wavefront: A = T Kf^T (prefill: also Aq = T Qf^T, register r:
-            // token 4r + q, row n) on the matrix pipe, and between its products
-            // its own copy of Y = M^T = (I + N^T)^-1 on the vector ALU, by
-            // right-looking back substitution: lane (q, m), register r holds
-            // Y[4r + q][m].  Row e2 is final once the rows below it have been
-            // folded in; it is then broadcast to the four row groups and folded
-            // into every row above it (N[e2][e] is zero for e >= e2, so no
-            // masking).  Y[r] in lane (q, m) is M[m][4r + q]: the left operand of
-            // C = M R as the matrix pipe takes it.  The keys of block b + 1 are
-            // requested before the products of block b; the scheduling barriers
-            // keep that order.
+            // token 4r + q, row n) on the matrix pipe.  The keys of block b + 1
+            // are requested before the products of block b; the scheduling
+            // barriers keep that order.
             v4d Aq4 = {0.0, 0.0, 0.0, 0.0};
             v4d A4;
-            v4d Y;
             {
                 const double(*kf)[KP] = kf_of(c & 1);
-                constexpr int SPB = (EB - 2 + NB) / NB;  // substitution steps per key block
                 v4d acc[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] = v4d{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Y[r] = (4 * r + q == m) ? 1.0 : 0.0;
-                // prefill: the queries of block b are requested with the keys of
-                // block b + 1 (one buffer, the products on keys go first)
                 double kc[2][4], qc[4];
                 auto load_keys = [&](int b, double* kd) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) kd[r] = kf[m][16 * b + 4 * q + r];
                 };
-                load_keys(0, kc[0]);
+                // (prefill, short of registers: the keys of block b with its queries)
+                if constexpr (!PF) load_keys(0, kc[0]);
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    const int cur = b & 1;
-                    if (b + 1 < NB) load_keys(b + 1, kc[cur ^ 1]);
+                    const int cur = PF ? 0 : b & 1;
+                    if (PF) load_keys(b, kc[0]);
+                    else if (b + 1 < NB) load_keys(b + 1, kc[cur ^ 1]);
                     if constexpr (PF) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) qc[r] = lds_qf[m][16 * b + 4 * q + r];
-                    }
-                    double nr[SPB][4];
-#pragma unroll
-                    for (int s = 0; s < SPB; ++s) {
-                        const int e2 = EB - 1 - (SPB * b + s);
-                        if (e2 >= 1) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) nr[s][r] = lds_N[e2][q][r];
-                        }
                     }
                     if constexpr (PF) {
 #pragma unroll
@@ -764,15 +750,6 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                     } else {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) acc[r] = mfma(kc[cur][r], T[b][r], acc[r]);
-                    }
-#pragma unroll
-                    for (int s = 0; s < SPB; ++s) {
-                        const int e2 = EB - 1 - (SPB * b + s);
-                        if (e2 >= 1) {
-                            const double y = group_bcast(Y[e2 >> 2], e2 & 3);
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) Y[r] = __builtin_fma(-nr[s][r], y, Y[r]);
-                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -793,12 +770,47 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 const double vp = KDA ? (double)lds_v[e][n] : (double)lds_v[e][n] * lds_ig[e];
                 R4[r] = (double)lds_b[e] * (vp - A4[r]);
             }
+            // M = (I + N)^-1 by right-looking back substitution on one wavefront
+            // (the last: the first computes the scalar gates), while the next
+            // chunk is staged, into LDS.  As vector ALU work beside the products
+            // it slowed the matrix pipe.  Lane (q, m), register r holds
+            // Y[4r + q][m] of Y = M^T; row e2 is final once the rows below it
+            // have been folded in; it is then broadcast to the four row groups
+            // and folded into every row above it (N[e2][e] is zero for e >= e2,
+            // so no masking).  Y[4r + q][m] = M[m][4r + q].  Each step's row of
+            // N is requested two steps ahead.
+            auto solve_m = [&]() {
+                if (wave != NW - 1) return;
+                v4d Y;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Y[r] = (4 * r + q == m) ? 1.0 : 0.0;
+                constexpr int PD = 3;  // prefetch depth, steps
+                double nr[PD][4];
+#pragma unroll
+                for (int d = 0; d < PD - 1; ++d)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) nr[(EB - 1 - d) % PD][r] = lds_N[EB - 1 - d][q][r];
+#pragma unroll
+                for (int e2 = EB - 1; e2 >= 1; --e2) {
+                    if (e2 - (PD - 1) >= 1) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) nr[(e2 - (PD - 1)) % PD][r] = lds_N[e2 - (PD - 1)][q][r];
+                    }
+                    const double y = group_bcast(Y[e2 >> 2], e2 & 3);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Y[r] = __builtin_fma(-nr[e2 % PD][r], y, Y[r]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) lds_M[m][4 * r + q] = Y[r];
+            };
+            if (more) __syncthreads();  // chunk c's staged data, keys aside, is read
+            stage(c + 1, more, solve_m);
             // C = M R (per row): register r -> token 4r + q, row n
             v4d C4a = {0.0, 0.0, 0.0, 0.0}, C4b = {0.0, 0.0, 0.0, 0.0};
-            C4a = mfma(Y[0], R4[0], C4a);
-            C4b = mfma(Y[1], R4[1], C4b);
-            C4a = mfma(Y[2], R4[2], C4a);
-            C4b = mfma(Y[3], R4[3], C4b);
+            C4a = mfma(lds_M[m][q], R4[0], C4a);
+            C4b = mfma(lds_M[m][4 + q], R4[1], C4b);
+            C4a = mfma(lds_M[m][8 + q], R4[2], C4a);
+            C4b = mfma(lds_M[m][12 + q], R4[3], C4b);
             const v4d C4 = C4a + C4b;
             // prefill outputs of the chunk's tokens: o_e = T qf_e + sum_{e' <= e} C_e' (kb_e' . qf_e)
             const bool outs = PF && a.po != nullptr;
@@ -844,11 +856,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                     __builtin_amdgcn_sched_barrier(0);
                 }
             };
-            if (more) {
-                __syncthreads();  // chunk c's staged data, keys aside, is read
-                stage(c + 1);
-                gram_issue(c + 1);
-            }
+            if (more) gram_issue(c + 1);
             t_update(more);
         }
         // back to S
@@ -874,6 +882,16 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             continue;
         }
 
+        {
+        // the lane's coordinates again through an opaque copy of the thread
+        // index: recomputed here rather than kept live across the replay
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int wave = tid / kWave;
+        const int lane = tid % kWave;
+        const int q = lane >> 4;
+        const int m = lane & 15;
+        const int n = 16 * wave + m;
         // ---------------- C1: line scores
         {
             double rs = 0.0;
@@ -1031,6 +1049,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 }
                 *reinterpret_cast<uint32_t*>(a.blob.codes + ((size_t)u * D + n) * D + 16 * b + 4 * q) = packed;
             }
+        }
         }
         if (tid == 0) {
             a.blob.fill[u] = 0;
