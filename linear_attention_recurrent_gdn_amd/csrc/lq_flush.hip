@@ -53,6 +53,7 @@
 // combine the wavefronts through LDS in a fixed order, so results are
 // deterministic.
 
+#include <atomic>
 #include "lq_internal.h"
 
 namespace lq {
@@ -1060,55 +1061,122 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 }
 
 // Units whose window is due, in ascending order, into the blob's work list.
+// A pass covers 16 blocks of 1,024 units: every thread requests all of its
+// fill counts and sequence flags before it uses any (one memory trip per pass,
+// not one per block), the per-wavefront counts of the pass are scanned once,
+// and each due unit is written at its offset.
 __global__ __launch_bounds__(1024) void due_scan_kernel(MatArgs a) {
-    __shared__ int wave_cnt[16];
+    constexpr int P = 16;      // 1,024-unit blocks per pass
+    constexpr int NWV = 16;    // wavefronts
+    __shared__ int cnt[P * NWV];  // due units per (block, wavefront), then their offsets
     __shared__ int base;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = lane_id();
+    const int n = a.dm.n_units;
     if (tid == 0) base = 0;
-    __syncthreads();
-    for (int c0 = 0; c0 < a.dm.n_units; c0 += 1024) {
-        const int u = c0 + tid;
-        bool due = false;
-        if (u < a.dm.n_units) {
-            const int fill = a.blob.fill[u];
-            const int s = u / a.dm.n_v_heads;
-            due = fill >= a.dm.window || (a.force != nullptr && a.force[s] != 0 && fill > 0);
+    for (int p0 = 0; p0 < n; p0 += P * 1024) {
+        int fill[P], forced[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int u = p0 + i * 1024 + tid;
+            const bool in = u < n;
+            fill[i] = in ? a.blob.fill[u] : 0;
+            forced[i] = (in && a.force != nullptr) ? (int)a.force[u / a.dm.n_v_heads] : 0;
         }
-        const uint64_t m = __ballot(due);
-        const int before =
-            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (lane == 0) wave_cnt[wave] = __popcll(m);
-        __syncthreads();
-        int off = base;
-        for (int w = 0; w < wave; ++w) off += wave_cnt[w];
-        if (due) a.blob.work[1 + off + before] = u;
-        __syncthreads();
-        if (tid == 0) {
-            int t = 0;
-            for (int w = 0; w < 16; ++w) t += wave_cnt[w];
-            base += t;
+        uint64_t mask[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const bool due = fill[i] >= a.dm.window || (forced[i] != 0 && fill[i] > 0);
+            mask[i] = __ballot(due);
+            if (lane == 0) cnt[i * NWV + wave] = __popcll(mask[i]);
         }
         __syncthreads();
+        if (wave == 0) {
+            // exclusive offsets in (block, wavefront) order: four counts per
+            // lane, then an inclusive scan of the lane sums
+            static_assert(P * NWV == 4 * kWave, "four counts per lane");
+            int c[4], sum = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[j] = cnt[4 * lane + j];
+                sum += c[j];
+            }
+            int incl = sum;
+#pragma unroll
+            for (int d = 1; d < kWave; d *= 2) {
+                const int y = __shfl_up(incl, d, kWave);
+                if (lane >= d) incl += y;
+            }
+            int off = base + incl - sum;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                cnt[4 * lane + j] = off;
+                off += c[j];
+            }
+            const int total = __shfl(incl, kWave - 1, kWave);
+            if (lane == 0) base += total;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const uint64_t m = mask[i];
+            if ((m >> lane) & 1u) {
+                const int before =
+                    __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+                a.blob.work[1 + cnt[i * NWV + wave] + before] = p0 + i * 1024 + tid;
+            }
+        }
+        __syncthreads();  // the offsets are rewritten by the next pass
     }
     if (tid == 0) a.blob.work[0] = base;
 }
 
-
 __global__ void clear_status_kernel(uint32_t* status) { *status = 0u; }
 
+// Workgroups of `kernel` that the device holds at once: the size of a
+// persistent grid.  Cached per device and variant; 0 when the runtime cannot
+// say (the caller then falls back to a fixed size).
+template <typename K>
+int resident_blocks(K kernel, int block, int variant) {
+    constexpr int kMaxDev = 64, kVariants = 16;
+    static std::atomic<int> cache[kMaxDev][kVariants];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const bool cacheable = dev >= 0 && dev < kMaxDev && variant >= 0 && variant < kVariants;
+    if (cacheable) {
+        const int c = cache[dev][variant].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block, 0) != hipSuccess) return 0;
+    const int r = cus * (per > 0 ? per : 1);
+    if (cacheable && r > 0) cache[dev][variant].store(r, std::memory_order_relaxed);
+    return r;
+}
+
 hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, hipStream_t st) {
-    // a fixed grid walks the units (init, dequant) or the work list (flush)
-    const int grid_cap = 2048;
-    const dim3 grid(a.dm.n_units < grid_cap ? a.dm.n_units : grid_cap), block(kWave * d / 16);
+    // a persistent grid, as many workgroups as the device holds at once, walks
+    // the units (init, dequant, prefill) or the work list (flush): idle
+    // workgroups would otherwise wait for a free CU only to find no work
+    const int block_threads = kWave * d / 16;
+    const dim3 block(block_threads);
     const bool kda = gate_kind == LQ_GATE_CHANNEL;
     if (mode == kModeFlush) {
         hipLaunchKernelGGL(due_scan_kernel, dim3(1), dim3(1024), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-#define LQ_MAT(D_, K_, M_) hipLaunchKernelGGL((materialize_kernel<D_, K_, M_>), grid, block, 0, st, a)
+    auto grid_for = [&](auto kernel, int variant) {
+        int g = resident_blocks(kernel, block_threads, variant);
+        if (g <= 0) g = 2048;
+        return dim3(a.dm.n_units < g ? a.dm.n_units : g);
+    };
+#define LQ_MAT(D_, K_, M_)                                                                              \
+    hipLaunchKernelGGL((materialize_kernel<D_, K_, M_>),                                               \
+                       grid_for(materialize_kernel<D_, K_, M_>, ((D_ == 128) * 2 + (K_ ? 1 : 0)) * 4 + M_), \
+                       block, 0, st, a)
 #define LQ_MAT_MODE(D_, K_)                                      \
     do {                                                         \
         if (mode == kModeInit) LQ_MAT(D_, K_, kModeInit);        \

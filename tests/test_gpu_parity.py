@@ -164,6 +164,36 @@ def test_forced_flush_of_empty_window_is_a_no_op():
     assert int(after["work"][0]) == 0  # nothing was due
 
 
+def test_due_list_over_several_scan_passes():
+    # 41,600 units: more than two passes of the due-unit scan (16,384 units
+    # each) with random fill counts and forced sequences.  The work list holds
+    # every unit whose window is full, or forced and non-empty, in ascending
+    # order; exactly those units restart with an empty window.
+    wl = small("gdn_decode", name="scan", n_seq=2600, n_v_heads=16, n_k_heads=16, d=64, window=4,
+               n_comp=2, prefill=0, outlier_rows=0, outlier_cols=0)
+    cfg = _cfg(wl)
+    st = lq.new_state(cfg)
+    lq.lq_state_init(cfg, st, None)
+    views = lq.state_views(cfg, st)
+    for k in ("buf_k", "buf_v", "buf_beta"):
+        views[k].zero_()
+    views["buf_gate"].fill_(1.0)
+    g = torch.Generator().manual_seed(5)
+    fill = torch.randint(0, wl.window + 1, (wl.n_units,), generator=g, dtype=torch.int32)
+    force = (torch.rand(wl.n_seq, generator=g) < 0.3).to(torch.uint8)
+    views["fill"].copy_(fill.cuda())
+    lq.lq_window_flush(cfg, st, force.cuda())
+    torch.cuda.synchronize()
+    forced_unit = force.repeat_interleave(wl.n_v_heads).bool()
+    due = (fill >= wl.window) | (forced_unit & (fill > 0))
+    expect = torch.nonzero(due).flatten().to(torch.int32)
+    work = views["work"].cpu()
+    assert int(work[0]) == expect.numel()
+    assert torch.equal(work[1:1 + expect.numel()], expect)
+    assert torch.equal(views["fill"].cpu(), torch.where(due, torch.zeros_like(fill), fill))
+    assert lq.lq_read_status(cfg, st, clear=True) == 0
+
+
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_fp32_state_kernel_matches_oracle(gate, d):
