@@ -978,17 +978,27 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                     *reinterpret_cast<float4*>(cvb + (size_t)(rslot - 1) * D + 16 * b + 4 * q) =
                         make_float4((float)T[b][0], (float)T[b][1], (float)T[b][2], (float)T[b][3]);
             }
+            // column lines, one chosen column at a time: its block and register
+            // are uniform (a scalar branch picks them), its quad is the lane
+            // mask; where a row line crosses it, the row line keeps the value
+            for (int c = 0; c < nc; ++c) {
+                const int idx = __builtin_amdgcn_readfirstlane(lds_chosen[c]);
+                if (idx < D) continue;
+                const int col = idx - D, cb = col >> 4, cr = col & 3;
+                const bool mine = q == ((col >> 2) & 3);
+                float* dst = cvb + (size_t)(__builtin_amdgcn_readfirstlane(lds_slot[idx]) - 1) * D + n;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
+                for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int cs = lds_slot[D + 16 * b + 4 * q + r];
-                    if (cs) {
-                        cvb[(size_t)(cs - 1) * D + n] = rslot ? 0.0f : (float)T[b][r];
-                        T[b][r] = 0.0;
-                    }
-                    if (rslot) T[b][r] = 0.0;
-                }
+                    for (int r = 0; r < 4; ++r)
+                        if (b == cb && r == cr && mine) {
+                            *dst = rslot ? 0.0f : (float)T[b][r];
+                            T[b][r] = 0.0;
+                        }
+            }
+            if (rslot) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) T[b] = v4d{0.0, 0.0, 0.0, 0.0};
             }
         }
 
@@ -1032,23 +1042,32 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             const float sg = (float)(mx / (e4m3 ? 448.0 : 127.0));
             if (q == 0) a.blob.sigma[(size_t)u * D + n] = sg;
             const double isg = sg != 0.0f ? 1.0 / (double)sg : 0.0;
+            // an all-zero row (sigma 0) takes code 0 by a select, not a branch
+            const bool live = sg != 0.0f;
+            uint32_t* crow = reinterpret_cast<uint32_t*>(a.blob.codes + ((size_t)u * D + n) * D + 4 * q);
+            if (e4m3) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                uint32_t packed = 0u;
+                for (int b = 0; b < NB; ++b) {
+                    uint32_t packed = 0u;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    uint32_t code = 0u;
-                    if (sg != 0.0f) {
-                        const double x = T[b][r] * (isg * lds_ismooth[16 * b + 4 * q + r]);
-                        if (e4m3) {
-                            code = e4m3_code(x);
-                        } else {
-                            code = (uint32_t)(int)fmin(fmax(rint(x), -127.0), 127.0) & 0xFFu;
-                        }
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t code = e4m3_code(T[b][r] * (isg * lds_ismooth[16 * b + 4 * q + r]));
+                        packed |= (live ? code : 0u) << (8 * r);
                     }
-                    packed |= code << (8 * r);
+                    crow[4 * b] = packed;
                 }
-                *reinterpret_cast<uint32_t*>(a.blob.codes + ((size_t)u * D + n) * D + 16 * b + 4 * q) = packed;
+            } else {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    uint32_t packed = 0u;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const double x = T[b][r] * (isg * lds_ismooth[16 * b + 4 * q + r]);
+                        const uint32_t code = (uint32_t)(int)fmin(fmax(rint(x), -127.0), 127.0) & 0xFFu;
+                        packed |= (live ? code : 0u) << (8 * r);
+                    }
+                    crow[4 * b] = packed;
+                }
             }
         }
         }
