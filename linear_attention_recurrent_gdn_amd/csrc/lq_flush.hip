@@ -361,12 +361,55 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     const int nc = a.dm.n_comp;
 
     const int n_work = (MODE == kModeFlush) ? a.blob.work[0] : a.dm.n_units;
+    constexpr bool kFromCodes = !(MODE == kModeInit || PF);  // the start state is the quantized one
+    // the unit of the next work item is read one item ahead
+    int u_next = (MODE == kModeFlush) ? a.blob.work[1 + min((int)blockIdx.x, max(n_work - 1, 0))]
+                                      : (int)blockIdx.x;
     for (int wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
-        const int u = (MODE == kModeFlush) ? a.blob.work[1 + wi] : wi;
+        const int u = u_next;
+        if constexpr (MODE == kModeFlush) {
+            const int wn = wi + (int)gridDim.x;
+            u_next = a.blob.work[1 + (wn < n_work ? wn : wi)];
+        } else {
+            u_next = wi + (int)gridDim.x;
+        }
         const int s = u / a.dm.n_v_heads;
         const int h = u - s * a.dm.n_v_heads;
         const int kh = h / a.dm.group;
         const size_t kvec = (size_t)s * a.dm.n_k_heads + kh;
+
+        // ---------------- A: the window-start state; T[b][r] = S[n][16b + 4q + r]
+        //
+        // Its loads depend on the unit alone and are requested first.  The
+        // window count and then the first chunk of replayed tokens follow, so
+        // the dequantization waits for none of those (vector loads complete in
+        // order), while the chunk's latency overlaps it.
+        float4 sv[NB];    // start state S0 (init, prefill) or smoothing factors
+        uint32_t wd[NB];  // codes of the row's 16-column blocks (4 per word)
+        float sgr_f = 0.f;
+        float4 cv4 = make_float4(0.f, 0.f, 0.f, 0.f);  // this thread's four floats of the compensator lines
+        int cil = 0;                                    // slot indices, lane c holds slot c
+        if constexpr (!kFromCodes) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                sv[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+                wd[b] = 0u;
+                if (a.S0 != nullptr)
+                    sv[b] = *reinterpret_cast<const float4*>(a.S0 + ((size_t)u * D + n) * D + 16 * b + 4 * q);
+            }
+        } else {
+            sgr_f = a.blob.sigma[(size_t)u * D + n];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                sv[b] = *reinterpret_cast<const float4*>(a.blob.smooth + (size_t)u * D + 16 * b + 4 * q);
+                wd[b] = *reinterpret_cast<const uint32_t*>(a.blob.codes + ((size_t)u * D + n) * D + 16 * b + 4 * q);
+            }
+            if (nc > 0) {
+                static_assert(NT * 4 >= 16 * D, "one float4 per thread covers 16 lines");
+                cv4 = *reinterpret_cast<const float4*>(a.blob.comp_vec + (size_t)u * nc * D + min(4 * tid, nc * D - 4));
+                cil = a.blob.comp_idx[(size_t)u * nc + min(lane, nc - 1)];
+            }
+        }
 
         int n_replay = 0;
         if (MODE == kModeFlush || (MODE == kModeDequant && a.include_buffer)) {
@@ -375,8 +418,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
         }
         if constexpr (PF) n_replay = a.n_tok;
 
-        // the replayed tokens (window buffer, or the prompt): the first chunk is
-        // requested before the window-start state so the two latencies overlap
+        // the replayed tokens (window buffer, or the prompt)
         bool h16 = a.dm.buffer_format == LQ_BUFFER_FP16;
         const size_t esz = h16 ? 2 : 4;
         const void* bk = (const char*)a.blob.buf_k + kvec * (size_t)W * D * esz;
@@ -407,59 +449,43 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             if constexpr (PF) pfq = fetch_q<D>(bq, ts.k, 0, n_replay, tid);
         }
 
-        // ---------------- A: the window-start state; T[b][r] = S[n][16b + 4q + r]
         v4d T[NB];
-        if constexpr (MODE == kModeInit || PF) {
+        if constexpr (!kFromCodes) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (a.S0 != nullptr)
-                    f = *reinterpret_cast<const float4*>(a.S0 + ((size_t)u * D + n) * D + 16 * b + 4 * q);
-                T[b] = v4d{(double)f.x, (double)f.y, (double)f.z, (double)f.w};
-            }
+            for (int b = 0; b < NB; ++b)
+                T[b] = v4d{(double)sv[b].x, (double)sv[b].y, (double)sv[b].z, (double)sv[b].w};
         } else {
-            const double sgr = (double)a.blob.sigma[(size_t)u * D + n];
+            const double sgr = (double)sgr_f;
             const bool e4m3 = a.dm.code_format == LQ_CODE_E4M3;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const float4 s4 = *reinterpret_cast<const float4*>(a.blob.smooth + (size_t)u * D + 16 * b + 4 * q);
-                const uint32_t wd = *reinterpret_cast<const uint32_t*>(a.blob.codes + ((size_t)u * D + n) * D + 16 * b + 4 * q);
                 float cv[4];
                 if (e4m3) {
                     // exact: every E4M3 value is an fp32 value
-                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd, false);
-                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd, true);
+                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[b], false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[b], true);
                     cv[0] = lo.x;
                     cv[1] = lo.y;
                     cv[2] = hi.x;
                     cv[3] = hi.y;
                 } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) cv[r] = (float)((int)(wd << (24 - 8 * r)) >> 24);
+                    for (int r = 0; r < 4; ++r) cv[r] = (float)((int)(wd[b] << (24 - 8 * r)) >> 24);
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) T[b][r] = sgr * (double)cv[r] * (double)pick4(s4, r);
+                for (int r = 0; r < 4; ++r) T[b][r] = sgr * (double)cv[r] * (double)pick4(sv[b], r);
             }
             // compensator lines: a row slot adds its line to the four lanes of
             // that row, a column slot adds one value per row.  The unit's lines
-            // (at most 16 d floats) go to LDS, into the partial-gram space that
-            // the replay only uses later, in the same trip as the slot indices:
-            // no load waits for another
+            // (at most 16 d floats) pass through LDS, in the partial-gram space
+            // that the replay only uses later
             if (nc > 0) {
-                const int* ci = a.blob.comp_idx + (size_t)u * nc;
-                const float* cv = a.blob.comp_vec + (size_t)u * nc * D;
                 float* lds_cv = reinterpret_cast<float*>(&lds_gram[0][0][0]);
-                static_assert(sizeof(lds_gram) >= 16 * D * sizeof(float) && NT * 4 >= 16 * D, "room for 16 lines");
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)(cv + min(4 * tid, nc * D - 4)),
-                    (void __attribute__((address_space(3)))*)(lds_cv + 4 * kWave * wave), 16, 0, 0);
-                // the slot indices in one vector load (lane c holds slot c), not
-                // one scalar load and wait per slot
-                const int cil = ci[min(lane, nc - 1)];
+                static_assert(sizeof(lds_gram) >= 16 * D * sizeof(float), "room for 16 lines");
+                *reinterpret_cast<float4*>(lds_cv + 4 * tid) = cv4;
                 int my_slot = -1;  // the row slot holding this lane's row, if any
                 for (int c = 0; c < nc; ++c)
                     if (__builtin_amdgcn_readlane(cil, c) == n) my_slot = c;
-                __builtin_amdgcn_s_waitcnt(0);  // this thread's lines are in LDS
                 __syncthreads();
                 float4 rowv[NB];
                 const float* rv = lds_cv + max(my_slot, 0) * D;
