@@ -34,9 +34,11 @@
  *    pointers;
  *  - `stream` is a hipStream_t (NULL = the default stream); every call except
  *    lq_read_status is asynchronous on it, launches nothing when it returns
- *    an error, and never allocates device memory; the library holds no
- *    global mutable state, so distinct state blobs may be used concurrently;
- *    calls on one blob must be ordered on one stream;
+ *    an error, and never allocates device memory; the library's only global
+ *    state is a per-device cache of a launch size (how many flush workgroups
+ *    the device holds at once, from the HIP occupancy query, written once with
+ *    atomic stores), so distinct state blobs may be used concurrently, from
+ *    any host thread; calls on one blob must be ordered on one stream;
  *  - device pointers must be 16-byte aligned, the state blob 256-byte
  *    aligned (LQ_EINVAL otherwise);
  *  - errors found on the device (a decode step on a full window, a
