@@ -158,53 +158,15 @@ __device__ __forceinline__ double group_bcast(double x, int g) {
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-// Wavefront argmax of (value, candidate index), larger value first, equal
-// values to the lower index; the result in every lane.  Lanes are paired by
-// DPP inside each 16-lane row (quad swaps, then the half-row and row
-// mirrors), then the rows by the gfx950 row swaps, which hand every lane both
-// values of its pair: no LDS round trips.
-struct Cand {
-    double v;
-    int i;
-};
-
-__device__ __forceinline__ Cand better(Cand a, Cand b) {
-    return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
-}
-
-template <int CTRL>
-__device__ __forceinline__ Cand argmax_dpp(Cand a) {
-    Cand b;
-    b.v = dpp_f64<CTRL>(a.v);
-    b.i = __builtin_amdgcn_update_dpp(0, a.i, CTRL, 0xF, 0xF, false);
-    return better(a, b);
-}
-
-template <bool WIDE>
-__device__ __forceinline__ Cand argmax_swap(Cand a) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, a.v);
-    const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
-    const auto pl = WIDE ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
-                         : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    const auto ph = WIDE ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
-                         : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    const auto pi = WIDE ? __builtin_amdgcn_permlane32_swap(a.i, a.i, false, false)
-                         : __builtin_amdgcn_permlane16_swap(a.i, a.i, false, false);
-    Cand x, y;
-    x.v = __builtin_bit_cast(double, ((uint64_t)(uint32_t)ph[0] << 32) | (uint32_t)pl[0]);
-    x.i = (int)pi[0];
-    y.v = __builtin_bit_cast(double, ((uint64_t)(uint32_t)ph[1] << 32) | (uint32_t)pl[1]);
-    y.i = (int)pi[1];
-    return better(x, y);
-}
-
-__device__ __forceinline__ Cand wave_argmax(Cand a) {
-    a = argmax_dpp<kDppQuadXor1>(a);
-    a = argmax_dpp<kDppQuadXor2>(a);
-    a = argmax_dpp<kDppRowHalfMirror>(a);
-    a = argmax_dpp<kDppRowMirror>(a);
-    a = argmax_swap<false>(a);
-    return argmax_swap<true>(a);
+// Wavefront maximum of a double, in every lane: DPP inside each 16-lane row,
+// then the row swaps.  fmax returns one of its inputs, so the result equals
+// some lane's value exactly.
+__device__ __forceinline__ double wave_max(double x) {
+    x = fmax(x, dpp_f64<kDppQuadXor1>(x));
+    x = fmax(x, dpp_f64<kDppQuadXor2>(x));
+    x = fmax(x, dpp_f64<kDppRowHalfMirror>(x));
+    x = fmax(x, dpp_f64<kDppRowMirror>(x));
+    return across_rows<true>(x);
 }
 
 // E4M3 byte of x (FP64): the nearest value of the 8-bit float format with
@@ -950,34 +912,38 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 
         // ---------------- C2: top-n_comp selection (wavefront 0)
         if (wave == 0) {
-            // scores are >= 0; a NaN score (non-finite input) ranks below every
-            // real one, and a lane with nothing left offers (-1, INT_MAX), which
-            // always loses, so every round picks one untaken candidate
+            // Each round takes every lane's best untaken candidate (the lower
+            // index on equal scores), the wavefront maximum of those, and the
+            // first lane that offers it: its candidates precede those of later
+            // lanes, so equal scores go to the lower candidate index.  Scores
+            // are >= 0; a NaN score (non-finite input) ranks below every real
+            // one, and a taken candidate becomes -1, which never wins.
             double val[CPL];
-            bool taken[CPL];
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const double sc = lds_score[lane * CPL + i];
                 val[i] = __builtin_isnan(sc) ? -0.5 : sc;
-                taken[i] = false;
             }
+            int mine = 0;  // lane r: the candidate chosen in round r
             for (int r = 0; r < nc; ++r) {
                 double bv_ = -1.0;
-                int bi = 0x7fffffff;
+                int bi_ = 0;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i)
-                    if (!taken[i] && val[i] > bv_) {
+                    if (val[i] > bv_) {
                         bv_ = val[i];
-                        bi = lane * CPL + i;
+                        bi_ = i;
                     }
-                {
-                    const Cand best = wave_argmax(Cand{bv_, bi});
-                    bi = best.i;
-                }
+                const double top = wave_max(bv_);
+                const uint64_t hit = __ballot(bv_ == top);
+                const int L = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+                const int pick = __builtin_amdgcn_readlane(bi_, L);
+                const int best = L * CPL + pick;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i)
-                    if (bi == lane * CPL + i) taken[i] = true;
-                if (lane == 0) lds_chosen[r] = bi;
+                    if (lane == L && i == pick) val[i] = -1.0;
+                if (lane == r) mine = best;
+                if (lane == 0) lds_chosen[r] = best;
             }
             // slots in ascending candidate order (rows, then columns)
             for (int x = lane; x < 2 * D; x += kWave) lds_slot[x] = 0;
@@ -985,11 +951,10 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (lane < nc) {
-                const int me = lds_chosen[lane];
                 int rank = 0;
-                for (int q2 = 0; q2 < nc; ++q2) rank += lds_chosen[q2] < me;
-                lds_slot[me] = rank + 1;
-                a.blob.comp_idx[(size_t)u * nc + rank] = me;
+                for (int q2 = 0; q2 < nc; ++q2) rank += __builtin_amdgcn_readlane(mine, q2) < mine;
+                lds_slot[mine] = rank + 1;
+                a.blob.comp_idx[(size_t)u * nc + rank] = mine;
             }
         }
         __syncthreads();
