@@ -27,9 +27,12 @@
 // tokens ahead (so the wait counts are exact and memory latency is paid once
 // per ring, not per token), the d-length dot products reduce with DPP, and
 // with a scalar gate the running gate product stays off the dependent chain.
-// After one barrier every wavefront multiplies its tile rows by s*r (read from
-// LDS, each lane covering 16 columns, rows reduced over 8 lanes with DPP) and
-// writes its rows of o.  The kernel is HBM-bound (about one flop per byte):
+// Wavefronts 1-3 convert their codes to floats while the reverse pass runs
+// (wavefront 0 converts its own after it).  After one barrier every
+// wavefront multiplies its tile rows by s*r (read from LDS, each lane covering
+// 16 columns, rows reduced over 8 lanes with DPP) and writes its rows of o:
+// only the products are left there, where the four units that share a CU
+// reach it together.  The kernel is HBM-bound (about one flop per byte):
 // no MFMA.
 //
 // decode_fp32_kernel: the FP32-state step the pages compare against (the
@@ -196,6 +199,27 @@ __device__ __forceinline__ Vec<EPL> unpack_halves(uint32_t w) {
     return r;
 }
 
+// The 16 codes of one 16-byte tile load as floats, in column order (exact:
+// an INT8 code or an E4M3 value is an fp32 value).
+template <int FMT>
+__device__ __forceinline__ void codes_to_float(const uint4& w4, float (&cf)[16]) {
+    const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+        if constexpr (FMT == LQ_CODE_E4M3) {
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[wi], false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[wi], true);
+            cf[4 * wi + 0] = lo.x;
+            cf[4 * wi + 1] = lo.y;
+            cf[4 * wi + 2] = hi.x;
+            cf[4 * wi + 3] = hi.y;
+        } else {
+#pragma unroll
+            for (int by = 0; by < 4; ++by) cf[4 * wi + by] = (float)((int)(wd[wi] << (24 - 8 * by)) >> 24);
+        }
+    }
+}
+
 }  // namespace
 
 template <int D, bool KDA, int P, int NWB, int FMT, bool H16>
@@ -229,6 +253,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     const uint4* tile = reinterpret_cast<const uint4*>(a.blob.codes + ((size_t)u * D + row0) * D);
     const int my_row = row0 + min(cg, NLW - 1) * RPL + lane / LPR;  // row this lane writes (cg < NLW)
     uint4 tw[NLW];
+    float cf[NLW][16];  // the tile quarter as floats, converted before the barrier
     float sg_row;
 
     // tokens already in the window (uniform: every branch below is scalar).
@@ -245,6 +270,10 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         for (int t = 0; t < NLW; ++t) tw[t] = tile[t * kWave + lane];
         sg_row = a.blob.sigma[(size_t)u * D + my_row];
         j = __builtin_amdgcn_readfirstlane(j_ld);
+        // the codes to floats while wavefront 0 runs the reverse pass, so
+        // that only the products remain after the barrier
+#pragma unroll
+        for (int t = 0; t < NLW; ++t) codes_to_float<FMT>(tw[t], cf[t]);
     } else {
         const size_t kb0 = kvec * (size_t)W * D;  // element offsets of this unit's k and v entries
         const size_t vb0 = (size_t)u * W * D;
@@ -446,6 +475,8 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
             lds_x[lane * EPL + e] = sm.e[e] * r.e[e];
             lds_add[lane * EPL + e] = acc.e[e];
         }
+#pragma unroll
+        for (int t = 0; t < NLW; ++t) codes_to_float<FMT>(tw[t], cf[t]);
     }
     lds_barrier();
 
@@ -462,25 +493,12 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     float mine = 0.f;
 #pragma unroll
     for (int t = 0; t < NLW; ++t) {
-        const uint32_t wd[4] = {tw[t].x, tw[t].y, tw[t].z, tw[t].w};
+        // even columns into p0, odd into p1, each in column order
         float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-        for (int wi = 0; wi < 4; ++wi) {
-            if constexpr (FMT == LQ_CODE_E4M3) {
-                // bytes 0, 1 and 2, 3 of the word (columns 4 wi .. 4 wi + 3)
-                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[wi], false);
-                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[wi], true);
-                p0 = __builtin_fmaf(lo.x, xs[4 * wi + 0], p0);
-                p1 = __builtin_fmaf(lo.y, xs[4 * wi + 1], p1);
-                p0 = __builtin_fmaf(hi.x, xs[4 * wi + 2], p0);
-                p1 = __builtin_fmaf(hi.y, xs[4 * wi + 3], p1);
-            } else {
-#pragma unroll
-                for (int by = 0; by < 4; by += 2) {
-                    p0 = __builtin_fmaf((float)((int)(wd[wi] << (24 - 8 * by)) >> 24), xs[4 * wi + by], p0);
-                    p1 = __builtin_fmaf((float)((int)(wd[wi] << (16 - 8 * by)) >> 24), xs[4 * wi + by + 1], p1);
-                }
-            }
+        for (int c = 0; c < 16; c += 2) {
+            p0 = __builtin_fmaf(cf[t][c], xs[c], p0);
+            p1 = __builtin_fmaf(cf[t][c + 1], xs[c + 1], p1);
         }
         float p = p0 + p1;
         if constexpr (LPR == 8) p = sum8(p);
