@@ -253,7 +253,11 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     const uint4* tile = reinterpret_cast<const uint4*>(a.blob.codes + ((size_t)u * D + row0) * D);
     const int my_row = row0 + min(cg, NLW - 1) * RPL + lane / LPR;  // row this lane writes (cg < NLW)
     uint4 tw[NLW];
-    float cf[NLW][16];  // the tile quarter as floats, converted before the barrier
+    // The tile quarter as floats, converted before the barrier.  Not with the
+    // binary16 buffer: there the extra registers cost a wavefront per SIMD of
+    // occupancy, more than the conversion saves.
+    constexpr bool kEarlyCodes = !H16;
+    float cf[NLW][16];
     float sg_row;
 
     // tokens already in the window (uniform: every branch below is scalar).
@@ -272,8 +276,10 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         j = __builtin_amdgcn_readfirstlane(j_ld);
         // the codes to floats while wavefront 0 runs the reverse pass, so
         // that only the products remain after the barrier
+        if constexpr (kEarlyCodes) {
 #pragma unroll
-        for (int t = 0; t < NLW; ++t) codes_to_float<FMT>(tw[t], cf[t]);
+            for (int t = 0; t < NLW; ++t) codes_to_float<FMT>(tw[t], cf[t]);
+        }
     } else {
         const size_t kb0 = kvec * (size_t)W * D;  // element offsets of this unit's k and v entries
         const size_t vb0 = (size_t)u * W * D;
@@ -475,8 +481,10 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
             lds_x[lane * EPL + e] = sm.e[e] * r.e[e];
             lds_add[lane * EPL + e] = acc.e[e];
         }
+        if constexpr (kEarlyCodes) {
 #pragma unroll
-        for (int t = 0; t < NLW; ++t) codes_to_float<FMT>(tw[t], cf[t]);
+            for (int t = 0; t < NLW; ++t) codes_to_float<FMT>(tw[t], cf[t]);
+        }
     }
     lds_barrier();
 
@@ -493,6 +501,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     float mine = 0.f;
 #pragma unroll
     for (int t = 0; t < NLW; ++t) {
+        if constexpr (!kEarlyCodes) codes_to_float<FMT>(tw[t], cf[t]);
         // even columns into p0, odd into p1, each in column order
         float p0 = 0.f, p1 = 0.f;
 #pragma unroll
