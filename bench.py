@@ -15,7 +15,9 @@ Prints one JSON line:
   value            unit-tokens/s (seq·head·tokens/s) of the INT8 path over the timed steps
   roofline         the decode kernel's algorithmic bytes per launch / its average
                    launch time (a graph of one window of decode launches, HIP events
-                   around the replay), against 8 TB/s
+                   around the replay), against 8 TB/s; `practical` adds what a plain
+                   streaming-read kernel reaches on this device at the same bytes
+                   per launch (probe/stream_read, run after the timed region)
   fp32_state       the FP32-state kernel on the same steps, and the speedup
   cpu_baseline     the CPU oracle (FP64, definitional windowed form) on a bounded
                    sample of the same workload, on this host's cores
@@ -246,6 +248,24 @@ def prefill_timing(lq, wl, cfg, gen, dev, timed_graph):
 # measured HBM traffic (rocprofv3 --pmc), valid only for the kernel it was taken on
 # ---------------------------------------------------------------------------
 
+def practical_read(nbytes: float):
+    """Best rate of the plain streaming-read probe (16-byte loads, grid-stride,
+    nothing else) over its grid sizes at `nbytes` per launch, in GB/s, or None
+    when the probe is not built.  Runs as a child process after the timed work."""
+    import subprocess
+
+    from linear_attention_recurrent_gdn_amd import _build
+
+    if not os.path.exists(_build.PROBE):
+        return None
+    r = subprocess.run([_build.PROBE, str(int(nbytes))], capture_output=True, text=True, timeout=120)
+    rows = [json.loads(line) for line in r.stdout.splitlines() if line.startswith("{")]
+    if r.returncode != 0 or not rows:
+        return None
+    best = max(rows, key=lambda x: x["TBps"])
+    return {"GBps": best["TBps"] * 1e3, "us": best["us"], "grid": best["grid"]}
+
+
 def variant_tag(workload, fmt="int8", buffer="fp32"):
     """Name of a workload variant in profile file names."""
     return workload + ("" if fmt == "int8" else f"_{fmt}") + ("" if buffer == "fp32" else f"_{buffer}buf")
@@ -456,6 +476,17 @@ def main():
 
     if not args.no_prefill and wl.prefill > 0 and not wl.projected and L == 1:
         result["prefill"] = prefill_timing(lq, wl, cfg, gen, dev, timed_graph)
+
+    # the practical ceiling at the decode launch's byte count (a child process;
+    # the device is idle here)
+    torch.cuda.synchronize()
+    pr = practical_read(avg_bytes)
+    if pr is not None:
+        result["roofline"]["practical"] = {
+            "kernel": "stream_read (probe/stream_read.hip): 16-byte loads, grid-stride, nothing else",
+            "bytes_per_launch": avg_bytes, "achieved": pr["GBps"], "unit": "GB/s",
+            "frac_of_peak": pr["GBps"] / HBM_PEAK_GBS, "decode_frac_of_practical": achieved / pr["GBps"],
+        }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds, args.format, args.buffer)
