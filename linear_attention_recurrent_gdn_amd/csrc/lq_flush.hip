@@ -971,13 +971,18 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             }
             // column lines, one chosen column at a time: its block and register
             // are uniform (a scalar branch picks them), its quad is the lane
-            // mask; where a row line crosses it, the row line keeps the value
+            // mask; where a row line crosses it, the row line keeps the value.
+            // The chosen candidates come in one read (lane c holds round c's),
+            // a column's slot is its rank among them (a ballot), so the loop
+            // itself waits for no LDS read
+            const int chl = lds_chosen[max(min(lane, nc - 1), 0)];
             for (int c = 0; c < nc; ++c) {
-                const int idx = __builtin_amdgcn_readfirstlane(lds_chosen[c]);
+                const int idx = __builtin_amdgcn_readlane(chl, c);
                 if (idx < D) continue;
                 const int col = idx - D, cb = col >> 4, cr = col & 3;
                 const bool mine = q == ((col >> 2) & 3);
-                float* dst = cvb + (size_t)(__builtin_amdgcn_readfirstlane(lds_slot[idx]) - 1) * D + n;
+                const int rank = __popcll(__ballot(lane < nc && chl < idx));
+                float* dst = cvb + (size_t)rank * D + n;
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
