@@ -34,16 +34,16 @@
  *    pointers;
  *  - `stream` is a hipStream_t (NULL = the default stream); every call except
  *    lq_read_status is asynchronous on it, launches nothing when it returns
- *    an error, and never allocates device memory; the library's only global
- *    state is a per-device cache of a launch size (how many flush workgroups
- *    the device holds at once, from the HIP occupancy query, written once with
- *    atomic stores), so distinct state blobs may be used concurrently, from
- *    any host thread; calls on one blob must be ordered on one stream;
+ *    an error, and never allocates device memory; the library holds no
+ *    global mutable state (each call derives its launch sizes afresh), so
+ *    distinct state blobs may be used concurrently, from any host thread;
+ *    calls on one blob must be ordered on one stream;
  *  - device pointers must be 16-byte aligned, the state blob 256-byte
  *    aligned (LQ_EINVAL otherwise);
  *  - errors found on the device (a decode step on a full window, a
- *    non-finite input) never abort: they set sticky flags in the blob, read
- *    with lq_read_status.
+ *    non-finite input or start state) never abort: they set sticky flags in
+ *    the blob, read with lq_read_status and reset with lq_clear_status (and
+ *    by lq_state_init / lq_prefill, which start a new state).
  *
  * Layouts (row-major, fp32 unless noted; unit u = s * n_v_heads + h; value
  * head h reads key head h / (n_v_heads / n_k_heads)):
@@ -63,6 +63,10 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* The HIP runtime's stream handle, declared exactly as <hip/hip_runtime_api.h>
+ * declares it, so this header needs no HIP header. */
+typedef struct ihipStream_t* hipStream_t;
 
 /* return codes */
 #define LQ_OK 0
@@ -84,7 +88,7 @@ extern "C" {
 
 /* sticky device flags (lq_read_status) */
 #define LQ_DEV_WINDOW_OVERFLOW 0x1u /* lq_decode_step found a full window: that unit's o is NaN, nothing appended */
-#define LQ_DEV_NONFINITE_INPUT 0x2u /* a decode input (q, k, v, beta, gate) was NaN or Inf */
+#define LQ_DEV_NONFINITE_INPUT 0x2u /* an input (decode token, prompt token, start state S0) was NaN or Inf */
 #define LQ_DEV_BUFFER_SATURATED 0x4u /* binary16 buffer: a k or v magnitude above 65504 was stored as 65504 */
 
 /*
@@ -148,10 +152,11 @@ int32_t lq_state_layout(const lq_config* cfg, lq_layout* layout);
 /*
  * Quantize a start state into the blob: compensators, smoothing, scales and
  * codes of S0 (the abstract's window-end quantization with an empty window),
- * fill = 0, status = 0.  S0 may be NULL for the zero state.  Buffers are left
- * as they are (never read while fill = 0).
+ * fill = 0, status = 0 (then LQ_DEV_NONFINITE_INPUT if S0 holds a NaN or Inf).
+ * S0 may be NULL for the zero state.  Buffers are left as they are (never
+ * read while fill = 0).
  */
-int32_t lq_state_init(const lq_config* cfg, void* state, const float* S0, void* stream);
+int32_t lq_state_init(const lq_config* cfg, void* state, const float* S0, hipStream_t stream);
 
 /*
  * One decode token for every sequence.  Per unit: append (k, v, beta, gate)
@@ -165,18 +170,24 @@ int32_t lq_state_init(const lq_config* cfg, void* state, const float* S0, void* 
  */
 int32_t lq_decode_step(const lq_config* cfg, void* state, const float* q, const float* k,
                        const float* v, const float* beta, const float* gate, float* o,
-                       void* stream);
+                       hipStream_t stream);
 
 /*
- * Window-boundary requantization.  Every unit whose window is full
- * (fill == window), and every unit of a sequence s with force_mask[s] != 0
- * and fill > 0, is advanced through its buffered tokens in FP64, gets new
- * compensators, smoothing, scales and codes, and fill = 0.  Other units are
- * untouched.  force_mask: device uint8 [n_seq], or NULL.  Must be called
- * between the decode step that fills a window and the next decode step.
+ * Window-boundary requantization: the arXiv 2609.38166 abstract ("Abstract
+ * (arXiv)" section, mlsanity.com paper page) leaps over a window of tokens and
+ * quantizes the state once, at the window's end, keeping the largest outliers
+ * as Compensator Tokens and smoothing the residual before quantization; the
+ * bedrocknews.com review adds that this happens at the window boundary instead
+ * of after every update.  Every unit whose window is full (fill == window),
+ * and every unit of a sequence s with force_mask[s] != 0 and fill > 0, is
+ * advanced through its buffered tokens in FP64, gets new compensators,
+ * smoothing, scales and codes, and fill = 0.  Other units are untouched.
+ * force_mask: device uint8 [n_seq], or NULL.  Must be called between the
+ * decode step that fills a window and the next decode step.  Uses the blob's
+ * work section as scratch (the list of due units).
  */
 int32_t lq_window_flush(const lq_config* cfg, void* state, const uint8_t* force_mask,
-                        void* stream);
+                        hipStream_t stream);
 
 /*
  * Prefill: run a prompt of n_tok tokens (n_tok >= 0, the same for every
@@ -194,20 +205,25 @@ int32_t lq_window_flush(const lq_config* cfg, void* state, const uint8_t* force_
  * (channel), all fp32, same conventions as lq_decode_step.  o (fp32
  * [n_tok][n_seq][n_v_heads][d_v], or NULL) receives o_t = S_t q_t for every
  * prompt token.  Pointers are device pointers owned by the caller, 16-byte
- * aligned (beta and a scalar gate 4-byte); errors as for lq_state_init.
+ * aligned (beta and a scalar gate 4-byte); errors as for lq_state_init (a
+ * NaN or Inf in S0 or in a prompt token sets LQ_DEV_NONFINITE_INPUT).
  */
 int32_t lq_prefill(const lq_config* cfg, void* state, const float* S0, int32_t n_tok,
                    const float* q, const float* k, const float* v, const float* beta,
-                   const float* gate, float* o, void* stream);
+                   const float* gate, float* o, hipStream_t stream);
 
 /*
  * Dequantized state into S_out (fp32): the window-start state
- * Diag(sigma) Q Diag(s) + compensator lines, or, with include_buffer != 0,
- * that state advanced through the buffered tokens (the state after the last
- * decode step).  For inspection and checkpoint conversion.
+ * Diag(sigma) Q Diag(s) + compensator lines -- the fixed low-bit state that
+ * the arXiv 2609.38166 abstract ("Abstract (arXiv)" section, mlsanity.com
+ * paper page) keeps for the whole window, with the Compensator Tokens added
+ * back -- or, with include_buffer != 0, that state advanced through the
+ * buffered tokens: the abstract's fixed low-bit state together with the
+ * high-precision buffered updates, i.e. the state after the last decode step.
+ * For inspection and checkpoint conversion.
  */
 int32_t lq_dequant_state(const lq_config* cfg, const void* state, float* S_out,
-                         int32_t include_buffer, void* stream);
+                         int32_t include_buffer, hipStream_t stream);
 
 /*
  * The FP32-state comparison step: S (fp32, in place) advanced by one token
@@ -217,14 +233,20 @@ int32_t lq_dequant_state(const lq_config* cfg, const void* state, float* S_out,
  */
 int32_t lq_fp32_decode_step(const lq_config* cfg, float* S, const float* q, const float* k,
                             const float* v, const float* beta, const float* gate, float* o,
-                            void* stream);
+                            hipStream_t stream);
 
 /*
- * Synchronizes `stream`, then returns the blob's sticky flags in *flags.
- * clear != 0 resets them to 0 afterwards (ordered on the stream).
+ * Synchronizes `stream`, then returns the blob's sticky device flags
+ * (LQ_DEV_*) in *flags (host pointer).  The flags stay set.
  */
-int32_t lq_read_status(const lq_config* cfg, void* state, uint32_t* flags, int32_t clear,
-                       void* stream);
+int32_t lq_read_status(const lq_config* cfg, const void* state, uint32_t* flags,
+                       hipStream_t stream);
+
+/*
+ * Resets the blob's sticky device flags to 0, asynchronously on `stream`
+ * (ordered after the calls already queued there).
+ */
+int32_t lq_clear_status(const lq_config* cfg, void* state, hipStream_t stream);
 
 /* Static description of a return code. */
 const char* lq_strerror(int32_t code);

@@ -35,7 +35,7 @@ LQ_DEV_BUFFER_SATURATED = 0x4
 
 EXPORTS = ("lq_state_bytes", "lq_state_layout", "lq_state_init", "lq_prefill", "lq_decode_step",
            "lq_window_flush", "lq_dequant_state", "lq_fp32_decode_step", "lq_read_status",
-           "lq_strerror")
+           "lq_clear_status", "lq_strerror")
 
 
 class LQError(RuntimeError):
@@ -103,7 +103,8 @@ def load_library(path: Optional[str] = None):
     lib.lq_window_flush.argtypes = [CP, P, P, P]
     lib.lq_dequant_state.argtypes = [CP, P, P, ctypes.c_int32, P]
     lib.lq_fp32_decode_step.argtypes = [CP, P, P, P, P, P, P, P, P]
-    lib.lq_read_status.argtypes = [CP, P, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32, P]
+    lib.lq_read_status.argtypes = [CP, P, ctypes.POINTER(ctypes.c_uint32), P]
+    lib.lq_clear_status.argtypes = [CP, P, P]
     for f in EXPORTS[:-1]:
         getattr(lib, f).restype = ctypes.c_int32
     lib.lq_strerror.argtypes = [ctypes.c_int32]
@@ -268,11 +269,20 @@ def lq_fp32_decode_step(cfg: Config, S, q, k, v, beta, gate, o, stream=None) -> 
 
 
 def lq_read_status(cfg: Config, state, clear: bool = False, stream=None) -> int:
+    """The blob's sticky device flags (synchronizes the stream); with
+    ``clear`` they are then reset through lq_clear_status."""
     flags = ctypes.c_uint32(0)
     rc = load_library().lq_read_status(ctypes.byref(cfg.c()), _state_ptr(cfg, state),
-                                       ctypes.byref(flags), int(bool(clear)), _stream(stream))
+                                       ctypes.byref(flags), _stream(stream))
     _check("lq_read_status", rc)
+    if clear:
+        lq_clear_status(cfg, state, stream)
     return flags.value
+
+
+def lq_clear_status(cfg: Config, state, stream=None) -> None:
+    rc = load_library().lq_clear_status(ctypes.byref(cfg.c()), _state_ptr(cfg, state), _stream(stream))
+    _check("lq_clear_status", rc)
 
 
 def lq_strerror(code: int) -> str:

@@ -64,7 +64,7 @@ int32_t lq_state_layout(const lq_config* cfg, lq_layout* layout) {
     return LQ_OK;
 }
 
-int32_t lq_state_init(const lq_config* cfg, void* state, const float* S0, void* stream) {
+int32_t lq_state_init(const lq_config* cfg, void* state, const float* S0, hipStream_t stream) {
     int32_t rc = check_config(cfg);
     if (rc != LQ_OK) return rc;
     if (state == nullptr || !aligned(state, kSectionAlign)) return LQ_EINVAL;
@@ -75,12 +75,12 @@ int32_t lq_state_init(const lq_config* cfg, void* state, const float* S0, void* 
     a.blob = blob_ptrs(state, L);
     a.dm = dims_of(cfg);
     a.S0 = S0;
-    return hip_status(launch_materialize(a, kModeInit, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+    return hip_status(launch_materialize(a, kModeInit, cfg->d_k, cfg->gate_kind, stream));
 }
 
 int32_t lq_prefill(const lq_config* cfg, void* state, const float* S0, int32_t n_tok, const float* q,
                    const float* k, const float* v, const float* beta, const float* gate, float* o,
-                   void* stream) {
+                   hipStream_t stream) {
     int32_t rc = check_config(cfg);
     if (rc != LQ_OK) return rc;
     if (state == nullptr || n_tok < 0) return LQ_EINVAL;
@@ -107,12 +107,12 @@ int32_t lq_prefill(const lq_config* cfg, void* state, const float* S0, int32_t n
     a.pbeta = beta;
     a.pgate = gate;
     a.po = n_tok > 0 ? o : nullptr;
-    return hip_status(launch_materialize(a, kModePrefill, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+    return hip_status(launch_materialize(a, kModePrefill, cfg->d_k, cfg->gate_kind, stream));
 }
 
 int32_t lq_decode_step(const lq_config* cfg, void* state, const float* q, const float* k,
                        const float* v, const float* beta, const float* gate, float* o,
-                       void* stream) {
+                       hipStream_t stream) {
     int32_t rc = check_config(cfg);
     if (rc != LQ_OK) return rc;
     if (state == nullptr || q == nullptr || k == nullptr || v == nullptr || beta == nullptr ||
@@ -133,11 +133,11 @@ int32_t lq_decode_step(const lq_config* cfg, void* state, const float* q, const 
     a.beta = beta;
     a.gate = gate;
     a.o = o;
-    return hip_status(launch_decode_q8(a, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+    return hip_status(launch_decode_q8(a, cfg->d_k, cfg->gate_kind, stream));
 }
 
 int32_t lq_window_flush(const lq_config* cfg, void* state, const uint8_t* force_mask,
-                        void* stream) {
+                        hipStream_t stream) {
     int32_t rc = check_config(cfg);
     if (rc != LQ_OK) return rc;
     if (state == nullptr || !aligned(state, kSectionAlign)) return LQ_EINVAL;
@@ -147,11 +147,11 @@ int32_t lq_window_flush(const lq_config* cfg, void* state, const uint8_t* force_
     a.blob = blob_ptrs(state, L);
     a.dm = dims_of(cfg);
     a.force = force_mask;
-    return hip_status(launch_materialize(a, kModeFlush, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+    return hip_status(launch_materialize(a, kModeFlush, cfg->d_k, cfg->gate_kind, stream));
 }
 
 int32_t lq_dequant_state(const lq_config* cfg, const void* state, float* S_out,
-                         int32_t include_buffer, void* stream) {
+                         int32_t include_buffer, hipStream_t stream) {
     int32_t rc = check_config(cfg);
     if (rc != LQ_OK) return rc;
     if (state == nullptr || S_out == nullptr || !aligned(state, kSectionAlign) || !aligned(S_out, 16))
@@ -163,12 +163,12 @@ int32_t lq_dequant_state(const lq_config* cfg, const void* state, float* S_out,
     a.dm = dims_of(cfg);
     a.S_out = S_out;
     a.include_buffer = include_buffer != 0;
-    return hip_status(launch_materialize(a, kModeDequant, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+    return hip_status(launch_materialize(a, kModeDequant, cfg->d_k, cfg->gate_kind, stream));
 }
 
 int32_t lq_fp32_decode_step(const lq_config* cfg, float* S, const float* q, const float* k,
                             const float* v, const float* beta, const float* gate, float* o,
-                            void* stream) {
+                            hipStream_t stream) {
     int32_t rc = check_config(cfg);
     if (rc != LQ_OK) return rc;
     if (S == nullptr || q == nullptr || k == nullptr || v == nullptr || beta == nullptr ||
@@ -186,23 +186,29 @@ int32_t lq_fp32_decode_step(const lq_config* cfg, float* S, const float* q, cons
     a.beta = beta;
     a.gate = gate;
     a.o = o;
-    return hip_status(launch_decode_fp32(a, cfg->d_k, cfg->gate_kind, (hipStream_t)stream));
+    return hip_status(launch_decode_fp32(a, cfg->d_k, cfg->gate_kind, stream));
 }
 
-int32_t lq_read_status(const lq_config* cfg, void* state, uint32_t* flags, int32_t clear,
-                       void* stream) {
+int32_t lq_read_status(const lq_config* cfg, const void* state, uint32_t* flags, hipStream_t stream) {
     int32_t rc = check_config(cfg);
     if (rc != LQ_OK) return rc;
     if (state == nullptr || flags == nullptr || !aligned(state, kSectionAlign)) return LQ_EINVAL;
     lq_layout L;
     compute_layout(*cfg, L);
-    hipStream_t st = (hipStream_t)stream;
-    uint32_t* dev = (uint32_t*)((char*)state + L.status);
-    if (hipMemcpyAsync(flags, dev, sizeof(uint32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+    const uint32_t* dev = (const uint32_t*)((const char*)state + L.status);
+    if (hipMemcpyAsync(flags, dev, sizeof(uint32_t), hipMemcpyDeviceToHost, stream) != hipSuccess)
         return LQ_EHIP;
-    if (hipStreamSynchronize(st) != hipSuccess) return LQ_EHIP;
-    if (clear) return hip_status(launch_clear_status(dev, st));
+    if (hipStreamSynchronize(stream) != hipSuccess) return LQ_EHIP;
     return LQ_OK;
+}
+
+int32_t lq_clear_status(const lq_config* cfg, void* state, hipStream_t stream) {
+    int32_t rc = check_config(cfg);
+    if (rc != LQ_OK) return rc;
+    if (state == nullptr || !aligned(state, kSectionAlign)) return LQ_EINVAL;
+    lq_layout L;
+    compute_layout(*cfg, L);
+    return hip_status(launch_clear_status((uint32_t*)((char*)state + L.status), stream));
 }
 
 const char* lq_strerror(int32_t code) {

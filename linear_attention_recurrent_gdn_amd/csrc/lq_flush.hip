@@ -53,7 +53,6 @@
 // combine the wavefronts through LDS in a fixed order, so results are
 // deterministic.
 
-#include <atomic>
 #include "lq_internal.h"
 
 namespace lq {
@@ -193,6 +192,19 @@ __device__ __forceinline__ uint32_t e4m3_code(double x) {
         m = (uint32_t)(k - 8);
     }
     return (x < 0.0 ? 0x80u : 0u) | (e << 3) | m;
+}
+
+__device__ __forceinline__ bool finite4(const float4& f) {
+    return __builtin_isfinite(f.x) && __builtin_isfinite(f.y) && __builtin_isfinite(f.z) &&
+           __builtin_isfinite(f.w);
+}
+
+// Raise LQ_DEV_NONFINITE_INPUT when any lane of the wavefront saw a NaN or
+// Inf (rare: a uniform branch around one atomic).
+__device__ __forceinline__ void flag_nonfinite(uint32_t* status, bool bad) {
+    if (__builtin_expect(__any(bad), 0)) {
+        if (lane_id() == 0) atomicOr(status, (uint32_t)LQ_DEV_NONFINITE_INPUT);
+    }
 }
 
 __device__ __forceinline__ float pick4(const float4& f, int i) {
@@ -413,9 +425,13 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 
         v4d T[NB];
         if constexpr (!kFromCodes) {
+            bool bad = false;
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NB; ++b) {
                 T[b] = v4d{(double)sv[b].x, (double)sv[b].y, (double)sv[b].z, (double)sv[b].w};
+                bad = bad || !finite4(sv[b]);
+            }
+            flag_nonfinite(a.blob.status, bad);  // a NaN or Inf in the caller's start state
         } else {
             const double sgr = (double)sgr_f;
             const bool e4m3 = a.dm.code_format == LQ_CODE_E4M3;
@@ -518,6 +534,13 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             const int i0 = c * EB;
             const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
             const int qb = c & 1;  // chunk parity: keys, queries (prefill), running gate (channel)
+            if constexpr (PF) {
+                // a NaN or Inf in the prompt
+                bool bad = !finite4(pf.k) || !finite4(pf.v) || !finite4(pfq) ||
+                           !__builtin_isfinite(pf.b) || !__builtin_isfinite(pf.al);
+                if constexpr (KDA) bad = bad || !finite4(pf.g);
+                flag_nonfinite(a.blob.status, bad);
+            }
             {
                 const int x = 4 * tid;
                 const int e = x / D, col = x % D;
@@ -1067,10 +1090,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             }
         }
         }
-        if (tid == 0) {
-            a.blob.fill[u] = 0;
-            if ((MODE == kModeInit || PF) && u == 0) *a.blob.status = 0u;
-        }
+        if (tid == 0) a.blob.fill[u] = 0;
         __syncthreads();  // LDS is reused by the next unit
     }
 }
@@ -1150,25 +1170,16 @@ __global__ __launch_bounds__(1024) void due_scan_kernel(MatArgs a) {
 __global__ void clear_status_kernel(uint32_t* status) { *status = 0u; }
 
 // Workgroups of `kernel` that the device holds at once: the size of a
-// persistent grid.  Cached per device and variant; 0 when the runtime cannot
-// say (the caller then falls back to a fixed size).
+// persistent grid, asked of the runtime at every launch (the library keeps no
+// state between calls); 0 when the runtime cannot say (the caller then falls
+// back to a fixed size).
 template <typename K>
-int resident_blocks(K kernel, int block, int variant) {
-    constexpr int kMaxDev = 64, kVariants = 16;
-    static std::atomic<int> cache[kMaxDev][kVariants];
-    int dev = 0;
+int resident_blocks(K kernel, int block) {
+    int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    const bool cacheable = dev >= 0 && dev < kMaxDev && variant >= 0 && variant < kVariants;
-    if (cacheable) {
-        const int c = cache[dev][variant].load(std::memory_order_relaxed);
-        if (c > 0) return c;
-    }
-    int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block, 0) != hipSuccess) return 0;
-    const int r = cus * (per > 0 ? per : 1);
-    if (cacheable && r > 0) cache[dev][variant].store(r, std::memory_order_relaxed);
-    return r;
+    return cus * (per > 0 ? per : 1);
 }
 
 hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, hipStream_t st) {
@@ -1178,19 +1189,24 @@ hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, 
     const int block_threads = kWave * d / 16;
     const dim3 block(block_threads);
     const bool kda = gate_kind == LQ_GATE_CHANNEL;
+    if (mode == kModeInit || mode == kModePrefill) {
+        // a new state starts with no flags; cleared before any unit can raise one
+        hipError_t e = launch_clear_status(a.blob.status, st);
+        if (e != hipSuccess) return e;
+    }
     if (mode == kModeFlush) {
         hipLaunchKernelGGL(due_scan_kernel, dim3(1), dim3(1024), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    auto grid_for = [&](auto kernel, int variant) {
-        int g = resident_blocks(kernel, block_threads, variant);
+    auto grid_for = [&](auto kernel) {
+        int g = resident_blocks(kernel, block_threads);
         if (g <= 0) g = 2048;
         return dim3(a.dm.n_units < g ? a.dm.n_units : g);
     };
 #define LQ_MAT(D_, K_, M_)                                                                              \
     hipLaunchKernelGGL((materialize_kernel<D_, K_, M_>),                                               \
-                       grid_for(materialize_kernel<D_, K_, M_>, ((D_ == 128) * 2 + (K_ ? 1 : 0)) * 4 + M_), \
+                       grid_for(materialize_kernel<D_, K_, M_>),                                \
                        block, 0, st, a)
 #define LQ_MAT_MODE(D_, K_)                                      \
     do {                                                         \

@@ -2,7 +2,9 @@
 oracle on one workload.
 
 Tolerances (the decode step's outputs are fp32; the oracle is fp64):
-  * outputs: relative L2 error of each decode call's outputs <= 1e-4;
+  * outputs: relative L2 error of each decode call's outputs <= 1e-4, both
+    over all checked units together and for every checked unit on its own
+    (the per-unit maximum is reported);
   * codes after each init / flush: identical, except neighbouring codes (1 LSB
     for INT8, one grid spacing for E4M3) where the oracle's unrounded value
     lies within 2^-10 of a spacing of their midpoint, in at most 0.01% of that
@@ -11,8 +13,9 @@ Tolerances (the decode step's outputs are fp32; the oracle is fp64):
     (n_c+1)-th line scores are within 1e-6 relative (then the GPU's choice is
     adopted and the oracle's quantizer re-run with it forced);
   * compensator vectors <= 1e-4 relative L2; scales and smoothing <= 1e-6 relative;
-  * dequantized state (with and without the buffer) <= 1e-4 relative L2
-    against the oracle's dequantization of the GPU's own stored state.
+  * dequantized state (with and without the buffer) <= 1e-4 relative L2,
+    over all checked units and per unit, against the oracle's dequantization
+    of the GPU's own stored state.
 After each init and flush the oracle adopts the GPU's stored state, so a
 permitted code difference never compounds.
 
@@ -49,6 +52,15 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / n) if n > 0 else float(np.linalg.norm(a - b))
 
 
+def unit_rel_l2(a, b) -> np.ndarray:
+    """Relative L2 error of each unit (leading axis) on its own."""
+    a = np.asarray(a, np.float64).reshape(len(a), -1)
+    b = np.asarray(b, np.float64).reshape(len(b), -1)
+    d = np.linalg.norm(a - b, axis=1)
+    n = np.linalg.norm(b, axis=1)
+    return np.where(n > 0, d / np.where(n > 0, n, 1.0), d)
+
+
 def config_of(wl: I.Workload) -> lq.Config:
     fmt = {"int8": lq.LQ_CODE_INT8, "e4m3": lq.LQ_CODE_E4M3}[wl.code_format]
     buf = {"fp32": lq.LQ_BUFFER_FP32, "fp16": lq.LQ_BUFFER_FP16}[wl.buffer_format]
@@ -59,8 +71,10 @@ def config_of(wl: I.Workload) -> lq.Config:
 @dataclasses.dataclass
 class Report:
     name: str
-    max_out_err: float = 0.0
+    max_out_err: float = 0.0         # worst decode call, all checked units together
+    max_unit_out_err: float = 0.0    # worst single unit in any decode call
     max_state_err: float = 0.0
+    max_unit_state_err: float = 0.0
     flushes: int = 0
     codes_checked: int = 0
     code_flips: int = 0
@@ -238,7 +252,12 @@ def run(wl: I.Workload, n_tokens: Optional[int] = None, checked: Optional[Sequen
                                       sel(pu["gate"]))
         err = rel_l2(o_chk, o_ref[0])
         assert err <= TOL_OUT, f"{wl.name}: decode token {t}: output rel-L2 {err}"
+        per = unit_rel_l2(o_chk, o_ref[0])
+        worst = int(np.argmax(per))
+        assert per[worst] <= TOL_OUT, \
+            f"{wl.name}: decode token {t}: unit {checked[worst]} output rel-L2 {per[worst]}"
         rep.max_out_err = max(rep.max_out_err, err)
+        rep.max_unit_out_err = max(rep.max_unit_out_err, float(per[worst]))
         rep.decode_calls += 1
         fill += 1
         # the stored low-bit state is read-only inside a window
@@ -247,12 +266,17 @@ def run(wl: I.Workload, n_tokens: Optional[int] = None, checked: Optional[Sequen
 
         if dequant_every and (t % dequant_every == dequant_every - 1):
             lq.lq_dequant_state(cfg, state, S_out, include_buffer=True)
-            e1 = rel_l2(S_out.index_select(0, chk_dev).cpu().numpy(), S_hat)
+            g1 = S_out.index_select(0, chk_dev).cpu().numpy()
+            e1, p1 = rel_l2(g1, S_hat), unit_rel_l2(g1, S_hat).max()
             lq.lq_dequant_state(cfg, state, S_out, include_buffer=False)
-            e0 = rel_l2(S_out.index_select(0, chk_dev).cpu().numpy(),
-                        orc.dequant(blob_host(views, checked, wl.code_format)))
+            g0 = S_out.index_select(0, chk_dev).cpu().numpy()
+            r0 = orc.dequant(blob_host(views, checked, wl.code_format))
+            e0, p0 = rel_l2(g0, r0), unit_rel_l2(g0, r0).max()
             assert max(e0, e1) <= TOL_STATE, f"{wl.name}: dequantized state at token {t}: {e0}, {e1}"
+            assert max(p0, p1) <= TOL_STATE, \
+                f"{wl.name}: dequantized state at token {t}: worst unit {p0}, {p1}"
             rep.max_state_err = max(rep.max_state_err, e0, e1)
+            rep.max_unit_state_err = max(rep.max_unit_state_err, float(p0), float(p1))
 
         force_seq = np.zeros(wl.n_seq, np.uint8)
         if sched is not None:
@@ -274,7 +298,9 @@ def run(wl: I.Workload, n_tokens: Optional[int] = None, checked: Optional[Sequen
             frozen = None
     flags = lq.lq_read_status(cfg, state)
     assert flags == 0, f"{wl.name}: device flags {flags:#x}"
-    print(f"[parity] {wl.name}: ok max_out_err={rep.max_out_err:.3g} flushes={rep.flushes} "
+    print(f"[parity] {wl.name}: ok max_out_err={rep.max_out_err:.3g} "
+          f"max_unit_out_err={rep.max_unit_out_err:.3g} max_unit_state_err={rep.max_unit_state_err:.3g} "
+          f"flushes={rep.flushes} "
           f"flips={rep.code_flips}/{rep.codes_checked} ambiguous={rep.ambiguous_selections}",
           flush=True)
     return rep

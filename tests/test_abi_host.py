@@ -115,7 +115,10 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert lib.lq_decode_step(ctypes.byref(c), *a, None) == lq.LQ_EINVAL
     assert lib.lq_window_flush(ctypes.byref(c), None, None, None) == lq.LQ_EINVAL
     assert lib.lq_dequant_state(ctypes.byref(c), ok, None, 0, None) == lq.LQ_EINVAL
-    assert lib.lq_read_status(ctypes.byref(c), ok, None, 0, None) == lq.LQ_EINVAL
+    assert lib.lq_read_status(ctypes.byref(c), ok, None, None) == lq.LQ_EINVAL
+    assert lib.lq_read_status(ctypes.byref(c), None, ctypes.byref(ctypes.c_uint32()), None) == lq.LQ_EINVAL
+    assert lib.lq_clear_status(ctypes.byref(c), None, None) == lq.LQ_EINVAL
+    assert lib.lq_clear_status(ctypes.byref(c), P((1 << 20) + 16), None) == lq.LQ_EINVAL
     # prefill: a negative prompt length, a missing input for a non-empty prompt,
     # misaligned pointers; an empty prompt needs no inputs (then it is an init)
     assert lib.lq_prefill(ctypes.byref(c), ok, None, -1, ok, ok, ok, ok, ok, ok, None) == lq.LQ_EINVAL

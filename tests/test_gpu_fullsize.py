@@ -45,3 +45,39 @@ def test_fullsize_parity_hybrid_stack_layer(layer):
     rep = parity.run(wl, n_tokens=wl.decode, checked=sample_units(wl, 16), layer=layer,
                      dequant_every=33)
     assert rep.flushes == 1
+
+
+@pytest.mark.parametrize("name,layer", [("gdn_decode", 0), ("kda_decode", 0), ("hybrid_stack", 0)])
+def test_fp32_kernel_fullsize_sampled(name, layer):
+    # the FP32-state comparison kernel at the full launch size the benchmark
+    # times (every unit of the workload in one launch), its outputs and states
+    # followed unit by unit on a sample against the oracle's plain recurrence
+    import linear_attention_recurrent_gdn_amd as lq
+    import oracle as orc
+
+    wl = I.WORKLOADS[name]
+    cfg = parity.config_of(wl)
+    U, d = wl.n_units, wl.d
+    checked = np.asarray(sample_units(wl, 16))
+    gen = torch.Generator("cuda").manual_seed(11)
+    S = torch.randn((U, d, d), device="cuda", generator=gen) * 0.5
+    chk = torch.as_tensor(checked, device="cuda")
+    S_ref = S.index_select(0, chk).double().cpu().numpy()
+    src = parity.TokenSource(wl, layer)
+    o = torch.empty((wl.n_seq, wl.n_v_heads, d), device="cuda")
+    worst = 0.0
+    for t in range(6):
+        tk = src.token(t)
+        dev = {k: torch.from_numpy(v).cuda() for k, v in tk.items()}
+        lq.lq_fp32_decode_step(cfg, S, dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], o)
+        pu = I.tokens_per_unit(wl, {k: v[None] for k, v in tk.items()})
+        sel = lambda a: np.ascontiguousarray(a[:, checked])
+        S_ref, o_ref = orc.recurrence(S_ref, sel(pu["q"]), sel(pu["k"]), sel(pu["v"]), sel(pu["beta"]),
+                                      sel(pu["gate"]))
+        per = parity.unit_rel_l2(o.view(U, d).index_select(0, chk).cpu().numpy(), o_ref[0])
+        assert per.max() <= 1e-5, (t, checked[int(np.argmax(per))], per.max())
+        worst = max(worst, float(per.max()))
+    per_s = parity.unit_rel_l2(S.index_select(0, chk).cpu().numpy(), S_ref)
+    assert per_s.max() <= 1e-5, per_s.max()
+    print(f"[fp32 kernel] {name}: {U} units per launch, {len(checked)} followed, worst unit output "
+          f"rel-L2 {worst:.3g}, state {per_s.max():.3g}", flush=True)

@@ -310,3 +310,42 @@ def test_checkpoint_mid_window_resumes_bitwise(buffer):
     va, vb = lq.state_views(cfg, st), lq.state_views(cfg, restored)
     for key in ("fill", "codes", "sigma", "smooth", "comp_idx", "comp_vec", "buf_k", "buf_v"):
         assert torch.equal(va[key], vb[key]), key
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_nonfinite_start_state_and_prompt_set_flag(gate):
+    # a NaN or Inf in the start state (lq_state_init, lq_prefill) or in a prompt
+    # token (lq_prefill) raises LQ_DEV_NONFINITE_INPUT; a clean call starts
+    # from cleared flags
+    base = "gdn_decode" if gate == "scalar" else "kda_decode"
+    wl = small(base, name=f"nonfinite_{gate}", n_seq=2, n_v_heads=4, n_k_heads=2, window=8, n_comp=2,
+               prefill=0)
+    cfg = _cfg(wl)
+    U, d = wl.n_units, wl.d
+    st = lq.new_state(cfg)
+    gen = torch.Generator("cuda").manual_seed(4)
+    S0 = torch.randn((U, d, d), device="cuda", generator=gen)
+    lq.lq_state_init(cfg, st, S0)
+    assert lq.lq_read_status(cfg, st) == 0
+    bad = S0.clone()
+    bad[3, 17, 5] = float("nan")
+    lq.lq_state_init(cfg, st, bad)
+    assert lq.lq_read_status(cfg, st) == lq.LQ_DEV_NONFINITE_INPUT
+    lq.lq_state_init(cfg, st, S0)  # a new state: the flag is gone
+    assert lq.lq_read_status(cfg, st) == 0
+    bad[3, 17, 5] = float("inf")
+    lq.lq_prefill(cfg, st, bad, None, None, None, None, None)
+    assert lq.lq_read_status(cfg, st) == lq.LQ_DEV_NONFINITE_INPUT
+    T = 21
+    toks = I.tokens(wl, 0, T, I.PHASE_PREFILL)
+    x = {k: torch.from_numpy(v).cuda() for k, v in toks.items()}
+    o = torch.empty((T, wl.n_seq, wl.n_v_heads, d), device="cuda")
+    lq.lq_prefill(cfg, st, S0, x["q"], x["k"], x["v"], x["beta"], x["gate"], o)
+    assert lq.lq_read_status(cfg, st) == 0
+    for key, idx in (("v", (19, 1, 2, 7)), ("k", (5, 0, 1, 3)), ("beta", (17, 1, 3))):
+        y = {k: v.clone() for k, v in x.items()}
+        y[key][idx] = float("nan")
+        lq.lq_prefill(cfg, st, S0, y["q"], y["k"], y["v"], y["beta"], y["gate"], o)
+        assert lq.lq_read_status(cfg, st) == lq.LQ_DEV_NONFINITE_INPUT, key
+    lq.lq_clear_status(cfg, st)
+    assert lq.lq_read_status(cfg, st) == 0

@@ -44,6 +44,8 @@ MUTANTS = {
     "row_slot_to_column": ("for (int j = 0; j < dk; ++j) Su[(size_t)c * dk + j] += (double)cv[j];",
                            "for (int j = 0; j < dk && j < dv; ++j) Su[(size_t)j * dk + c] += (double)cv[j];"),
     "flush_one_early": ("if (fill == W || forced)", "if (fill == W - 1 || forced)"),
+    "smoothing_switch_ignored": ("if (smooth_enable && a > 0.0)", "if (a > 0.0)"),
+    "smoothing_switch_inverted": ("if (smooth_enable && a > 0.0)", "if (!smooth_enable && a > 0.0)"),
 }
 
 

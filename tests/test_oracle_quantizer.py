@@ -153,3 +153,19 @@ def test_golden_3x3_worked_example(orc, n_c):
     sig = [np.float32(int(a) / int(b)) for a, b in (r.split("/") for r in g[p + "sigma_ratio"])]
     np.testing.assert_array_equal(blob.sigma[0], np.array(sig, np.float32))
     assert blob.codes[0].ravel().tolist() == [int(x) for x in g[p + "codes"]]
+
+
+def test_golden_3x3_naive_ablation(orc):
+    # the naive per-token ablation's quantizer (no compensators, no smoothing)
+    # against the hand-worked values: s = 1, sigma = row absmax / 127
+    g = parse_golden("quantizer_3x3.txt")
+    S = np.array(g["S"], float).reshape(1, 3, 3)
+    blob, _, _ = orc.qz(S, 0, smooth=False)
+    assert blob.comp_idx.shape == (1, 0)
+    np.testing.assert_array_equal(blob.smooth[0], np.array(g["naive.smooth"], np.float32))
+    sig = [np.float32(int(a) / int(b)) for a, b in (r.split("/") for r in g["naive.sigma_ratio"])]
+    np.testing.assert_array_equal(blob.sigma[0], np.array(sig, np.float32))
+    assert blob.codes[0].ravel().tolist() == [int(x) for x in g["naive.codes"]]
+    # the same state with smoothing on differs (the ablation switch is live)
+    smoothed, _, _ = orc.qz(S, 0, smooth=True)
+    assert not np.array_equal(smoothed.smooth[0], blob.smooth[0])

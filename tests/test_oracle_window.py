@@ -158,3 +158,25 @@ def test_windowing_beats_per_token_quantization(orc):
     naive = orc.windowed_run(S0, q, k, v, b, g, W=1, n_c=0, smooth=False)
     err = lambda o: np.linalg.norm(o - ref) / np.linalg.norm(ref)
     assert err(lq) < err(naive)
+
+
+def test_golden_naive_per_token_2x2(orc):
+    # the naive per-token ablation (W = 1, no compensators, no smoothing) over
+    # two tokens, against the hand-worked run in the golden file
+    g = parse_golden("naive_per_token_2x2.txt")
+    S0 = np.array(g["S0"], float).reshape(1, 2, 2)
+    tok = lambda key, t, n: np.array(g[f"t{t}.{key}"], np.float32).reshape(n)
+    q = np.stack([tok("q", t, (1, 2)) for t in (1, 2)])
+    k = np.stack([tok("k", t, (1, 2)) for t in (1, 2)])
+    v = np.stack([tok("v", t, (1, 2)) for t in (1, 2)])
+    b = np.stack([tok("beta", t, (1,)) for t in (1, 2)])
+    a = np.stack([tok("alpha", t, (1,)) for t in (1, 2)])
+    o, S_end = orc.windowed_run(S0, q, k, v, b, a, W=1, n_c=0, smooth=False, want_state=True)
+    assert o[0, 0].tolist() == [float(x) for x in g["t1.o"]]
+    sig = [np.float32(float(x) / float(y)) for x, y in (r.split("/") for r in g["t1.sigma_ratio"])]
+    codes = [int(x) for x in g["t1.codes"]]
+    want_S1 = np.array([[codes[0] * float(sig[0]), codes[1] * float(sig[0])],
+                        [codes[2] * float(sig[1]), codes[3] * float(sig[1])]])
+    np.testing.assert_array_equal(S_end[0], want_S1)  # token 2 leaves the requantized state as is
+    c2 = [int(x) for x in g["t2.o_codes"]]
+    assert o[1, 0].tolist() == [c2[0] * float(sig[0]), c2[1] * float(sig[1])]
