@@ -3,24 +3,40 @@
 
 One step = one decode token for every (sequence, head) unit of every layer
 (lq_decode_step), plus the window-boundary requantization (lq_window_flush)
-for every unit whose window filled on that token.  Inputs are synthetic,
-seeded, and resident in HBM before the timed region starts.  The timed steps
-are captured as one HIP graph and replayed between HIP events (median of
---repeats replays), so the host's launch cost is not in the figure.  The same
-steps are then timed on the FP32-state comparison kernel.  --replicas R runs
-every step on R independent copies of the states in turn, which pushes a
-working set that would fit the 256 MB last-level cache out to HBM.
+of every layer whose units filled their window on that token.  Inputs are
+synthetic, seeded, and resident in HBM before the timed region starts.
+
+Steady state.  Windows are staggered so that any run of steps carries its
+share of boundary work and sees every fill position of the window: with
+several layers, layer l starts its windows floor(l W / L) tokens later than
+layer 0 (every layer flushes all its units once per W steps, at different
+steps); with one layer, sequences are split into G groups at offsets g W / G
+(G up to 8, each group at least 256 units, one per CU); a workload defined
+with per-sequence offsets (the serving step) keeps them.  A set-up phase of
+W untimed tokens (forced flushes) establishes the offsets, then --warmup
+untimed steps run, then --steps steps are timed.  The timed steps run as HIP
+graphs of --steps steps each, captured and replayed once per segment, for
+--repeats consecutive segments (HIP events around each replay); the median
+segment gives ms_per_step, so the host's launch cost is not in the figure.
+The same steps then run on the FP32-state comparison kernel.  --replicas R
+runs every step on R independent copies of the states in turn, which pushes
+a working set that would fit the 256 MB last-level cache out to HBM.
 
 Prints one JSON line:
-  value            unit-tokens/s (seq·head·tokens/s) of the INT8 path over the timed steps
-  roofline         the decode kernel's algorithmic bytes per launch / its average
-                   launch time (a graph of one window of decode launches, HIP events
-                   around the replay), against 8 TB/s; `practical` adds what a plain
-                   streaming-read kernel reaches on this device at the same bytes
-                   per launch (probe/stream_read, run after the timed region)
+  value            unit-tokens/s (seq.head.tokens/s, all layers) of the INT8 path,
+                   window-boundary requantization included
+  roofline         the decode kernel: algorithmic bytes per launch / its average
+                   launch time (a graph of one window of decode launches, every
+                   layer at fill 0 .. W-1, HIP events around the replay), against
+                   8 TB/s; `practical` adds what a plain streaming-read kernel
+                   reaches from HBM on this device at the same bytes per launch
+  flush            the boundary kernel alone (all units of a layer after a full
+                   window) and its FP64 matrix-core roofline (5 d^2 W flop per unit)
+  checks           ms_per_step against the decode launches it must contain, and
+                   the speedup against the byte-ratio ceiling
   fp32_state       the FP32-state kernel on the same steps, and the speedup
   cpu_baseline     the CPU oracle (FP64, definitional windowed form) on a bounded
-                   sample of the same workload, on this host's cores
+                   sample of the same workload: all host threads, and one thread
 """
 from __future__ import annotations
 
@@ -35,15 +51,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+LLC_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 METRIC = "seq·head·tokens/s decode; HBM GB/s vs peak; speedup vs FP32-state kernel"
 
 
-def parse_args():
+def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed decode tokens (default: the workload's)")
-    ap.add_argument("--warmup", type=int, default=None, help="untimed tokens first (default: one window)")
-    ap.add_argument("--workload", default="gdn_decode",
+    ap.add_argument("--steps", type=int, default=None, help="timed steps per segment (default: the workload's "
+                                                            "decode tokens)")
+    ap.add_argument("--warmup", type=int, default=8, help="untimed steps after the set-up phase")
+    ap.add_argument("--workload", default="hybrid_stack",
                     help="tiny_gdn | gdn_decode | kda_decode | gdn_serving | hybrid_stack")
     ap.add_argument("--window", type=int, default=None, help="override the workload's window W (1..256)")
     ap.add_argument("--n-comp", type=int, default=None, help="override the workload's compensator count (0..16)")
@@ -57,13 +75,13 @@ def parse_args():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip timing lq_prefill on the workload's prompt against the token-by-token FP32 kernel")
     ap.add_argument("--repeats", type=int, default=5,
-                    help="replays of the timed-steps graph, median reported (1 if the steps are not whole "
-                         "windows: only then does a replay restart the same fill pattern)")
+                    help="consecutive timed segments of --steps steps, each one HIP graph replayed once; "
+                         "the median is reported")
     ap.add_argument("--replicas", type=int, default=1,
                     help="independent copies of every state, each token run on every copy in turn: with "
                          "enough copies the working set exceeds the 256 MB last-level cache, so every launch "
                          "reads its state from HBM (throughput counts the units of all copies)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 # ---------------------------------------------------------------------------
@@ -137,40 +155,108 @@ def projected(wl, w, h):
 
 
 # ---------------------------------------------------------------------------
+# staggered windows: the host mirror of every (layer, sequence)'s fill count
+# ---------------------------------------------------------------------------
+
+def stagger_groups(wl) -> int:
+    """Groups of sequences at distinct window offsets in a one-layer workload:
+    the most (up to 8) that divide the window and the sequences and leave at
+    least 256 units (one per CU) to each group's boundary launch."""
+    for G in (8, 4, 2):
+        if wl.window % G == 0 and wl.n_seq % G == 0 and wl.n_units // G >= 256:
+            return G
+    return 1
+
+
+def window_offsets(wl, n_layers):
+    """Fill count [layer, sequence] after the set-up phase (the window offsets)."""
+    import numpy as np
+
+    W, S = wl.window, wl.n_seq
+    if wl.stagger:  # the workload's own per-sequence offsets
+        return np.tile(np.arange(S) % W, (n_layers, 1))
+    if n_layers > 1:  # layer l starts its windows floor(l W / L) tokens later
+        return np.repeat(((np.arange(n_layers) * W) // n_layers)[:, None], S, axis=1)
+    G = stagger_groups(wl)
+    return ((np.arange(S) % G) * (W // G))[None, :]
+
+
+class Schedule:
+    """Host mirror of the window fill of every (layer, sequence).  step()
+    advances one token and returns, for each layer that needs a boundary call,
+    (layer, per-sequence force mask or None, sequences due).  During the
+    set-up phase (token index given) sequence s of layer l is force-flushed
+    after token W - 1 - offset, so it ends the phase `offset` tokens into a
+    window; later steps flush only full windows."""
+
+    def __init__(self, wl, n_layers):
+        import numpy as np
+
+        self.W = wl.window
+        self.offsets = window_offsets(wl, n_layers)
+        self.fill = np.zeros((n_layers, wl.n_seq), np.int64)
+        self.force_at = np.where(self.offsets == 0, -1, self.W - 1 - self.offsets)
+
+    def step(self, setup_token=None):
+        self.fill += 1
+        out = []
+        for layer in range(self.fill.shape[0]):
+            f = self.fill[layer]
+            forced = (self.force_at[layer] == setup_token) if setup_token is not None else None
+            due = f >= self.W
+            if forced is not None:
+                due = due | (forced & (f > 0))
+            if due.any():
+                out.append((layer, forced if (forced is not None and forced.any()) else None, int(due.sum())))
+                f[due] = 0
+        return out
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl, n_tok, target_s, fmt="int8", buffer="fp32"):
+def cpu_baseline(wl, target_s, fmt="int8", buffer="fp32", single_thread_s=4.0):
+    """The oracle's definitional windowed form (FP64) over one whole window of
+    W decode tokens per unit, its boundary requantization included, on a
+    sample of units sized to about target_s seconds on all host threads, then
+    on one thread (about single_thread_s seconds)."""
     import numpy as np
 
     import oracle as orc
     from linear_attention_recurrent_gdn_amd import inputs as I
 
     src = wl.scaled(projected=False) if wl.projected else wl
+    n_tok = wl.window  # one window and its boundary
 
-    def sample(units, n):
-        st = I.prefill_streams(src, units, n=n, phase=I.PHASE_DECODE, with_queries=True)
+    def sample(units):
+        st = I.prefill_streams(src, units, n=n_tok, phase=I.PHASE_DECODE, with_queries=True)
         S0 = I.surrogate_state(src, units).astype(np.float64)
         return S0, st
 
-    # calibrate on a few units, then size the sample for about target_s seconds
-    cal_units = list(range(min(2 * orc.num_threads(), wl.n_units)))
-    cal_tok = min(n_tok, 2 * wl.window)
-    S0, st = sample(cal_units, cal_tok)
-    t0 = time.perf_counter()
-    orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp, fmt=fmt,
-                     buffer=buffer)
-    rate = len(cal_units) * cal_tok / max(time.perf_counter() - t0, 1e-6)
+    def timed(units, reps=1):
+        S0, st = sample(units)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp,
+                             fmt=fmt, buffer=buffer)
+        return time.perf_counter() - t0
+
+    threads = orc.num_threads()
+    cal_units = list(range(min(2 * threads, wl.n_units)))
+    rate = len(cal_units) * n_tok / max(timed(cal_units), 1e-6)
     n_units = int(max(1, min(wl.n_units, rate * target_s / n_tok)))
-    # the whole workload may take well under target_s: repeat it to get a steady figure
     reps = int(max(1, min(20, round(rate * target_s / (n_units * n_tok)))))
     units = np.linspace(0, wl.n_units - 1, n_units).astype(int)
-    S0, st = sample(units, n_tok)
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp, fmt=fmt,
-                         buffer=buffer)
-    dt = time.perf_counter() - t0
+    dt = timed(units, reps)
+    value = reps * n_units * n_tok / dt
+    # one thread, on a smaller sample
+    orc.set_num_threads(1)
+    try:
+        n1 = int(max(1, min(n_units, value / threads * single_thread_s / n_tok)))
+        dt1 = timed(units[:n1])
+    finally:
+        orc.set_num_threads(threads)
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -178,12 +264,14 @@ def cpu_baseline(wl, n_tok, target_s, fmt="int8", buffer="fp32"):
     except Exception:
         pass
     return {
-        "value": reps * n_units * n_tok / dt,
+        "value": value,
         "unit": "seq·head·tokens/s",
-        "cores": orc.num_threads(),
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"{n_units} of {wl.n_units} units x {n_tok} decode tokens (flushes included) x {reps} passes, "
-                   f"FP64 definitional windowed form, {dt:.1f} s; input generation excluded; "
+        "single_thread_value": n1 * n_tok / dt1,
+        "sample": (f"{n_units} of {wl.n_units} units x one window of {n_tok} decode tokens with its boundary "
+                   f"requantization x {reps} passes on {threads} threads ({dt:.1f} s); one thread: {n1} units, "
+                   f"{dt1:.1f} s; FP64 definitional windowed form, input generation excluded; "
                    f"host CPU: {cpu_model}"),
     }
 
@@ -286,8 +374,30 @@ def measured_traffic(workload, fmt="int8", buffer="fp32"):
 
 # ---------------------------------------------------------------------------
 
-def main():
-    args = parse_args()
+def timed_graph(torch, stream, body, repeats=1):
+    """Capture body() as one HIP graph, replay it `repeats` times, each between
+    HIP events on `stream`; the median replay time (ms)."""
+    import numpy as np
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        body()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(1, repeats)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del g
+    return float(np.median(times))
+
+
+def main(argv=None):
+    args = parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); units shard across GPUs with no exchange, "
@@ -307,22 +417,26 @@ def main():
     if args.n_comp is not None:
         wl = wl.scaled(n_comp=args.n_comp)
     wl = wl.scaled(code_format=args.format, buffer_format=args.buffer)
-    W, U, L, d = wl.window, wl.n_units, wl.layers, wl.d
-    steps = wl.decode if args.steps is None else args.steps
-    warmup = W if args.warmup is None else args.warmup
+    W, U, L, d, H = wl.window, wl.n_units, wl.layers, wl.d, wl.n_v_heads
+    K = wl.decode if args.steps is None else args.steps
+    warmup = max(0, args.warmup)
+    n_seg = max(1, args.repeats)
+    R = max(1, args.replicas)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)  # default priority
+    torch.cuda.set_stream(stream)
     gen = torch.Generator(dev).manual_seed(1000 + wl.seed)
     code_format = {"int8": lq.LQ_CODE_INT8, "e4m3": lq.LQ_CODE_E4M3}[args.format]
     buffer_format = {"fp32": lq.LQ_BUFFER_FP32, "fp16": lq.LQ_BUFFER_FP16}[args.buffer]
     cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind, code_format,
                     buffer_format)
-    stream = torch.cuda.current_stream()
+    t_setup = time.perf_counter()
 
     # ---- start states: FP32 prefill through the FP32-state kernel (input synthesis)
     weights = [projection_weights(wl, gen, dev) for _ in range(L)] if wl.projected else [None] * L
     S_fp32, states = [], []
-    o = torch.empty((wl.n_seq, wl.n_v_heads, d), device=dev)
+    o = torch.empty((wl.n_seq, H, d), device=dev)
     for layer in range(L):
         S = torch.zeros((U, d, d), device=dev)
         for tk in device_tokens(wl, wl.prefill, layer, gen, dev, weights[layer]):
@@ -335,75 +449,72 @@ def main():
         lq.lq_state_init(cfg, st, S)
         states.append(st)
         S_fp32.append(S)
-    R = max(1, args.replicas)
     blobs = [[st] + [st.clone() for _ in range(R - 1)] for st in states]  # [layer][copy]
     if not args.no_fp32:
         S_fp32 = [[S] + [S.clone() for _ in range(R - 1)] for S in S_fp32]
-    n_tok = warmup + steps
-    toks = [device_tokens(wl, n_tok, layer, gen, dev, weights[layer]) for layer in range(L)]
+    else:
+        del S_fp32
+    # decode inputs: a pool of tokens per layer, step t uses token t mod pool
+    n_pool = min(W + warmup + n_seg * K, 32)
+    pool = [device_tokens(wl, n_pool, layer, gen, dev, weights[layer]) for layer in range(L)]
+    tok = lambda layer, t: pool[layer][t % n_pool]
     torch.cuda.synchronize()
 
-    sched = I.stagger_schedule(wl)
-    fill = np.zeros(wl.n_seq, np.int64)
+    sched = Schedule(wl, L)
     force_dev = torch.zeros(wl.n_seq, dtype=torch.uint8, device=dev)
-    flush_calls = []
+    acct = {"decode_bytes": 0.0, "flush_bytes": 0.0, "flush_calls": 0, "flushed_units": 0, "decode_launches": 0}
 
-    def q8_step(t):
+    def q8_step(t, setup_token=None):
         for layer in range(L):
-            tk = toks[layer][t]
+            tk = tok(layer, t)
+            fills = sched.fill[layer]
+            acct["decode_bytes"] += R * H * float(sum(decode_bytes(wl, int(j)) for j in fills))
+            acct["decode_launches"] += R
             for st in blobs[layer]:
                 lq.lq_decode_step(cfg, st, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
-        fill[:] += 1
-        forced = (sched == t) if (sched is not None and t < warmup) else np.zeros(wl.n_seq, bool)
-        due = (fill >= W) | (forced & (fill > 0))
-        if due.any():
+        for layer, forced, n_due in sched.step(setup_token):
             fm = None
-            if forced.any():
+            if forced is not None:
                 force_dev.copy_(torch.from_numpy(forced.astype(np.uint8)))
                 fm = force_dev
-            for layer in range(L):
-                for st in blobs[layer]:
-                    lq.lq_window_flush(cfg, st, fm)
-            flush_calls.append(int(due.sum()) * wl.n_v_heads)
-            fill[due] = 0
+            for st in blobs[layer]:
+                lq.lq_window_flush(cfg, st, fm)
+            acct["flush_calls"] += R
+            acct["flushed_units"] += R * H * n_due
+            acct["flush_bytes"] += R * H * n_due * flush_bytes(wl, W)
 
-    def timed_graph(body, repeats=1):
-        """Capture body() as one HIP graph, replay it `repeats` times, each between
-        HIP events; the median replay time (ms)."""
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            body()
-        torch.cuda.synchronize()
-        times = []
-        for _ in range(max(1, repeats)):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            g.replay()
-            b.record(stream)
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b))
-        del g
-        return float(np.median(times))
-
-    for t in range(warmup):
+    # ---- set-up phase (window offsets), then warm-up: untimed
+    for t in range(W):
+        q8_step(t, setup_token=t)
+    assert (sched.fill == sched.offsets).all()
+    for t in range(W, W + warmup):
         q8_step(t)
-    n_flush_warm = len(flush_calls)
-    # the timed steps run as one graph: kernels back to back, no host launch cost
-    repeats = args.repeats if steps % W == 0 else 1
-    q8_ms = timed_graph(lambda: [q8_step(t) for t in range(warmup, n_tok)], repeats)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    # ---- timed: n_seg consecutive segments of K steps, one graph each, replayed once
+    for key in acct:
+        acct[key] = 0
+    t0 = W + warmup
+    seg_ms = []
+    for r in range(n_seg):
+        a = t0 + r * K
+        seg_ms.append(timed_graph(torch, stream, lambda: [q8_step(t) for t in range(a, a + K)]))
+    ms_seg = float(np.median(seg_ms))
     flags = [lq.lq_read_status(cfg, st) for bl in blobs for st in bl]
     if any(flags):
         raise RuntimeError(f"device flags set during the run: {flags}")
-
+    steps_timed = n_seg * K
+    units_step = U * L * R
+    ws_bytes = L * R * lq.lq_state_bytes(cfg)
     result = {
         "metric": METRIC,
-        "value": U * L * R * steps / (q8_ms * 1e-3),
+        "value": units_step * K / (ms_seg * 1e-3),
         "unit": "seq·head·tokens/s",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": K,
         "warmup": warmup,
-        "ms_per_step": q8_ms / steps,
+        "ms_per_step": ms_seg / K,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -412,25 +523,65 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name,
-            "layers": L, "n_seq": wl.n_seq, "n_v_heads": wl.n_v_heads, "n_k_heads": wl.n_k_heads,
+            "layers": L, "n_seq": wl.n_seq, "n_v_heads": H, "n_k_heads": wl.n_k_heads,
             "d_k": d, "d_v": d, "gate": wl.gate, "window": W, "n_comp": wl.n_comp,
             "code_format": args.format, "buffer_format": args.buffer,
-            "prefill": wl.prefill, "units": U * L * R, "state_copies": R,
+            "prefill": wl.prefill, "units": units_step, "state_copies": R,
+            "state_bytes": ws_bytes,
+            "residency": ("hbm" if ws_bytes > 2 * LLC_BYTES else
+                          "cache (the states fit the 256 MB last-level cache; --replicas pushes them to HBM)"),
         },
-        "timing": f"HIP graph of the timed steps, median of {repeats} replays, HIP events around each",
+        "timing": (f"{n_seg} consecutive segments of {K} steps after {W} set-up and {warmup} warm-up steps; "
+                   f"each segment one HIP graph replayed once between HIP events; median segment "
+                   f"({', '.join(f'{x:.3f}' for x in seg_ms)} ms); windows staggered "
+                   + ("per sequence (the workload's offsets)" if wl.stagger else
+                      f"across layers (layer l offset floor(l*{W}/{L}))" if L > 1 else
+                      f"over {stagger_groups(wl)} sequence groups")
+                   + ", so the timed steps carry their share of boundary requantization"),
+        "timed_steps": {
+            "decode_launches": acct["decode_launches"],
+            "flush_calls": acct["flush_calls"],
+            "flushed_units": acct["flushed_units"],
+            "flushed_units_per_step": acct["flushed_units"] / steps_timed,
+            "flush_share_expected_per_step": units_step / W,
+            "alg_bytes_per_step": (acct["decode_bytes"] + acct["flush_bytes"]) / steps_timed,
+            "alg_GBps": (acct["decode_bytes"] + acct["flush_bytes"]) / steps_timed / (ms_seg / K * 1e-3) / 1e9,
+        },
+        "setup_s": round(setup_s, 1),
     }
 
-    # ---- the decode kernel alone over one whole window (every unit at j = 0 .. W-1),
-    # replayed as a graph: its average launch time against its algorithmic bytes
+    # ---- FP32-state comparison on the same steps
+    fp32 = None
+    if not args.no_fp32:
+        def fp32_steps(ta, tb):
+            for t in range(ta, tb):
+                for layer in range(L):
+                    tk = tok(layer, t)
+                    for S in S_fp32[layer]:
+                        lq.lq_fp32_decode_step(cfg, S, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+        fp32_steps(0, warmup)
+        fp32_ms = timed_graph(torch, stream, lambda: fp32_steps(t0, t0 + K), n_seg)
+        g = d if wl.gate == "channel" else 1
+        fp32_b = 8 * d * d + 4 * (2 * d // wl.group + 2 * d + 1 + g)
+        fp32 = {
+            "value": units_step * K / (fp32_ms * 1e-3),
+            "ms_per_step": fp32_ms / K,
+            "alg_GBps": units_step * fp32_b / (fp32_ms / K * 1e-3) / 1e9,
+            "speedup_vs_fp32": fp32_ms / ms_seg,
+        }
+        result["fp32_state"] = fp32
+        del S_fp32
+
+    # ---- the decode kernel alone over one whole window (every layer at fill
+    # 0 .. W-1), as one graph: its average launch time against its bytes
     all_seq = torch.ones(wl.n_seq, dtype=torch.uint8, device=dev)
     for bl in blobs:
         for st in bl:
             lq.lq_window_flush(cfg, st, all_seq)  # forced: every window restarts empty
-    win_tok = [t % n_tok for t in range(W)]
-    dec_ms = timed_graph(lambda: [lq.lq_decode_step(cfg, st, toks[layer][t]["q"], toks[layer][t]["k"],
-                                                    toks[layer][t]["v"], toks[layer][t]["beta"],
-                                                    toks[layer][t]["gate"], o)
-                                  for t in win_tok for layer in range(L) for st in blobs[layer]])
+    dec_ms = timed_graph(torch, stream, lambda: [lq.lq_decode_step(cfg, st, tok(layer, j)["q"], tok(layer, j)["k"],
+                                                                    tok(layer, j)["v"], tok(layer, j)["beta"],
+                                                                    tok(layer, j)["gate"], o)
+                                                  for j in range(W) for layer in range(L) for st in blobs[layer]])
     n_launch = W * L * R
     avg_launch_s = dec_ms * 1e-3 / n_launch
     avg_bytes = float(np.mean([decode_bytes(wl, j) for j in range(W)])) * U
@@ -446,36 +597,47 @@ def main():
         "avg_launch_us": avg_launch_s * 1e6,
         "alg_bytes_per_launch": avg_bytes,
         "launches": n_launch,
-        "note": "one graph of one window of decode launches (j = 0..W-1), events around the replay",
+        "note": "one graph of one window of decode launches (every layer and copy at j = 0..W-1), HIP events "
+                "around the replay on the launch stream; bytes = the mean over j of the per-unit model x units",
     }
-    # flush alone: one forced boundary of every unit after a full window
-    fl_ms = timed_graph(lambda: [lq.lq_window_flush(cfg, blobs[layer][0], None) for layer in range(L)])
+    # ---- the boundary kernel alone: every unit of a layer after a full window
+    fl_ms = timed_graph(torch, stream, lambda: [lq.lq_window_flush(cfg, blobs[layer][0], None) for layer in range(L)])
+    fl_s = fl_ms * 1e-3 / L
+    flops = 5.0 * d * d * W * U
     result["flush"] = {
-        "avg_launch_us": fl_ms * 1e3 / L,
+        "avg_launch_us": fl_s * 1e6,
         "units_per_launch": U,
         "tokens_replayed": W,
-        "timed_steps_flushes": len(flush_calls) - n_flush_warm,
+        "alg_GBps": flush_bytes(wl, W) * U / fl_s / 1e9,
+        "roofline": {"bound": "mfma", "achieved": flops / fl_s / 1e12, "peak": PEAK_FP64_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops / fl_s / 1e12 / PEAK_FP64_MFMA_TFLOPS,
+                     "dtype": "f64", "flops_per_unit": 5.0 * d * d * W,
+                     "kernel": "materialize_kernel (flush mode) + due_scan_kernel",
+                     "note": "5 d^2 W flop per unit (the window transform's products); one launch per layer "
+                             "over all its units, HIP events around a graph of the layers' launches"},
     }
 
-    if not args.no_fp32:
-        def fp32_steps(t_from, t_to):
-            for t in range(t_from, t_to):
-                for layer in range(L):
-                    tk = toks[layer][t]
-                    for S in S_fp32[layer]:
-                        lq.lq_fp32_decode_step(cfg, S, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
-        fp32_steps(0, warmup)
-        fp32_ms = timed_graph(lambda: fp32_steps(warmup, n_tok), repeats)
-        fp32_bytes = U * L * R * (8 * d * d + 4 * (2 * d // wl.group + 2 * d + 1 + (d if wl.gate == "channel" else 1)))
-        result["fp32_state"] = {
-            "value": U * L * R * steps / (fp32_ms * 1e-3),
-            "ms_per_step": fp32_ms / steps,
-            "alg_GBps": fp32_bytes / (fp32_ms / steps * 1e-3) / 1e9,
-            "speedup_vs_fp32": fp32_ms / q8_ms,
-        }
+    # ---- self-checks
+    dec_floor_ms = L * R * avg_launch_s * 1e3
+    checks = {
+        "decode_launches_ms_per_step": dec_floor_ms,
+        "ms_per_step_over_decode_launches": (ms_seg / K) / dec_floor_ms,
+        "ms_per_step_at_least_decode_launches": bool(ms_seg / K >= 0.97 * dec_floor_ms),
+        # the boundary work per step if its time scaled with the units flushed
+        "flush_model_ms_per_step": (acct["flushed_units"] / steps_timed) / U * fl_s * 1e3,
+    }
+    if fp32 is not None:
+        int8_b = result["timed_steps"]["alg_bytes_per_step"]
+        g = d if wl.gate == "channel" else 1
+        fp32_step_b = units_step * (8 * d * d + 4 * (2 * d // wl.group + 2 * d + 1 + g))
+        ceiling = fp32_step_b / int8_b
+        checks["byte_ratio_ceiling"] = ceiling
+        checks["speedup_over_ceiling"] = fp32["speedup_vs_fp32"] / ceiling
+    result["checks"] = checks
 
-    if not args.no_prefill and wl.prefill > 0 and not wl.projected and L == 1:
-        result["prefill"] = prefill_timing(lq, wl, cfg, gen, dev, timed_graph)
+    if not args.no_prefill and wl.prefill > 0 and not wl.projected and L == 1 and R == 1:
+        result["prefill"] = prefill_timing(lq, wl, cfg, gen, dev,
+                                           lambda body, reps=1: timed_graph(torch, stream, body, reps))
 
     # the practical ceiling at the decode launch's byte count (a child process;
     # the device is idle here)
@@ -483,13 +645,14 @@ def main():
     pr = practical_read(avg_bytes)
     if pr is not None:
         result["roofline"]["practical"] = {
-            "kernel": "stream_read (probe/stream_read.hip): 16-byte loads, grid-stride, nothing else",
+            "kernel": "stream_read (probe/stream_read.hip): 16-byte loads, grid-stride, nothing else; "
+                      "consecutive launches read disjoint regions of a >= 2 GiB pool (HBM, not the cache)",
             "bytes_per_launch": avg_bytes, "achieved": pr["GBps"], "unit": "GB/s",
             "frac_of_peak": pr["GBps"] / HBM_PEAK_GBS, "decode_frac_of_practical": achieved / pr["GBps"],
         }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, steps, args.cpu_seconds, args.format, args.buffer)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, args.format, args.buffer)
     print(json.dumps(result), flush=True)
 
 

@@ -51,3 +51,40 @@ def test_decode_bytes_grow_by_one_entry_per_token(name):
     wl = I.WORKLOADS[name]
     step = [bench.decode_bytes(wl, j + 1) - bench.decode_bytes(wl, j) for j in range(wl.window - 1)]
     assert len(set(step)) == 1 and step[0] > 0
+
+
+@pytest.mark.parametrize("name,layers", [("gdn_decode", 1), ("kda_decode", 1), ("gdn_serving", 1),
+                                         ("hybrid_stack", 36), ("tiny_gdn", 1)])
+def test_staggered_schedule_reaches_offsets_and_spreads_flushes(name, layers):
+    # the set-up phase ends with every (layer, sequence) at its offset; after
+    # it, every window of W consecutive steps flushes every unit exactly once,
+    # and any K consecutive steps flush K/W of the units, within one group
+    import numpy as np
+
+    wl = I.WORKLOADS[name]
+    sch = bench.Schedule(wl, layers)
+    W = wl.window
+    for t in range(W):
+        sch.step(setup_token=t)
+    assert (sch.fill == sch.offsets).all()
+    flushed = []
+    for t in range(3 * W):
+        calls = sch.step()
+        assert all(forced is None for _, forced, _ in calls)  # after set-up only full windows flush
+        flushed.append(sum(n_due for _, _, n_due in calls))
+    flushed = np.array(flushed)
+    for t in range(0, 2 * W):
+        assert flushed[t:t + W].sum() == layers * wl.n_seq  # each sequence of each layer once per window
+    groups = layers if layers > 1 else (W if wl.stagger else bench.stagger_groups(wl))
+    per_group = layers * wl.n_seq // groups if layers == 1 else wl.n_seq
+    for K in (5, 20, 64):
+        for t in range(0, W):
+            share = flushed[t:t + K].sum()
+            assert abs(share - K * layers * wl.n_seq / W) <= per_group, (K, t, share)
+
+
+def test_stagger_groups_leave_a_unit_per_cu():
+    for name in ("gdn_decode", "kda_decode"):
+        wl = I.WORKLOADS[name]
+        G = bench.stagger_groups(wl)
+        assert G > 1 and wl.n_units // G >= 256 and wl.window % G == 0
