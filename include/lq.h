@@ -73,6 +73,7 @@ typedef struct ihipStream_t* hipStream_t;
 #define LQ_EINVAL (-1)       /* NULL where not allowed, misaligned pointer, inconsistent sizes */
 #define LQ_EUNSUPPORTED (-2) /* a configuration outside the supported set below */
 #define LQ_EHIP (-3)         /* the HIP runtime reported an error (launch or copy) */
+#define LQ_ESCRATCH (-4)     /* lq_window_flush_noalloc: more units than its scratch holds */
 
 /* gate kinds */
 #define LQ_GATE_SCALAR 0  /* Gated DeltaNet: one alpha per unit and token */
@@ -188,6 +189,22 @@ int32_t lq_decode_step(const lq_config* cfg, void* state, const float* q, const 
  */
 int32_t lq_window_flush(const lq_config* cfg, void* state, const uint8_t* force_mask,
                         hipStream_t stream);
+
+/*
+ * lq_window_flush without the blob's work section: for callers that cannot
+ * allocate device memory or must not have a call allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid it).  Same
+ * arguments, semantics and results as lq_window_flush; the list of due units
+ * is kept instead in a device array inside the library (one per GPU, 1 MiB,
+ * held until the process ends), so the call allocates nothing.  At most
+ * LQ_NOALLOC_MAX_UNITS units (n_seq * n_v_heads); more returns LQ_ESCRATCH
+ * and launches nothing.  Every call on one GPU uses that GPU's array: calls
+ * that overlap in time on one GPU (on different streams, or from different
+ * host threads without ordering) race and must not be issued.
+ */
+#define LQ_NOALLOC_MAX_UNITS 262144
+int32_t lq_window_flush_noalloc(const lq_config* cfg, void* state, const uint8_t* force_mask,
+                                hipStream_t stream);
 
 /*
  * Prefill: run a prompt of n_tok tokens (n_tok >= 0, the same for every

@@ -23,6 +23,8 @@ LQ_OK = 0
 LQ_EINVAL = -1
 LQ_EUNSUPPORTED = -2
 LQ_EHIP = -3
+LQ_ESCRATCH = -4
+LQ_NOALLOC_MAX_UNITS = 262144
 LQ_GATE_SCALAR = 0
 LQ_GATE_CHANNEL = 1
 LQ_CODE_INT8 = 0
@@ -35,7 +37,7 @@ LQ_DEV_BUFFER_SATURATED = 0x4
 
 EXPORTS = ("lq_state_bytes", "lq_state_layout", "lq_state_init", "lq_prefill", "lq_decode_step",
            "lq_window_flush", "lq_dequant_state", "lq_fp32_decode_step", "lq_read_status",
-           "lq_clear_status", "lq_strerror")
+           "lq_clear_status", "lq_window_flush_noalloc", "lq_strerror")
 
 
 class LQError(RuntimeError):
@@ -101,6 +103,7 @@ def load_library(path: Optional[str] = None):
     lib.lq_decode_step.argtypes = [CP, P, P, P, P, P, P, P, P]
     lib.lq_prefill.argtypes = [CP, P, P, ctypes.c_int32, P, P, P, P, P, P, P]
     lib.lq_window_flush.argtypes = [CP, P, P, P]
+    lib.lq_window_flush_noalloc.argtypes = [CP, P, P, P]
     lib.lq_dequant_state.argtypes = [CP, P, P, ctypes.c_int32, P]
     lib.lq_fp32_decode_step.argtypes = [CP, P, P, P, P, P, P, P, P]
     lib.lq_read_status.argtypes = [CP, P, ctypes.POINTER(ctypes.c_uint32), P]
@@ -245,6 +248,15 @@ def lq_window_flush(cfg: Config, state, force_mask=None, stream=None) -> None:
         ctypes.byref(cfg.c()), _state_ptr(cfg, state),
         _ptr(force_mask, "force_mask", torch.uint8, cfg.n_seq, allow_none=True), _stream(stream))
     _check("lq_window_flush", rc)
+
+
+def lq_window_flush_noalloc(cfg: Config, state, force_mask=None, stream=None) -> None:
+    import torch
+
+    rc = load_library().lq_window_flush_noalloc(
+        ctypes.byref(cfg.c()), _state_ptr(cfg, state),
+        _ptr(force_mask, "force_mask", torch.uint8, cfg.n_seq, allow_none=True), _stream(stream))
+    _check("lq_window_flush_noalloc", rc)
 
 
 def lq_dequant_state(cfg: Config, state, S_out, include_buffer: bool = False, stream=None) -> None:

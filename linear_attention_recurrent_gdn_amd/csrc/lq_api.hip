@@ -150,6 +150,24 @@ int32_t lq_window_flush(const lq_config* cfg, void* state, const uint8_t* force_
     return hip_status(launch_materialize(a, kModeFlush, cfg->d_k, cfg->gate_kind, stream));
 }
 
+int32_t lq_window_flush_noalloc(const lq_config* cfg, void* state, const uint8_t* force_mask,
+                                hipStream_t stream) {
+    int32_t rc = check_config(cfg);
+    if (rc != LQ_OK) return rc;
+    if (state == nullptr || !aligned(state, kSectionAlign)) return LQ_EINVAL;
+    if ((int64_t)cfg->n_seq * cfg->n_v_heads > kScratchMaxUnits) return LQ_ESCRATCH;
+    lq_layout L;
+    compute_layout(*cfg, L);
+    MatArgs a{};
+    a.blob = blob_ptrs(state, L);
+    a.dm = dims_of(cfg);
+    a.force = force_mask;
+    int32_t* work = nullptr;
+    if (scratch_work_list(&work) != hipSuccess) return LQ_EHIP;
+    a.blob.work = work;  // the library's array instead of the blob's work section
+    return hip_status(launch_materialize(a, kModeFlush, cfg->d_k, cfg->gate_kind, stream));
+}
+
 int32_t lq_dequant_state(const lq_config* cfg, const void* state, float* S_out,
                          int32_t include_buffer, hipStream_t stream) {
     int32_t rc = check_config(cfg);
@@ -217,6 +235,7 @@ const char* lq_strerror(int32_t code) {
         case LQ_EINVAL: return "invalid argument (null or misaligned pointer, or inconsistent sizes)";
         case LQ_EUNSUPPORTED: return "unsupported configuration";
         case LQ_EHIP: return "HIP runtime error";
+        case LQ_ESCRATCH: return "more units than the allocation-free call's scratch holds (262144)";
         default: return "unknown lq status code";
     }
 }

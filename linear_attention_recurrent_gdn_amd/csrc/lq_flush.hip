@@ -53,9 +53,41 @@
 // combine the wavefronts through LDS in a fixed order, so results are
 // deterministic.
 
+#include <atomic>
+
 #include "lq_internal.h"
 
 namespace lq {
+
+// Work list of the allocation-free boundary call (lq_window_flush_noalloc):
+// [0] = count, [1..] = units due.  Every call on a device shares that device's
+// copy and leaves the last call's list in it; the due-unit scan rewrites the
+// count and every entry it uses, so nothing needs clearing.  In host code the
+// name is a stand-in, not a device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) int32_t scratch[1 + kScratchMaxUnits];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t*> g_scratch_addr[kMaxDevices];  // per device, set on first use
+}  // namespace
+
+hipError_t scratch_work_list(int32_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int32_t* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void* q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        p = static_cast<int32_t*>(q);
+        g_scratch_addr[dev].store(p, std::memory_order_release);  // a racing thread stores the same address
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 namespace {
 

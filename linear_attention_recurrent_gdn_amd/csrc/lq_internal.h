@@ -138,6 +138,12 @@ hipError_t launch_decode_fp32(const Fp32DecodeArgs& a, int d, int gate_kind, hip
 hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, hipStream_t st);
 hipError_t launch_clear_status(uint32_t* status, hipStream_t st);
 
+// Units the allocation-free boundary call can list: its work list lives in a
+// file-scope device array of 1 + kScratchMaxUnits int32 (lq_flush.hip).
+constexpr int kScratchMaxUnits = LQ_NOALLOC_MAX_UNITS;
+// Device address of that array on the current device (looked up once per device).
+hipError_t scratch_work_list(int32_t** out);
+
 }  // namespace lq
 
 // ---------------------------------------------------------------------------

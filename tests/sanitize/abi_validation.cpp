@@ -17,6 +17,8 @@ hipError_t launch_decode_q8(const DecodeArgs&, int, int, hipStream_t) { ++g_laun
 hipError_t launch_decode_fp32(const Fp32DecodeArgs&, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_materialize(const MatArgs&, int, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_clear_status(uint32_t*, hipStream_t) { ++g_launches; return hipSuccess; }
+alignas(256) int32_t g_scratch[16];
+hipError_t scratch_work_list(int32_t** out) { *out = g_scratch; return hipSuccess; }
 }  // namespace lq
 
 // the runtime calls of lq_read_status: the device address is never touched
@@ -131,8 +133,18 @@ int main() {
     EXPECT(lq_prefill(&c, st, f, 7, f, f, f, f, f, o, nullptr) == LQ_OK);
     EXPECT(lq_clear_status(&c, st, nullptr) == LQ_OK);
     EXPECT(lq_read_status(&c, st, &flags, nullptr) == LQ_OK && flags == 0);
-    EXPECT(lq::g_launches == 9);
-    for (int code : {0, -1, -2, -3, 5, -100}) EXPECT(std::strlen(lq_strerror(code)) > 0);
+    EXPECT(lq_window_flush_noalloc(&c, st, nullptr, nullptr) == LQ_OK);
+    EXPECT(lq::g_launches == 10);
+    // the allocation-free call: its unit limit and its argument checks launch nothing
+    lq_config big = base();
+    big.n_seq = LQ_NOALLOC_MAX_UNITS / 4 + 1;  // 4 value heads: one unit over the limit
+    EXPECT(lq_window_flush_noalloc(&big, st, nullptr, nullptr) == LQ_ESCRATCH);
+    big.n_seq = LQ_NOALLOC_MAX_UNITS / 4;
+    EXPECT(lq_window_flush_noalloc(&big, st, nullptr, nullptr) == LQ_OK);
+    EXPECT(lq_window_flush_noalloc(&c, nullptr, nullptr, nullptr) == LQ_EINVAL);
+    EXPECT(lq_window_flush_noalloc(&c, st_mis, nullptr, nullptr) == LQ_EINVAL);
+    EXPECT(lq::g_launches == 11);
+    for (int code : {0, -1, -2, -3, -4, 5, -100}) EXPECT(std::strlen(lq_strerror(code)) > 0);
 
     if (g_fail) return 1;
     std::printf("abi validation: %d layouts, all checks passed\n", variants);
