@@ -354,6 +354,24 @@ def practical_read(nbytes: float):
     return {"GBps": best["TBps"] * 1e3, "us": best["us"], "grid": best["grid"]}
 
 
+def practical_mix(units: int):
+    """The access-mix probe (the decode step's reads and writes for an empty
+    window, d = 128) at `units` units: GB/s for reads only, with the writes,
+    and with the 512-byte writes non-temporal; None when the probe is not built."""
+    import subprocess
+
+    from linear_attention_recurrent_gdn_amd import _build
+
+    if not os.path.exists(_build.MIX):
+        return None
+    r = subprocess.run([_build.MIX, str(int(units))], capture_output=True, text=True, timeout=120)
+    rows = {x["mode"]: x for x in (json.loads(l) for l in r.stdout.splitlines() if l.startswith("{"))}
+    if r.returncode != 0 or len(rows) != 3:
+        return None
+    return {name: rows[m]["TBps"] * 1e3 for m, name in ((0, "reads_only_GBps"), (1, "with_writes_GBps"),
+                                                         (2, "with_writes_nt_GBps"))}
+
+
 def variant_tag(workload, fmt="int8", buffer="fp32"):
     """Name of a workload variant in profile file names."""
     return workload + ("" if fmt == "int8" else f"_{fmt}") + ("" if buffer == "fp32" else f"_{buffer}buf")
@@ -650,6 +668,13 @@ def main(argv=None):
             "bytes_per_launch": avg_bytes, "achieved": pr["GBps"], "unit": "GB/s",
             "frac_of_peak": pr["GBps"] / HBM_PEAK_GBS, "decode_frac_of_practical": achieved / pr["GBps"],
         }
+
+    if d == 128:
+        pm = practical_mix(U)
+        if pm is not None:
+            result["roofline"]["practical_mix"] = dict(
+                kernel="access_mix (probe/access_mix.hip): the decode step's reads and writes for an empty window, "
+                       "nothing else, at this launch's unit count", unit="GB/s", **pm)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, args.format, args.buffer)

@@ -102,24 +102,43 @@ __device__ __forceinline__ int unit_of_block(int b, const Dims& dm) {
     return kvec * G + slot % G;
 }
 
+// A wavefront-uniform pair held in scalar registers (frees two vector
+// registers per ring slot).
+__device__ __forceinline__ float2 uniform2(float2 x) {
+    return make_float2(__builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x.x))),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x.y))));
+}
+
 __device__ __forceinline__ float lane_value(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Stores values that are already binary16-representable when H16.
-template <int EPL, bool H16>
+// Stores values that are already binary16-representable when H16; NT: as
+// non-temporal stores.
+template <int EPL, bool H16, bool NT = false>
 __device__ __forceinline__ void store_buf(void* base, size_t off, const Vec<EPL>& v) {
     if constexpr (H16) {
         _Float16* p = reinterpret_cast<_Float16*>(base) + off;
         if constexpr (EPL == 2) {
-            *reinterpret_cast<f16x2*>(p) = f16x2{(_Float16)v.e[0], (_Float16)v.e[1]};
+            const f16x2 h = f16x2{(_Float16)v.e[0], (_Float16)v.e[1]};
+            if constexpr (NT) __builtin_nontemporal_store(h, reinterpret_cast<f16x2*>(p));
+            else *reinterpret_cast<f16x2*>(p) = h;
         } else {
-            p[0] = (_Float16)v.e[0];
+            if constexpr (NT) __builtin_nontemporal_store((_Float16)v.e[0], p);
+            else p[0] = (_Float16)v.e[0];
         }
     } else {
-        store_vec(reinterpret_cast<float*>(base) + off, v);
+        float* p = reinterpret_cast<float*>(base) + off;
+        if constexpr (EPL == 2) {
+            const f32x2 f = f32x2{v.e[0], v.e[1]};
+            if constexpr (NT) __builtin_nontemporal_store(f, reinterpret_cast<f32x2*>(p));
+            else *reinterpret_cast<f32x2*>(p) = f;
+        } else {
+            if constexpr (NT) __builtin_nontemporal_store(v.e[0], p);
+            else p[0] = v.e[0];
+        }
     }
 }
 
@@ -222,7 +241,16 @@ __device__ __forceinline__ void codes_to_float(const uint4& w4, float (&cf)[16])
 
 }  // namespace
 
-template <int D, bool KDA, int P, int NWB, int FMT, bool H16>
+// LARGE selects the form for launches of many units per CU: no early code
+// conversion, four compensator slots in registers for the scalar gate and
+// the ring's beta and gate in scalar registers (72 registers, seven
+// wavefronts per SIMD: with many units per CU occupancy is worth more than
+// the conversion saved at the barrier), and the 512-byte writes (the
+// appended entry, the outputs) as non-temporal stores (about 1 us less per
+// launch on the hybrid stack; the 4-byte writes stay ordinary stores, as
+// non-temporal they cost more).  The other form (one round of workgroups)
+// keeps the codes converted early and eight slots in registers.
+template <int D, bool KDA, int P, int NWB, int FMT, bool H16, bool LARGE>
 __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     constexpr int EPL = D / kWave;   // state elements per lane in the chain wave
     constexpr int GE = KDA ? EPL : 1;
@@ -230,7 +258,9 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     constexpr int LPR = D / 16;      // lanes per code row (16 codes per 16-byte load)
     constexpr int RPL = kWave / LPR; // code rows per wave-wide 16-byte load
     constexpr int NLW = RW / RPL;    // 16-byte tile loads per lane
-    constexpr int NCP = 8;           // compensator slots held in registers
+    // compensator slots held in registers through the reverse pass (the rest
+    // are loaded after it)
+    constexpr int NCP = (KDA || !LARGE) ? 8 : 4;
 
     __shared__ float lds_x[D];       // s * r, r = A_1..A_n q (all waves read it)
     __shared__ float lds_add[D];     // buffered-token and compensator terms of o
@@ -256,7 +286,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     // The tile quarter as floats, converted before the barrier.  Not with the
     // binary16 buffer: there the extra registers cost a wavefront per SIMD of
     // occupancy, more than the conversion saves.
-    constexpr bool kEarlyCodes = !H16;
+    constexpr bool kEarlyCodes = !H16 && !LARGE;
     float cf[NLW][16];
     float sg_row;
 
@@ -372,8 +402,8 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
             if (__any(sat) && lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_BUFFER_SATURATED);
         }
         if (!over) {
-            if (h % a.dm.group == 0) store_buf<EPL, H16>(a.blob.buf_k, kb0 + (size_t)j * D + lane * EPL, cur.k);
-            store_buf<EPL, H16>(a.blob.buf_v, vb0 + (size_t)j * D + lane * EPL, cur.v);
+            if (h % a.dm.group == 0) store_buf<EPL, H16, LARGE>(a.blob.buf_k, kb0 + (size_t)j * D + lane * EPL, cur.k);
+            store_buf<EPL, H16, LARGE>(a.blob.buf_v, vb0 + (size_t)j * D + lane * EPL, cur.v);
         }
         // beta and scalar gate of every buffered slot into LDS, then the ring's
         // first entries take theirs (uniform reads; later refills read ahead)
@@ -384,7 +414,10 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int p = 0; p < P; ++p) ring[p].ba = lds_ba[max(jr - 1 - p, 0)];
+        for (int p = 0; p < P; ++p) {
+            const float2 ba = lds_ba[max(jr - 1 - p, 0)];
+            ring[p].ba = LARGE ? uniform2(ba) : ba;
+        }
         if (!over) {
             if constexpr (KDA) {
                 store_vec(bg + (size_t)j * D + lane * EPL, cur.g);
@@ -437,7 +470,8 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
                 const int i = jr - 1 - (s0 + p);
                 step(ring_k(p), ring_v(p), ring[p].g, ring[p].ba.x, ring[p].ba.y);
                 load_entry(i - P, ring[p]);
-                ring[p].ba = lds_ba[max(i - P, 0)];
+                const float2 ba = lds_ba[max(i - P, 0)];
+                ring[p].ba = LARGE ? uniform2(ba) : ba;
             }
         }
 #pragma unroll
@@ -516,7 +550,11 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     }
     const bool over = j >= W;
     if (cg < NLW)
-        a.o[(size_t)u * D + my_row] = over ? __builtin_nanf("") : __builtin_fmaf(sg_row, mine, lds_add[my_row]);
+    {
+        const float ov = over ? __builtin_nanf("") : __builtin_fmaf(sg_row, mine, lds_add[my_row]);
+        if constexpr (LARGE) __builtin_nontemporal_store(ov, a.o + (size_t)u * D + my_row);
+        else a.o[(size_t)u * D + my_row] = ov;
+    }
     if (wave == 0 && lane == 0) {
         if (over) atomicOr(a.blob.status, (uint32_t)LQ_DEV_WINDOW_OVERFLOW);
         else a.blob.fill[u] = j + 1;
@@ -616,28 +654,41 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
 #define LQ_RING_KDA_H16 4
 #endif
 
-template <int NWB, int FMT, bool H16>
+// Launches of more units than this take the LARGE form (many workgroups per
+// CU); the smaller ones (the GDN decode workload's 1,024 units: four
+// workgroups per CU, one round) keep the early code conversion.
+#ifndef LQ_LARGE_UNITS_MIN
+#define LQ_LARGE_UNITS_MIN 2048
+#endif
+
+template <int NWB, int FMT, bool H16, bool LARGE>
 void launch_decode_q8_w(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
     const dim3 grid(a.dm.n_units), block(256);
     if (d == 128) {
         constexpr int PK = H16 ? LQ_RING_KDA_H16 : LQ_RING_KDA;
         constexpr int PG = H16 ? LQ_RING_GDN_H16 : LQ_RING_GDN;
         if (gate_kind == LQ_GATE_CHANNEL)
-            hipLaunchKernelGGL((decode_q8_kernel<128, true, PK, NWB, FMT, H16>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<128, true, PK, NWB, FMT, H16, LARGE>), grid, block, 0, st, a);
         else
-            hipLaunchKernelGGL((decode_q8_kernel<128, false, PG, NWB, FMT, H16>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<128, false, PG, NWB, FMT, H16, LARGE>), grid, block, 0, st, a);
     } else {
         if (gate_kind == LQ_GATE_CHANNEL)
-            hipLaunchKernelGGL((decode_q8_kernel<64, true, 16, NWB, FMT, H16>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<64, true, 16, NWB, FMT, H16, LARGE>), grid, block, 0, st, a);
         else
-            hipLaunchKernelGGL((decode_q8_kernel<64, false, 16, NWB, FMT, H16>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<64, false, 16, NWB, FMT, H16, LARGE>), grid, block, 0, st, a);
     }
 }
 
 template <int FMT, bool H16>
 void launch_decode_q8_f(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
-    if (a.dm.window <= 2 * kWave) launch_decode_q8_w<2, FMT, H16>(a, d, gate_kind, st);
-    else launch_decode_q8_w<4, FMT, H16>(a, d, gate_kind, st);
+    const bool large = a.dm.n_units > LQ_LARGE_UNITS_MIN;
+    if (a.dm.window <= 2 * kWave) {
+        if (large) launch_decode_q8_w<2, FMT, H16, true>(a, d, gate_kind, st);
+        else launch_decode_q8_w<2, FMT, H16, false>(a, d, gate_kind, st);
+    } else {
+        if (large) launch_decode_q8_w<4, FMT, H16, true>(a, d, gate_kind, st);
+        else launch_decode_q8_w<4, FMT, H16, false>(a, d, gate_kind, st);
+    }
 }
 
 template <bool H16>

@@ -20,6 +20,17 @@ Three commands:
       Formats a ``rocprofv3 --stats`` kernel_stats.csv as a short text
       summary headed by the command that produced it.
 
+  flush    --workload W [--launches N]
+      Runs N window-boundary launches on one layer of the workload's shape
+      (every unit's window filled by W decode launches first, synthetic
+      tokens), meant to run under ``rocprofv3 --pmc SQ_INSTS_MFMA
+      SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE``.
+
+  mfma     --workload W --dir DIR --out FILE --command "..."
+      Reads that run's counter_collection.csv and writes, per flush launch,
+      the matrix-core counters, the busy fraction of the matrix pipes and the
+      FP64 rate the instruction count implies.
+
   hbm
       Practical memory bandwidth of this device for plain streaming kernels:
       the stream_read yardstick (probe/stream_read.hip: 16-byte loads,
@@ -97,7 +108,83 @@ def run_window(workload: str, fmt: str = "int8", buffer: str = "fp32") -> None:
         sys.exit(1)
 
 
+def run_flush(workload: str, launches: int = 3) -> None:
+    import torch
+
+    import linear_attention_recurrent_gdn_amd as lq
+    from linear_attention_recurrent_gdn_amd import inputs as I
+
+    lq.load_library()
+    wl = I.WORKLOADS[workload].scaled(projected=False, layers=1)
+    U, d, W = wl.n_units, wl.d, wl.window
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(dev).manual_seed(3000 + wl.seed)
+    cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind)
+    state = lq.new_state(cfg, dev)
+    S0 = torch.randn((U, d, d), generator=gen, device=dev) * 0.5
+    lq.lq_state_init(cfg, state, S0)
+    del S0
+    toks = [I.torch_token(wl, gen, dev) for _ in range(min(W, 16))]
+    o = torch.empty((wl.n_seq, wl.n_v_heads, d), device=dev)
+    for n in range(launches):
+        for t in range(W):
+            tk = toks[t % len(toks)]
+            lq.lq_decode_step(cfg, state, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+        torch.cuda.synchronize()
+        print(f"[flush] {workload}: boundary {n + 1}/{launches} over {U} units, {W} tokens each", flush=True)
+        lq.lq_window_flush(cfg, state, None)
+        torch.cuda.synchronize()
+    flags = lq.lq_read_status(cfg, state)
+    print(f"[flush] done, flags={flags:#x}", flush=True)
+    if flags:
+        sys.exit(1)
+
+
+MFMA_F64_FLOP = 2 * 16 * 16 * 4  # one v_mfma_f64_16x16x4f64
+PEAK_FP64_TFLOPS = 78.6
+N_CU = 256
+
+
+def mfma(workload: str, directory: str, out: str, cmd: str) -> dict:
+    """Per flush launch: the matrix-core counters and what they imply."""
+    from linear_attention_recurrent_gdn_amd import inputs as I
+
+    wl = I.WORKLOADS[workload]
+    cnt = {}
+    for name in ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"):
+        cnt[name] = _per_dispatch(_counter_rows(directory, name), "materialize_kernel")
+    n = len(cnt["SQ_INSTS_MFMA"])
+    if n == 0 or any(len(v) != n for v in cnt.values()):
+        raise SystemExit(f"expected the same flush dispatches for every counter, found "
+                         f"{ {k: len(v) for k, v in cnt.items()} }")
+    rows = []
+    for i in range(n):
+        mf, busy, sqb, gui = (cnt[k][i] for k in ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
+                                                  "GRBM_GUI_ACTIVE"))
+        rows.append({"mfma_insts": mf, "mfma_busy_cycles": busy, "sq_busy_cycles": sqb, "gui_active": gui,
+                     "busy_cycles_per_mfma": busy / mf if mf else 0.0,
+                     "mfma_flop": mf * MFMA_F64_FLOP})
+    rec = {"kernel": "materialize_kernel (flush mode)", "workload": workload, "units": wl.n_units,
+           "window": wl.window, "dispatches": rows, "command": cmd}
+    lines = [f"# matrix-core counters of the window-boundary kernel, {workload} shape "
+             f"({wl.n_units} units, W = {wl.window}, d = {wl.d})",
+             f"# command: {cmd}", "#",
+             "# per dispatch of the materialize kernel (the first is the state init, which replays nothing; "
+             "then the boundaries): SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES, busy cycles per MFMA, "
+             "GRBM_GUI_ACTIVE, MFMA flop (16x16x4 FP64: 2048 each), SQ_BUSY_CYCLES, matrix-pipe busy fraction "
+             "(busy cycles / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs))"]
+    for r in rows:
+        frac = r["mfma_busy_cycles"] / (r["gui_active"] / 8.0 * 4 * N_CU) if r["gui_active"] else 0.0
+        kind = "boundary" if r["mfma_insts"] else "init"
+        lines.append(f"  {kind:8s} {r['mfma_insts']:14.0f} {r['mfma_busy_cycles']:16.0f} {r['busy_cycles_per_mfma']:7.2f} "
+                     f"{r['gui_active']:14.0f} {r['mfma_flop']:16.4g} {r['sq_busy_cycles']:14.0f} {frac:6.3f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return rec
+
+
 STREAM_BYTES = (56397824, 378830848, 505602048, 902365184, 4 << 30)
+MIX_UNITS = (1024, 4096, 8192, 16384)  # decode launch sizes of the workloads
 
 
 def hbm() -> dict:
@@ -112,6 +199,14 @@ def hbm() -> dict:
     if r.returncode != 0:
         raise SystemExit(f"stream_read failed: {r.stderr.strip()}")
     out = {"stream_read": [json.loads(l) for l in r.stdout.splitlines() if l.startswith("{")]}
+    out["access_mix"] = []
+    if os.path.exists(_build.MIX):
+        for units in MIX_UNITS:
+            r = subprocess.run([_build.MIX, str(units)], capture_output=True, text=True)
+            sys.stdout.write(r.stdout)
+            if r.returncode != 0:
+                raise SystemExit(f"access_mix failed: {r.stderr.strip()}")
+            out["access_mix"] += [json.loads(l) for l in r.stdout.splitlines() if l.startswith("{")]
     import torch
 
     dev = torch.device("cuda", 0)
@@ -196,7 +291,19 @@ def traffic(workload: str, fetch_dir: str, write_dir: str, out: str, cmd: str) -
     return rec
 
 
-def stats(csv_path: str, cmd: str, out: str) -> None:
+def tail_mean_us(trace_csv: str, name_part: str, n: int):
+    """Mean duration (us) of the last n dispatches of a kernel in a kernel trace."""
+    with open(trace_csv) as f:
+        rows = [r for r in csv.DictReader(f) if name_part in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    tail = rows[-n:]
+    if not tail:
+        return None
+    return sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tail) / len(tail) / 1e3, len(tail)
+
+
+def stats(csv_path: str, cmd: str, out: str, trace_csv: str = None, tail_kernel: str = None,
+          tail_n: int = 0) -> None:
     with open(csv_path) as f:
         rows = list(csv.DictReader(f))
     lines = [f"# rocprofv3 kernel statistics", f"# command: {cmd}", "#",
@@ -208,6 +315,13 @@ def stats(csv_path: str, cmd: str, out: str) -> None:
         lines.append(f"  {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
                      f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e6:10.3f} "
                      f"{float(r['Percentage']):6.2f}  {name}")
+    if trace_csv and tail_kernel and tail_n > 0:
+        res = tail_mean_us(trace_csv, tail_kernel, tail_n)
+        if res is not None:
+            mean, n = res
+            lines.append("#")
+            lines.append(f"# {tail_kernel}: mean of its last {n} dispatches (the benchmark's graph of one "
+                         f"window of decode launches): {mean:.2f} us")
     text = "\n".join(lines) + "\n"
     with open(out, "w") as f:
         f.write(text)
@@ -233,6 +347,17 @@ def main(argv=None):
     c.add_argument("--csv", required=True)
     c.add_argument("--command", default="")
     c.add_argument("--out", required=True)
+    c.add_argument("--trace", default=None, help="kernel_trace.csv of the same run")
+    c.add_argument("--tail-kernel", default=None)
+    c.add_argument("--tail", type=int, default=0, help="also report the mean of the kernel's last N dispatches")
+    fl = sub.add_parser("flush")
+    fl.add_argument("--workload", default="gdn_decode")
+    fl.add_argument("--launches", type=int, default=3)
+    m = sub.add_parser("mfma")
+    m.add_argument("--workload", default="gdn_decode")
+    m.add_argument("--dir", required=True)
+    m.add_argument("--out", required=True)
+    m.add_argument("--command", default="")
     args = ap.parse_args(argv)
     if args.cmd == "window":
         run_window(args.workload, args.format, args.buffer)
@@ -244,13 +369,26 @@ def main(argv=None):
                      "#", "# stream_read (probe/stream_read.hip): bytes read per launch, grid, mean us, TB/s"]
             for r in res["stream_read"]:
                 lines.append(f"  {r['bytes']:>12d} {r['grid']:6d} {r['us']:10.2f} {r['TBps']:7.3f}")
-            lines.append("# torch: " + ", ".join(f"{k} {v}" for k, v in res.items() if k != "stream_read"))
+            lines.append("#")
+            lines.append("# access_mix (probe/access_mix.hip): the decode step's accesses for an empty window "
+                         "(d = 128, 4 compensators, 2 value heads per key head);")
+            lines.append("# mode 0 reads only, 1 with its writes, 2 with the 512-byte writes non-temporal")
+            lines.append("# units, mode, mean us, MB read, MB written, TB/s")
+            for r in res.get("access_mix", []):
+                lines.append(f"  {r['units']:>7d} {r['mode']:4d} {r['us']:10.2f} {r['read_bytes'] / 1e6:9.1f} "
+                             f"{r['write_bytes'] / 1e6:8.2f} {r['TBps']:7.3f}")
+            lines.append("# torch: " + ", ".join(f"{k} {v}" for k, v in res.items()
+                                                 if k not in ("stream_read", "access_mix")))
             with open(args.out, "w") as f:
                 f.write("\n".join(lines) + "\n")
     elif args.cmd == "traffic":
         print(json.dumps(traffic(args.workload, args.fetch, args.write, args.out, args.command), indent=1))
+    elif args.cmd == "flush":
+        run_flush(args.workload, args.launches)
+    elif args.cmd == "mfma":
+        print(json.dumps(mfma(args.workload, args.dir, args.out, args.command), indent=1))
     else:
-        stats(args.csv, args.command, args.out)
+        stats(args.csv, args.command, args.out, args.trace, args.tail_kernel, args.tail)
 
 
 if __name__ == "__main__":

@@ -81,3 +81,33 @@ def test_fp32_kernel_fullsize_sampled(name, layer):
     assert per_s.max() <= 1e-5, per_s.max()
     print(f"[fp32 kernel] {name}: {U} units per launch, {len(checked)} followed, worst unit output "
           f"rel-L2 {worst:.3g}, state {per_s.max():.3g}", flush=True)
+
+
+# launches of more than 2048 units take the large-launch form of the decode
+# kernel (no early code conversion, non-temporal 512-byte stores): a unit
+# count that is no multiple of the XCD grouping (4102 units, two value heads
+# per key head), four value heads per key head with more compensators than
+# the form holds in registers, and a window above 128 with E4M3 codes and the
+# binary16 buffer, each on a sample of units with a boundary inside the run
+LARGE_CASES = {
+    "large_odd_gqa2": I.WORKLOADS["gdn_decode"].scaled(
+        name="large_odd_gqa2", n_seq=2051, n_v_heads=2, n_k_heads=1, window=16, n_comp=3, prefill=24,
+        decode=40, outlier_rows=0, outlier_cols=0),
+    "large_gqa4_nc7": I.WORKLOADS["gdn_decode"].scaled(
+        name="large_gqa4_nc7", n_seq=256, n_v_heads=16, n_k_heads=4, window=32, n_comp=7, prefill=24,
+        decode=45),
+    "large_kda_w200_e4m3_h16": I.WORKLOADS["kda_decode"].scaled(
+        name="large_kda_w200_e4m3_h16", n_seq=1024, n_v_heads=4, n_k_heads=4, window=200, n_comp=8,
+        prefill=16, decode=210, code_format="e4m3", buffer_format="fp16"),
+}
+
+
+@pytest.mark.parametrize("name", list(LARGE_CASES))
+def test_large_launch_parity(name):
+    wl = LARGE_CASES[name]
+    assert wl.n_units > 2048
+    picks = {0, 1, 2, 3, wl.n_units - 1, wl.n_units - 2, wl.n_units // 2}
+    rng = np.random.default_rng(5)
+    picks.update(int(x) for x in rng.choice(wl.n_units, 9, replace=False))
+    rep = parity.run(wl, checked=sorted(picks), dequant_every=wl.window // 2 + 3)
+    assert rep.flushes >= 1 and rep.decode_calls == wl.decode
