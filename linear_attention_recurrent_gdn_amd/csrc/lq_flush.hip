@@ -243,26 +243,43 @@ __device__ __forceinline__ float pick4(const float4& f, int i) {
     return i == 0 ? f.x : i == 1 ? f.y : i == 2 ? f.z : f.w;
 }
 
-// One chunk of buffered tokens as fetched by one thread: one float4 of the
-// chunk's keys, values and channel gates (token-major, D floats per token)
-// and, for the first 16 threads, one beta and scalar gate.
+// One chunk of buffered tokens as fetched by one thread: four of the
+// chunk's keys and values as stored (four fp32, or four binary16 in the first
+// two words; token-major, D elements per token), four channel gates, and, for
+// the first 16 threads, one beta and scalar gate.  The conversion waits for
+// the data, so it happens when the chunk is staged, not when it is fetched.
 template <bool KDA>
 struct Stage {
-    float4 k, v, g;
+    uint4 k, v;
+    float4 g;
     float b, al;
 };
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-// Four consecutive buffer elements (fp32, or binary16 converted exactly).  A
-// 32-bit element offset from a uniform base keeps the address in the
-// scalar-base form (no 64-bit per-lane address registers).
-__device__ __forceinline__ float4 load4_buf(const void* base, uint32_t off, bool h16) {
+// Four consecutive buffer elements as stored.  A 32-bit element offset from a
+// uniform base keeps the address in the scalar-base form (no 64-bit per-lane
+// address registers).
+template <bool H16>
+__device__ __forceinline__ uint4 load4_buf(const void* base, uint32_t off) {
+    if constexpr (H16) {
+        const uint2 h = *reinterpret_cast<const uint2*>(reinterpret_cast<const _Float16*>(base) + off);
+        uint4 r;  // the last two words stay unset (unread): no write that must wait for an earlier load
+        r.x = h.x;
+        r.y = h.y;
+        return r;
+    } else {
+        return *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + off);
+    }
+}
+
+// The four elements of load4_buf as fp32 (binary16 converts exactly).
+__device__ __forceinline__ float4 unpack4(const uint4& r, bool h16) {
     if (h16) {
-        const f16x4 h = *reinterpret_cast<const f16x4*>(reinterpret_cast<const _Float16*>(base) + off);
+        const f16x4 h = __builtin_bit_cast(f16x4, make_uint2(r.x, r.y));
         return make_float4((float)h.x, (float)h.y, (float)h.z, (float)h.w);
     }
-    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+    return __builtin_bit_cast(float4, r);
 }
 
 // Token strides (elements) of the replayed tokens: the window buffer holds
@@ -272,30 +289,34 @@ struct TokStrides {
     size_t k, v, b, g;
 };
 
-template <int D, int NT, bool KDA>
-__device__ __forceinline__ Stage<KDA> fetch_stage(const void* bk, const void* bv, bool h16, const float* bb,
-                                                 const float* bg, TokStrides ts, int i0, int n_replay, int tid) {
+template <int D, int NT, bool KDA, bool H16>
+__device__ __forceinline__ Stage<KDA> fetch_stage(const void* bk, const void* bv, const float* bb,
+                                                    const float* bg, TokStrides ts, int i0, int n_replay, int tid) {
     constexpr int EB = 16;
     Stage<KDA> st;
     const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
     const int x = 4 * tid;
     const uint32_t e = (uint32_t)min(x / D, ne - 1), c = (uint32_t)(x % D);
     // uniform chunk bases, then 32-bit offsets inside the chunk (16 token strides)
-    const size_t esz = h16 ? 2 : 4;
+    constexpr size_t esz = H16 ? 2 : 4;
     const char* k0 = (const char*)bk + (size_t)i0 * ts.k * esz;
     const char* v0 = (const char*)bv + (size_t)i0 * ts.v * esz;
     const float* g0 = bg + (size_t)i0 * ts.g;
     const float* b0 = bb + (size_t)i0 * ts.b;
-    st.k = load4_buf(k0, e * (uint32_t)ts.k + c, h16);
-    st.v = load4_buf(v0, e * (uint32_t)ts.v + c, h16);
-    if constexpr (KDA) st.g = *reinterpret_cast<const float4*>(g0 + (e * (uint32_t)ts.g + c));
-    st.b = 0.f;
-    st.al = 1.f;
-    if (tid < EB) {
-        const uint32_t t = (uint32_t)min(tid, ne - 1);
-        st.b = b0[t * (uint32_t)ts.b];
-        if constexpr (!KDA) st.al = g0[t * (uint32_t)ts.g];
-    }
+    // every thread loads a (clamped) token's beta and scalar gate; the first
+    // 16 use them.  No constant is written to these registers: such a write
+    // would have to wait for every load in flight, this chunk's too.  For the
+    // same reason every address is formed before the first load is issued.
+    const uint32_t t = (uint32_t)min(tid, ne - 1);
+    const uint32_t ok = e * (uint32_t)ts.k + c, ov = e * (uint32_t)ts.v + c, og = e * (uint32_t)ts.g + c;
+    const uint32_t ob = t * (uint32_t)ts.b, oa = t * (uint32_t)ts.g;
+    __builtin_amdgcn_sched_barrier(0);
+    st.k = load4_buf<H16>(k0, ok);
+    st.v = load4_buf<H16>(v0, ov);
+    if constexpr (KDA) st.g = *reinterpret_cast<const float4*>(g0 + og);
+    st.b = b0[ob];
+    if constexpr (!KDA) st.al = g0[oa];
+    __builtin_amdgcn_sched_barrier(0);
     return st;
 }
 
@@ -314,8 +335,11 @@ __device__ __forceinline__ float4 fetch_q(const float* bq, size_t stride, int i0
 
 }  // namespace
 
-template <int D, bool KDA, int MODE>
+// H16: the window buffer holds binary16 keys and values (a flush or dequant
+// that replays it; fp32 otherwise)
+template <int D, bool KDA, int MODE, bool H16>
 __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) {
+    static_assert(!H16 || MODE == kModeFlush || MODE == kModeDequant, "binary16 applies to the window buffer");
     constexpr int NW = D / 16;          // wavefronts = 16-row groups
     constexpr int NT = kWave * NW;      // threads
     constexpr int NB = D / 16;          // 16-column blocks
@@ -368,16 +392,102 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 
     const int n_work = (MODE == kModeFlush) ? a.blob.work[0] : a.dm.n_units;
     constexpr bool kFromCodes = !(MODE == kModeInit || PF);  // the start state is the quantized one
-    // the unit of the next work item is read one item ahead
-    int u_next = (MODE == kModeFlush) ? a.blob.work[1 + min((int)blockIdx.x, max(n_work - 1, 0))]
-                                      : (int)blockIdx.x;
-    for (int wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
-        const int u = u_next;
+    // The unit of this workgroup's work item k.  A flush reads the work list
+    // 64 items at a time into a register (lane j: item 64 i + j), so that a
+    // unit is a register read rather than a wait for memory (a wait for one
+    // load is a wait for every load and store requested before it).  Called
+    // with k increasing, every multiple of 64 included.
+    int wl_units = 0;
+    auto work_unit = [&](int k) -> int {
         if constexpr (MODE == kModeFlush) {
-            const int wn = wi + (int)gridDim.x;
-            u_next = a.blob.work[1 + (wn < n_work ? wn : wi)];
+            if ((k & 63) == 0) {
+                const int idx = (int)blockIdx.x + (k + lane_id()) * (int)gridDim.x;
+                wl_units = idx < n_work ? a.blob.work[1 + idx] : 0;
+            }
+            return __builtin_amdgcn_readlane(wl_units, k & 63);
         } else {
-            u_next = wi + (int)gridDim.x;
+            return (int)blockIdx.x + k * (int)gridDim.x;
+        }
+    };
+    int u_next = (int)blockIdx.x < n_work ? work_unit(0) : 0;
+    // tokens replayed from a unit's window buffer
+    auto replay_count = [&](int fill) {
+        return (MODE == kModeFlush || (MODE == kModeDequant && a.include_buffer)) ? (fill < W ? fill : W) : 0;
+    };
+    // window buffer of unit uu: keys (per key head), values, betas, gates
+    auto unit_buffers = [&](int uu, const void*& bk, const void*& bv, const float*& bb, const float*& bg) {
+        const int s = uu / a.dm.n_v_heads;
+        const int h = uu - s * a.dm.n_v_heads;
+        const size_t kvec = (size_t)s * a.dm.n_k_heads + h / a.dm.group;
+        constexpr size_t esz = H16 ? 2 : 4;
+        bk = (const char*)a.blob.buf_k + kvec * (size_t)W * D * esz;
+        bv = (const char*)a.blob.buf_v + (size_t)uu * W * D * esz;
+        bb = a.blob.buf_beta + (size_t)uu * W;
+        bg = a.blob.buf_gate + (size_t)uu * W * (KDA ? D : 1);
+    };
+    // Starting from the codes, what a unit's start reads (codes, row scale,
+    // smoothing, compensator lines, window count, then the first chunk of its
+    // buffer) is requested one unit ahead, while the previous unit is
+    // quantized: hw, hsg (this lane's row), hsm (channel tid), hcv, hcil, hfill.
+    uint32_t hw[NB];
+    float hsg = 0.f, hsm = 1.f;
+    float4 hcv = make_float4(0.f, 0.f, 0.f, 0.f);
+    int hcil = 0, hfill = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) hw[b] = 0u;
+    Stage<KDA> pf{};  // the chunk being fetched (registers until it is staged)
+    auto head_fetch = [&](int uu) {
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));  // indices recomputed here, not kept live
+        const int rq = (t % kWave) >> 4, rn = 16 * (t / kWave) + (t & 15);
+        hsg = a.blob.sigma[(size_t)uu * D + rn];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            hw[b] = *reinterpret_cast<const uint32_t*>(a.blob.codes + ((size_t)uu * D + rn) * D + 16 * b + 4 * rq);
+        hsm = a.blob.smooth[(size_t)uu * D + min(t, D - 1)];
+        if (nc > 0) {
+            static_assert(NT * 4 >= 16 * D, "one float4 per thread covers 16 lines");
+            hcv = *reinterpret_cast<const float4*>(a.blob.comp_vec + (size_t)uu * nc * D + min(4 * t, nc * D - 4));
+            hcil = a.blob.comp_idx[(size_t)uu * nc + min(t % kWave, nc - 1)];
+        }
+        // a vector load, counted with the ones above (a scalar load would hold
+        // up the next wait on LDS)
+        const int* fp = a.blob.fill + uu;
+        asm volatile("" : "+v"(fp));
+        hfill = *fp;
+    };
+    int nr_next = 0;  // tokens the fetched unit replays (uniform)
+    // the head is in by the time this runs: a wait for it here, before the
+    // first chunk's loads (on every path, fetched or not), keeps the wait at
+    // the unit's start from covering those loads as well
+    auto head_settle = [&]() {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) asm volatile("" ::"v"(hw[b]));
+        asm volatile("" ::"v"(hsg), "v"(hsm), "v"(hcv.x), "v"(hcv.y), "v"(hcv.z), "v"(hcv.w), "v"(hcil), "v"(hfill));
+    };
+    auto chunk0_fetch = [&](int uu) {
+        const int nr = replay_count(__builtin_amdgcn_readfirstlane(hfill));
+        nr_next = nr;
+        if (nr > 0) {
+            const void *bk, *bv;
+            const float *bb, *bg;
+            unit_buffers(uu, bk, bv, bb, bg);
+            int t = threadIdx.x;
+            asm volatile("" : "+v"(t));
+            pf = fetch_stage<D, NT, KDA, H16>(bk, bv, bb, bg, TokStrides{(size_t)D, (size_t)D, 1, KDA ? (size_t)D : 1},
+                                              0, nr, t);
+        }
+    };
+    if constexpr (kFromCodes) {
+        if ((int)blockIdx.x < n_work) head_fetch(u_next);
+        head_settle();
+        if ((int)blockIdx.x < n_work) chunk0_fetch(u_next);
+    }
+    for (int wi = blockIdx.x, k = 0; wi < n_work; wi += gridDim.x, ++k) {
+        const int u = u_next;
+        const bool ahead = wi + (int)gridDim.x < n_work;  // uniform: this workgroup has a next item
+        if constexpr (!kFromCodes) {
+            if (ahead) u_next = work_unit(k + 1);
         }
         const int s = u / a.dm.n_v_heads;
         const int h = u - s * a.dm.n_v_heads;
@@ -386,47 +496,27 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 
         // ---------------- A: the window-start state; T[b][r] = S[n][16b + 4q + r]
         //
-        // Its loads depend on the unit alone and are requested first.  The
-        // window count and then the first chunk of replayed tokens follow, so
-        // the dequantization waits for none of those (vector loads complete in
-        // order), while the chunk's latency overlaps it.
-        float4 sv[NB];    // start state S0 (init, prefill) or smoothing factors
-        uint32_t wd[NB];  // codes of the row's 16-column blocks (4 per word)
-        float sgr_f = 0.f;
-        float4 cv4 = make_float4(0.f, 0.f, 0.f, 0.f);  // this thread's four floats of the compensator lines
-        int cil = 0;                                    // slot indices, lane c holds slot c
+        // From a start state (init, prefill): its loads depend on the unit
+        // alone and are requested first, the first chunk of replayed tokens
+        // after them, so the conversion waits for none of those (vector loads
+        // complete in order).  From the codes: everything was requested while
+        // the previous unit was quantized (or before the first).
+        float4 sv[NB];  // start state S0 (init, prefill)
         if constexpr (!kFromCodes) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 sv[b] = make_float4(0.f, 0.f, 0.f, 0.f);
-                wd[b] = 0u;
                 if (a.S0 != nullptr)
                     sv[b] = *reinterpret_cast<const float4*>(a.S0 + ((size_t)u * D + n) * D + 16 * b + 4 * q);
-            }
-        } else {
-            sgr_f = a.blob.sigma[(size_t)u * D + n];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                sv[b] = *reinterpret_cast<const float4*>(a.blob.smooth + (size_t)u * D + 16 * b + 4 * q);
-                wd[b] = *reinterpret_cast<const uint32_t*>(a.blob.codes + ((size_t)u * D + n) * D + 16 * b + 4 * q);
-            }
-            if (nc > 0) {
-                static_assert(NT * 4 >= 16 * D, "one float4 per thread covers 16 lines");
-                cv4 = *reinterpret_cast<const float4*>(a.blob.comp_vec + (size_t)u * nc * D + min(4 * tid, nc * D - 4));
-                cil = a.blob.comp_idx[(size_t)u * nc + min(lane, nc - 1)];
             }
         }
 
         int n_replay = 0;
-        if (MODE == kModeFlush || (MODE == kModeDequant && a.include_buffer)) {
-            const int fill = a.blob.fill[u];
-            n_replay = fill < W ? fill : W;
-        }
+        if constexpr (kFromCodes) n_replay = nr_next;
         if constexpr (PF) n_replay = a.n_tok;
 
         // the replayed tokens (window buffer, or the prompt)
-        bool h16 = a.dm.buffer_format == LQ_BUFFER_FP16;
-        const size_t esz = h16 ? 2 : 4;
+        constexpr size_t esz = H16 ? 2 : 4;
         const void* bk = (const char*)a.blob.buf_k + kvec * (size_t)W * D * esz;
         const void* bv = (const char*)a.blob.buf_v + (size_t)u * W * D * esz;
         const float* bb = a.blob.buf_beta + (size_t)u * W;
@@ -436,7 +526,6 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
         if constexpr (PF) {
             const size_t U = (size_t)a.dm.n_units;
             const size_t KU = U / a.dm.n_v_heads * a.dm.n_k_heads;  // key-head rows per token
-            h16 = false;
             bk = a.pk + kvec * D;
             bq = a.pq + kvec * D;
             bv = a.pv + (size_t)u * D;
@@ -448,10 +537,9 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
         if constexpr (KDA) {
             if (tid < D) lds_G[0][tid] = 1.0;
         }
-        Stage<KDA> pf{};
         float4 pfq = make_float4(0.f, 0.f, 0.f, 0.f);  // prefill: the staged chunk's queries
-        if (n_replay > 0) {
-            pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, ts, 0, n_replay, tid);
+        if (!kFromCodes && n_replay > 0) {
+            pf = fetch_stage<D, NT, KDA, H16>(bk, bv, bb, bg, ts, 0, n_replay, tid);
             if constexpr (PF) pfq = fetch_q<D>(bq, ts.k, 0, n_replay, tid);
         }
 
@@ -465,38 +553,42 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             }
             flag_nonfinite(a.blob.status, bad);  // a NaN or Inf in the caller's start state
         } else {
-            const double sgr = (double)sgr_f;
+            // the smoothing factors and the unit's compensator lines (at most
+            // 16 d floats, in the partial-gram space that the replay only uses
+            // later) pass through LDS
+            float* lds_cv = reinterpret_cast<float*>(&lds_gram[0][0][0]);
+            static_assert(sizeof(lds_gram) >= 16 * D * sizeof(float), "room for 16 lines");
+            if (tid < D) lds_smooth[tid] = hsm;
+            if (nc > 0) *reinterpret_cast<float4*>(lds_cv + 4 * tid) = hcv;
+            int my_slot = -1;  // the row slot holding this lane's row, if any
+            for (int c = 0; c < nc; ++c)
+                if (__builtin_amdgcn_readlane(hcil, c) == n) my_slot = c;
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < NB; ++b) sv[b] = *reinterpret_cast<const float4*>(&lds_smooth[16 * b + 4 * q]);
+            const double sgr = (double)hsg;
             const bool e4m3 = a.dm.code_format == LQ_CODE_E4M3;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 float cv[4];
                 if (e4m3) {
                     // exact: every E4M3 value is an fp32 value
-                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[b], false);
-                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[b], true);
+                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(hw[b], false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(hw[b], true);
                     cv[0] = lo.x;
                     cv[1] = lo.y;
                     cv[2] = hi.x;
                     cv[3] = hi.y;
                 } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) cv[r] = (float)((int)(wd[b] << (24 - 8 * r)) >> 24);
+                    for (int r = 0; r < 4; ++r) cv[r] = (float)((int)(hw[b] << (24 - 8 * r)) >> 24);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) T[b][r] = sgr * (double)cv[r] * (double)pick4(sv[b], r);
             }
             // compensator lines: a row slot adds its line to the four lanes of
-            // that row, a column slot adds one value per row.  The unit's lines
-            // (at most 16 d floats) pass through LDS, in the partial-gram space
-            // that the replay only uses later
+            // that row, a column slot adds one value per row
             if (nc > 0) {
-                float* lds_cv = reinterpret_cast<float*>(&lds_gram[0][0][0]);
-                static_assert(sizeof(lds_gram) >= 16 * D * sizeof(float), "room for 16 lines");
-                *reinterpret_cast<float4*>(lds_cv + 4 * tid) = cv4;
-                int my_slot = -1;  // the row slot holding this lane's row, if any
-                for (int c = 0; c < nc; ++c)
-                    if (__builtin_amdgcn_readlane(cil, c) == n) my_slot = c;
-                __syncthreads();
                 float4 rowv[NB];
                 const float* rv = lds_cv + max(my_slot, 0) * D;
 #pragma unroll
@@ -513,7 +605,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
                     if (c >= nc) break;
-                    const int col = __builtin_amdgcn_readlane(cil, c) - D;
+                    const int col = __builtin_amdgcn_readlane(hcil, c) - D;
                     if (col >= 0) {
                         // the column's block and register are uniform (a scalar
                         // branch picks them); its quad is the lane mask
@@ -568,7 +660,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             const int qb = c & 1;  // chunk parity: keys, queries (prefill), running gate (channel)
             if constexpr (PF) {
                 // a NaN or Inf in the prompt
-                bool bad = !finite4(pf.k) || !finite4(pf.v) || !finite4(pfq) ||
+                bool bad = !finite4(unpack4(pf.k, false)) || !finite4(unpack4(pf.v, false)) || !finite4(pfq) ||
                            !__builtin_isfinite(pf.b) || !__builtin_isfinite(pf.al);
                 if constexpr (KDA) bad = bad || !finite4(pf.g);
                 flag_nonfinite(a.blob.status, bad);
@@ -577,21 +669,22 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 const int x = 4 * tid;
                 const int e = x / D, col = x % D;
                 const bool live = e < ne;  // padding tokens: zero key, zero beta
-                *reinterpret_cast<float4*>(&lds_v[e][col]) = pf.v;
+                const float4 kx = unpack4(pf.k, H16), vx = unpack4(pf.v, H16);
+                *reinterpret_cast<float4*>(&lds_v[e][col]) = vx;
                 if constexpr (PF) *reinterpret_cast<float4*>(&lds_qraw[e][col]) = pfq;
                 if constexpr (KDA) {
-                    *reinterpret_cast<float4*>(&lds_kraw[e][col]) = pf.k;
+                    *reinterpret_cast<float4*>(&lds_kraw[e][col]) = kx;
                     *reinterpret_cast<float4*>(&lds_graw[e][col]) = pf.g;
                 } else {
                     double* kd = &lds_kf[qb][e][col];
-                    kd[0] = live ? (double)pf.k.x : 0.0;
-                    kd[1] = live ? (double)pf.k.y : 0.0;
-                    kd[2] = live ? (double)pf.k.z : 0.0;
-                    kd[3] = live ? (double)pf.k.w : 0.0;
+                    kd[0] = live ? (double)kx.x : 0.0;
+                    kd[1] = live ? (double)kx.y : 0.0;
+                    kd[2] = live ? (double)kx.z : 0.0;
+                    kd[3] = live ? (double)kx.w : 0.0;
                 }
                 if (tid < EB) {
                     lds_b[tid] = tid < ne ? pf.b : 0.f;
-                    lds_al[tid] = pf.al;
+                    if constexpr (!KDA) lds_al[tid] = pf.al;
                 }
                 if (KDA && tid == 0) lds_anyfold = 0;
                 if constexpr (!KDA) {
@@ -672,7 +765,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             }
             // the next chunk, in flight until the next stage
             if (i0 + EB < n_replay) {
-                pf = fetch_stage<D, NT, KDA>(bk, bv, h16, bb, bg, ts, i0 + EB, n_replay, tid);
+                pf = fetch_stage<D, NT, KDA, H16>(bk, bv, bb, bg, ts, i0 + EB, n_replay, tid);
                 if constexpr (PF) pfq = fetch_q<D>(bq, ts.k, i0 + EB, n_replay, tid);
             }
             if constexpr (KDA || PF) __syncthreads();
@@ -903,6 +996,11 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             if (more) gram_issue(c + 1);
             t_update(more);
         }
+        // the next unit's head, requested while this one finishes (from the codes)
+        if (kFromCodes && MODE != kModeDequant && ahead) {
+            u_next = work_unit(k + 1);
+            head_fetch(u_next);
+        }
         // back to S
         if constexpr (KDA) {
             __syncthreads();
@@ -917,7 +1015,14 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             for (int b = 0; b < NB; ++b) T[b] *= gam;
         }
 
+        // the next unit's start, requested a unit ahead (from the codes)
         if constexpr (MODE == kModeDequant) {
+            if (ahead) {
+                u_next = work_unit(k + 1);
+                head_fetch(u_next);
+            }
+            head_settle();
+            if (ahead) chunk0_fetch(u_next);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
                 *reinterpret_cast<float4*>(a.S_out + ((size_t)u * D + n) * D + 16 * b + 4 * q) =
@@ -965,6 +1070,12 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             __syncthreads();
         }
 
+        // (the next unit's first chunk, once its head is in: before the stores
+        // below, which a wait for the head would otherwise also wait for)
+        if constexpr (kFromCodes) {
+            head_settle();
+            if (ahead) chunk0_fetch(u_next);
+        }
         // ---------------- C2: top-n_comp selection (wavefront 0)
         if (wave == 0) {
             // Each round takes every lane's best untaken candidate (the lower
@@ -1053,6 +1164,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             }
         }
 
+        // (the next unit's first chunk, once its window count is in)
         // ---------------- C4: smoothing per key channel
         {
             double am[NV];
@@ -1236,16 +1348,18 @@ hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, 
         if (g <= 0) g = 2048;
         return dim3(a.dm.n_units < g ? a.dm.n_units : g);
     };
-#define LQ_MAT(D_, K_, M_)                                                                              \
-    hipLaunchKernelGGL((materialize_kernel<D_, K_, M_>),                                               \
-                       grid_for(materialize_kernel<D_, K_, M_>),                                \
+    const bool h16 = a.dm.buffer_format == LQ_BUFFER_FP16;
+#define LQ_MAT(D_, K_, M_, H_)                                                                  \
+    hipLaunchKernelGGL((materialize_kernel<D_, K_, M_, H_>), grid_for(materialize_kernel<D_, K_, M_, H_>), \
                        block, 0, st, a)
-#define LQ_MAT_MODE(D_, K_)                                      \
-    do {                                                         \
-        if (mode == kModeInit) LQ_MAT(D_, K_, kModeInit);        \
-        else if (mode == kModeFlush) LQ_MAT(D_, K_, kModeFlush); \
-        else if (mode == kModePrefill) LQ_MAT(D_, K_, kModePrefill); \
-        else LQ_MAT(D_, K_, kModeDequant);                       \
+#define LQ_MAT_MODE(D_, K_)                                                            \
+    do {                                                                               \
+        if (mode == kModeInit) LQ_MAT(D_, K_, kModeInit, false);                       \
+        else if (mode == kModePrefill) LQ_MAT(D_, K_, kModePrefill, false);            \
+        else if (mode == kModeFlush && h16) LQ_MAT(D_, K_, kModeFlush, true);          \
+        else if (mode == kModeFlush) LQ_MAT(D_, K_, kModeFlush, false);                \
+        else if (h16) LQ_MAT(D_, K_, kModeDequant, true);                              \
+        else LQ_MAT(D_, K_, kModeDequant, false);                                      \
     } while (0)
     if (d == 128) {
         if (kda) LQ_MAT_MODE(128, true);
