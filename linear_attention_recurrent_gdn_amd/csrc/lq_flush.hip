@@ -97,6 +97,48 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr double kRescaleBelow = 0x1p-200;  // fold the gate product into T below this
 constexpr double kMinGate = 0x1p-45;        // per-token gate floor inside the flush
 constexpr int kDppRowRor8 = 0x128;          // row_ror:8
+constexpr int kDppRowShr1 = 0x111;          // row_shr:n = 0x110 + n
+constexpr int kDppRowNewBcast0 = 0x150;     // row_newbcast:n = 0x150 + n (lane n of each row to the row)
+
+// The value lane L of each 16-lane row holds, in every lane of that row.
+template <int L>
+__device__ __forceinline__ double row_bcast(double x) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, kDppRowNewBcast0 + L, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), kDppRowNewBcast0 + L, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Steps E2, E2 - 1, .., 1 of a row-wise back substitution: lane e of a row
+// holds y[e], and step e2 folds the (final) y[e2] into every lane,
+// y[e] -= n[e2] y[e2], where lane e's n[e2] is zero for e >= e2.
+template <int E2, int N>
+__device__ __forceinline__ void back_substitute(double& y, const double (&n)[N]) {
+    if constexpr (E2 >= 1) {
+        y = __builtin_fma(-n[E2], row_bcast<E2>(y), y);
+        back_substitute<E2 - 1>(y, n);
+    }
+}
+
+// x * (the value of lane l - SH of the same 16-lane row, or 1 where that
+// lane lies before the row)
+template <int SH>
+__device__ __forceinline__ double times_row_shr(double x) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, kDppRowShr1 - 1 + SH, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0x3FF00000, (int)(uint32_t)(b >> 32), kDppRowShr1 - 1 + SH, 0xF, 0xF,
+                                               false);
+    return x * __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Inclusive prefix product over each 16-lane row: lane l gets the product of
+// lanes row_start .. l (four row_shr steps).
+__device__ __forceinline__ double row_prefix_product(double x) {
+    x = times_row_shr<1>(x);
+    x = times_row_shr<2>(x);
+    x = times_row_shr<4>(x);
+    return times_row_shr<8>(x);
+}
 
 __device__ __forceinline__ v4d mfma(double a, double b, v4d c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
@@ -235,7 +277,11 @@ __device__ __forceinline__ bool finite4(const float4& f) {
 // Inf (rare: a uniform branch around one atomic).
 __device__ __forceinline__ void flag_nonfinite(uint32_t* status, bool bad) {
     if (__builtin_expect(__any(bad), 0)) {
-        if (lane_id() == 0) atomicOr(status, (uint32_t)LQ_DEV_NONFINITE_INPUT);
+        // lane 0, its index recomputed here from an opaque mask (not kept live)
+        uint32_t all = ~0u;
+        asm volatile("" : "+s"(all));
+        if (__builtin_amdgcn_mbcnt_hi(all, __builtin_amdgcn_mbcnt_lo(all, 0u)) == 0)
+            atomicOr(status, (uint32_t)LQ_DEV_NONFINITE_INPUT);
     }
 }
 
@@ -357,7 +403,6 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     __shared__ float lds_kraw[KDA ? EB : 1][KDA ? D : 1];  // channel gate: keys as fetched
     __shared__ float lds_graw[KDA ? EB : 1][KDA ? D : 1];  // channel gate: gates as fetched
     __shared__ float lds_b[EB];
-    __shared__ float lds_al[EB];                            // scalar gate: gates as fetched
     __shared__ double lds_ig[EB];                           // scalar gate: 1 / g_e
     __shared__ double lds_gs[2];                            // scalar gate: fold factor, new g
     __shared__ double lds_G[2][KDA ? D : 1];                // channel gate: running G per column (by chunk parity)
@@ -366,7 +411,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     // small [16][16] matrices padded to 17 columns: a column read across the
     // 16 rows (a matrix-pipe operand) would otherwise hit one LDS bank
     __shared__ double lds_gram[NW][EB][EB + 1];             // partial kf . kb over column slices
-    __shared__ double lds_N[EB][4][4];                      // Diag(beta) L, [e2][q][r] = N[e2][4r + q]
+    __shared__ double lds_N[EB][EB];                        // Diag(beta) L (strictly lower)
     __shared__ double lds_M[EB][EB + 1];                    // (I + N)^-1
     // prefill outputs: queries as fetched and scaled, qf . kb, its future part
     __shared__ float lds_qraw[PF ? EB : 1][PF ? D : 1];
@@ -401,7 +446,11 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     auto work_unit = [&](int k) -> int {
         if constexpr (MODE == kModeFlush) {
             if ((k & 63) == 0) {
-                const int idx = (int)blockIdx.x + (k + lane_id()) * (int)gridDim.x;
+                // the lane index recomputed here (from an opaque mask), not kept live across the unit
+                uint32_t all = ~0u;
+                asm volatile("" : "+s"(all));
+                const int l = (int)__builtin_amdgcn_mbcnt_hi(all, __builtin_amdgcn_mbcnt_lo(all, 0u));
+                const int idx = (int)blockIdx.x + (k + l) * (int)gridDim.x;
                 wl_units = idx < n_work ? a.blob.work[1 + idx] : 0;
             }
             return __builtin_amdgcn_readlane(wl_units, k & 63);
@@ -558,64 +607,68 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             // later) pass through LDS
             float* lds_cv = reinterpret_cast<float*>(&lds_gram[0][0][0]);
             static_assert(sizeof(lds_gram) >= 16 * D * sizeof(float), "room for 16 lines");
-            if (tid < D) lds_smooth[tid] = hsm;
+            if (tid < D) lds_ismooth[tid] = (double)hsm;  // the smoothing factors, in FP64 here
             if (nc > 0) *reinterpret_cast<float4*>(lds_cv + 4 * tid) = hcv;
-            int my_slot = -1;  // the row slot holding this lane's row, if any
-            for (int c = 0; c < nc; ++c)
-                if (__builtin_amdgcn_readlane(hcil, c) == n) my_slot = c;
+            // slot + 1 of each row (x < D) and column (x - D) that is a line, 0 otherwise
+            static_assert(NT >= 2 * D, "one thread per candidate line");
+            if (tid < 2 * D) {
+                int sl = 0;
+                for (int c = 0; c < nc; ++c)
+                    if (__builtin_amdgcn_readlane(hcil, c) == tid) sl = c + 1;
+                lds_slot[tid] = sl;
+            }
             __syncthreads();
-#pragma unroll
-            for (int b = 0; b < NB; ++b) sv[b] = *reinterpret_cast<const float4*>(&lds_smooth[16 * b + 4 * q]);
             const double sgr = (double)hsg;
             const bool e4m3 = a.dm.code_format == LQ_CODE_E4M3;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                float cv[4];
+                double cd[4];  // the codes' values (exact in FP64)
                 if (e4m3) {
                     // exact: every E4M3 value is an fp32 value
                     const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(hw[b], false);
                     const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(hw[b], true);
-                    cv[0] = lo.x;
-                    cv[1] = lo.y;
-                    cv[2] = hi.x;
-                    cv[3] = hi.y;
+                    cd[0] = (double)lo.x;
+                    cd[1] = (double)lo.y;
+                    cd[2] = (double)hi.x;
+                    cd[3] = (double)hi.y;
                 } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) cv[r] = (float)((int)(hw[b] << (24 - 8 * r)) >> 24);
+                    for (int r = 0; r < 4; ++r) cd[r] = (double)((int)(hw[b] << (24 - 8 * r)) >> 24);
                 }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) T[b][r] = sgr * (double)cv[r] * (double)pick4(sv[b], r);
+                const double2 s01 = *reinterpret_cast<const double2*>(&lds_ismooth[16 * b + 4 * q]);
+                const double2 s23 = *reinterpret_cast<const double2*>(&lds_ismooth[16 * b + 4 * q + 2]);
+                T[b][0] = sgr * cd[0] * s01.x;
+                T[b][1] = sgr * cd[1] * s01.y;
+                T[b][2] = sgr * cd[2] * s23.x;
+                T[b][3] = sgr * cd[3] * s23.y;
             }
             // compensator lines: a row slot adds its line to the four lanes of
-            // that row, a column slot adds one value per row
+            // that row, a column slot adds one value per row.  The per-lane
+            // slot reads come from the table above; a wavefront with no lane
+            // concerned skips each step (at most 16 of its 32 value positions
+            // meet a column line).
             if (nc > 0) {
-                float4 rowv[NB];
-                const float* rv = lds_cv + max(my_slot, 0) * D;
+                const int rs = lds_slot[n];
+                if (__any(rs > 0)) {
+                    const float* rv = lds_cv + max(rs - 1, 0) * D;
 #pragma unroll
-                for (int b = 0; b < NB; ++b) rowv[b] = *reinterpret_cast<const float4*>(rv + 16 * b + 4 * q);
-                float colv[16];
+                    for (int b = 0; b < NB; ++b) {
+                        const float4 x = *reinterpret_cast<const float4*>(rv + 16 * b + 4 * q);
+                        if (rs > 0) {
 #pragma unroll
-                for (int c = 0; c < 16; ++c) colv[c] = lds_cv[min(c, nc - 1) * D + n];
-                if (my_slot >= 0) {
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) T[b][r] += (double)pick4(rowv[b], r);
+                            for (int r = 0; r < 4; ++r) T[b][r] += (double)pick4(x, r);
+                        }
+                    }
                 }
 #pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    if (c >= nc) break;
-                    const int col = __builtin_amdgcn_readlane(hcil, c) - D;
-                    if (col >= 0) {
-                        // the column's block and register are uniform (a scalar
-                        // branch picks them); its quad is the lane mask
-                        const int cb = col >> 4, cr = col & 3;
-                        const bool mine = q == ((col >> 2) & 3);
+                for (int b = 0; b < NB; ++b) {
+                    const int4 cs4 = *reinterpret_cast<const int4*>(&lds_slot[D + 16 * b + 4 * q]);
 #pragma unroll
-                        for (int b = 0; b < NB; ++b)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (b == cb && r == cr && mine) T[b][r] += (double)colv[c];
+                    for (int r = 0; r < 4; ++r) {
+                        const int cs = r == 0 ? cs4.x : r == 1 ? cs4.y : r == 2 ? cs4.z : cs4.w;
+                        if (__any(cs > 0)) {
+                            if (cs > 0) T[b][r] += (double)lds_cv[(cs - 1) * D + n];
+                        }
                     }
                 }
             }
@@ -684,24 +737,22 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 }
                 if (tid < EB) {
                     lds_b[tid] = tid < ne ? pf.b : 0.f;
-                    if constexpr (!KDA) lds_al[tid] = pf.al;
                 }
                 if (KDA && tid == 0) lds_anyfold = 0;
                 if constexpr (!KDA) {
                     // the running gate product g_e = g * prod_{l <= e} alpha_l and its
-                    // reciprocal, one token per lane of wavefront 0; the chunk folds g
-                    // into T first when its product could fall below the threshold
+                    // reciprocal, one token per lane of wavefront 0 (lane e holds
+                    // alpha_e as fetched; padding tokens count 1) by a prefix
+                    // product across the lanes; the chunk folds g into T first
+                    // when its product could fall below the threshold
                     if (wave == 0) {
-                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                        __builtin_amdgcn_wave_barrier();
-                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                        double P = 1.0, pre = 1.0;
-#pragma unroll
-                        for (int l = 0; l < EB; ++l) {
-                            const double al = l < ne ? fmax((double)lds_al[l], kMinGate) : 1.0;
-                            P *= al;
-                            if (l <= lane) pre *= al;
-                        }
+                        const double al = lane < ne ? fmax((double)pf.al, kMinGate) : 1.0;
+                        const double pre = row_prefix_product(al);
+                        const double P = __builtin_bit_cast(
+                            double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                         (int)(__builtin_bit_cast(uint64_t, pre) >> 32), EB - 1) << 32) |
+                                        (uint32_t)__builtin_amdgcn_readlane(
+                                            (int)(uint32_t)__builtin_bit_cast(uint64_t, pre), EB - 1));
                         const bool fold = gam * P < kRescaleBelow;
                         const double g = (fold ? 1.0 : gam) * pre;
                         if (lane < EB) lds_ig[lane] = lane < ne ? 1.0 / g : 0.0;
@@ -816,7 +867,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 if (!PF || idx < EB * EB) {
 #pragma unroll
                     for (int w = 0; w < NW; ++w) sum += lds_gram[w][e][e2];
-                    lds_N[e][e2 & 3][e2 >> 2] = e2 < e ? (double)lds_b[e] * sum : 0.0;
+                    lds_N[e][e2] = e2 < e ? (double)lds_b[e] * sum : 0.0;
                 } else if constexpr (PF) {
 #pragma unroll
                     for (int w = 0; w < NW; ++w) sum += lds_gramq[w][e][e2];
@@ -907,38 +958,27 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 const double vp = KDA ? (double)lds_v[e][n] : (double)lds_v[e][n] * lds_ig[e];
                 R4[r] = (double)lds_b[e] * (vp - A4[r]);
             }
-            // M = (I + N)^-1 by right-looking back substitution on one wavefront
-            // (the last: the first computes the scalar gates), while the next
-            // chunk is staged, into LDS.  As vector ALU work beside the products
-            // it slowed the matrix pipe.  Lane (q, m), register r holds
-            // Y[4r + q][m] of Y = M^T; row e2 is final once the rows below it
-            // have been folded in; it is then broadcast to the four row groups
-            // and folded into every row above it (N[e2][e] is zero for e >= e2,
-            // so no masking).  Y[4r + q][m] = M[m][4r + q].  Each step's row of
-            // N is requested two steps ahead.
+            // M = (I + N)^-1 while the next chunk is staged, into LDS, on the
+            // last four wavefronts (the first computes the scalar gates), one row
+            // of M per row group: lane (g, e) of solver wavefront w holds
+            // Y = M[m][e], m = 4 w + g.  M (I + N) = I with N strictly lower
+            // gives M[m][e] = [m == e] - sum_{e2 > e} M[m][e2] N[e2][e]: from
+            // e2 = 15 down, M[m][e2] is final, is broadcast across its row group
+            // (DPP row_newbcast) and folds into every e < e2 (N[e2][e] is zero
+            // for e >= e2, so every lane takes the same step).  Each step waits
+            // on one FMA and one broadcast; lane e's column of N is requested
+            // before the first.  (As vector ALU work beside the products it
+            // slowed the matrix pipe.)
             auto solve_m = [&]() {
-                if (wave != NW - 1) return;
-                v4d Y;
+                if (wave < NW - 4) return;
+                const int e = lane & 15;
+                const int mrow = 4 * (wave - (NW - 4)) + (lane >> 4);
+                double ncol[EB];  // ncol[e2] = N[e2][e]
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Y[r] = (4 * r + q == m) ? 1.0 : 0.0;
-                constexpr int PD = 3;  // prefetch depth, steps
-                double nr[PD][4];
-#pragma unroll
-                for (int d = 0; d < PD - 1; ++d)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) nr[(EB - 1 - d) % PD][r] = lds_N[EB - 1 - d][q][r];
-#pragma unroll
-                for (int e2 = EB - 1; e2 >= 1; --e2) {
-                    if (e2 - (PD - 1) >= 1) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) nr[(e2 - (PD - 1)) % PD][r] = lds_N[e2 - (PD - 1)][q][r];
-                    }
-                    const double y = group_bcast(Y[e2 >> 2], e2 & 3);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) Y[r] = __builtin_fma(-nr[e2 % PD][r], y, Y[r]);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) lds_M[m][4 * r + q] = Y[r];
+                for (int e2 = 1; e2 < EB; ++e2) ncol[e2] = lds_N[e2][e];
+                double Y = e == mrow ? 1.0 : 0.0;
+                back_substitute<EB - 1>(Y, ncol);
+                lds_M[mrow][e] = Y;
             };
             if (more) __syncthreads();  // chunk c's staged data, keys aside, is read
             stage(c + 1, more, solve_m);
@@ -1192,14 +1232,18 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 
         // ---------------- C5: per-row scale and codes
         {
-            // divisions by s_j and sigma_i s_j as products with FP64 reciprocals
-            // (a few ulps of FP64 off the quotient; the codes round at 2^-10 of
-            // a tie or closer only by chance either way)
+            // divisions by s_j, then by sigma_i, as products with FP64
+            // reciprocals (a few ulps of FP64 off the quotient; the codes round
+            // at 2^-10 of a tie or closer only by chance either way).  T is
+            // divided in place: it is not needed after the codes.
             double mx = 0.0;
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmax(mx, fabs(T[b][r] * lds_ismooth[16 * b + 4 * q + r]));
+                for (int r = 0; r < 4; ++r) {
+                    T[b][r] *= lds_ismooth[16 * b + 4 * q + r];
+                    mx = fmax(mx, fabs(T[b][r]));
+                }
             mx = across_rows<true>(mx);
             const bool e4m3 = a.dm.code_format == LQ_CODE_E4M3;
             const float sg = (float)(mx / (e4m3 ? 448.0 : 127.0));
@@ -1214,7 +1258,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                     uint32_t packed = 0u;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const uint32_t code = e4m3_code(T[b][r] * (isg * lds_ismooth[16 * b + 4 * q + r]));
+                        const uint32_t code = e4m3_code(T[b][r] * isg);
                         packed |= (live ? code : 0u) << (8 * r);
                     }
                     crow[4 * b] = packed;
@@ -1225,7 +1269,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                     uint32_t packed = 0u;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const double x = T[b][r] * (isg * lds_ismooth[16 * b + 4 * q + r]);
+                        const double x = T[b][r] * isg;
                         const uint32_t code = (uint32_t)(int)fmin(fmax(rint(x), -127.0), 127.0) & 0xFFu;
                         packed |= (live ? code : 0u) << (8 * r);
                     }
