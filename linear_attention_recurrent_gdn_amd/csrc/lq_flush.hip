@@ -645,8 +645,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             // compensator lines: a row slot adds its line to the four lanes of
             // that row, a column slot adds one value per row.  The per-lane
             // slot reads come from the table above; a wavefront with no lane
-            // concerned skips each step (at most 16 of its 32 value positions
-            // meet a column line).
+            // concerned skips each step.
             if (nc > 0) {
                 const int rs = lds_slot[n];
                 if (__any(rs > 0)) {
@@ -660,17 +659,22 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                         }
                     }
                 }
+                // value positions (4 b + r) that some column line meets in some
+                // row quad: the same for every wavefront, a scalar mask
+                uint32_t pos = 0u;
+                for (int c = 0; c < nc; ++c) {
+                    const int col = __builtin_amdgcn_readlane(hcil, c) - D;
+                    if (col >= 0) pos |= 1u << (4 * (col >> 4) + (col & 3));
+                }
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const int4 cs4 = *reinterpret_cast<const int4*>(&lds_slot[D + 16 * b + 4 * q]);
+                for (int b = 0; b < NB; ++b)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int cs = r == 0 ? cs4.x : r == 1 ? cs4.y : r == 2 ? cs4.z : cs4.w;
-                        if (__any(cs > 0)) {
+                        if (pos & (1u << (4 * b + r))) {
+                            const int cs = lds_slot[D + 16 * b + 4 * q + r];
                             if (cs > 0) T[b][r] += (double)lds_cv[(cs - 1) * D + n];
                         }
                     }
-                }
             }
         }
 
@@ -1175,29 +1179,30 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                     *reinterpret_cast<float4*>(cvb + (size_t)(rslot - 1) * D + 16 * b + 4 * q) =
                         make_float4((float)T[b][0], (float)T[b][1], (float)T[b][2], (float)T[b][3]);
             }
-            // column lines, one chosen column at a time: its block and register
-            // are uniform (a scalar branch picks them), its quad is the lane
-            // mask; where a row line crosses it, the row line keeps the value.
-            // The chosen candidates come in one read (lane c holds round c's),
-            // a column's slot is its rank among them (a ballot), so the loop
-            // itself waits for no LDS read
+            // column lines: the value positions (4 b + r) that a chosen column
+            // meets in some row quad form a scalar mask (the same for every
+            // wavefront); at such a position a lane whose column is chosen
+            // (its slot from the table) writes the line's value for its row
+            // and zeroes it.  Where a row line crosses it, the row line keeps
+            // the value.
             const int chl = lds_chosen[max(min(lane, nc - 1), 0)];
+            uint32_t pos = 0u;
             for (int c = 0; c < nc; ++c) {
-                const int idx = __builtin_amdgcn_readlane(chl, c);
-                if (idx < D) continue;
-                const int col = idx - D, cb = col >> 4, cr = col & 3;
-                const bool mine = q == ((col >> 2) & 3);
-                const int rank = __popcll(__ballot(lane < nc && chl < idx));
-                float* dst = cvb + (size_t)rank * D + n;
+                const int col = __builtin_amdgcn_readlane(chl, c) - D;
+                if (col >= 0) pos |= 1u << (4 * (col >> 4) + (col & 3));
+            }
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (b == cb && r == cr && mine) {
-                            *dst = rslot ? 0.0f : (float)T[b][r];
+                for (int r = 0; r < 4; ++r) {
+                    if (pos & (1u << (4 * b + r))) {
+                        const int cs = lds_slot[D + 16 * b + 4 * q + r];
+                        if (cs > 0) {
+                            cvb[(size_t)(cs - 1) * D + n] = rslot ? 0.0f : (float)T[b][r];
                             T[b][r] = 0.0;
                         }
-            }
+                    }
+                }
             if (rslot) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) T[b] = v4d{0.0, 0.0, 0.0, 0.0};
