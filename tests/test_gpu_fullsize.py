@@ -111,3 +111,20 @@ def test_large_launch_parity(name):
     picks.update(int(x) for x in rng.choice(wl.n_units, 9, replace=False))
     rep = parity.run(wl, checked=sorted(picks), dequant_every=wl.window // 2 + 3)
     assert rep.flushes >= 1 and rep.decode_calls == wl.decode
+
+
+@pytest.mark.parametrize("d,n_seq,gate", [(128, 640, "scalar"), (64, 1280, "scalar"), (128, 640, "channel")])
+def test_flush_more_than_64_items_per_workgroup(d, n_seq, gate):
+    # Every unit due at each boundary, more units than 64 per resident
+    # workgroup of the boundary kernel (256 workgroups at d = 128, 512 at
+    # d = 64): each workgroup reads its part of the work list 64 items at a
+    # time, so the later items come from a second read.  Sampled units include
+    # the last ones (item 79 of their workgroup at d = 128).
+    base = "gdn_decode" if gate == "scalar" else "kda_decode"
+    wl = I.WORKLOADS[base].scaled(name=f"many_{d}_{gate}", n_seq=n_seq, n_v_heads=32, n_k_heads=32, d=d,
+                                  window=2, prefill=8, decode=4, outlier_rows=0, outlier_cols=0)
+    assert wl.n_units > 64 * (256 if d == 128 else 512)
+    units = sample_units(wl, 12)
+    units += list(range(wl.n_units - 4, wl.n_units))
+    rep = parity.run(wl, n_tokens=4, checked=units, dequant_every=3)
+    assert rep.flushes == 2
