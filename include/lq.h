@@ -163,9 +163,9 @@ int32_t lq_state_init(const lq_config* cfg, void* state, const float* S0, hipStr
  * One decode token for every sequence.  Per unit: append (k, v, beta, gate)
  * to the window buffer, then write o = S_j q where S_j is the stored
  * window-start state advanced through the buffered tokens (the current one
- * included): the abstract's "outputs from the fixed low-bit state together
- * with high-precision buffered updates".  The INT8 codes, scales, smoothing
- * and compensators are read, never written.  A unit whose window is already
+ * included): per the abstract, a token inside a window reads the 8-bit state
+ * held since the window began plus the exactly kept tokens since.  The INT8
+ * codes, scales, smoothing and compensators are read, never written.  A unit whose window is already
  * full (lq_window_flush was not called) gets o = NaN and sets
  * LQ_DEV_WINDOW_OVERFLOW.
  */
@@ -174,9 +174,10 @@ int32_t lq_decode_step(const lq_config* cfg, void* state, const float* q, const 
                        hipStream_t stream);
 
 /*
- * Window-boundary requantization: the arXiv 2609.38166 abstract ("Abstract
- * (arXiv)" section, mlsanity.com paper page) leaps over a window of tokens and
- * quantizes the state once, at the window's end, keeping the largest outliers
+ * Window-boundary requantization: per the arXiv 2609.38166 abstract ("Abstract
+ * (arXiv)" section, mlsanity.com paper page) the state goes through a whole
+ * window of tokens unquantized and is requantized a single time when the
+ * window closes, keeping the largest outliers
  * as Compensator Tokens and smoothing the residual before quantization; the
  * bedrocknews.com review adds that this happens at the window boundary instead
  * of after every update.  Every unit whose window is full (fill == window),
@@ -235,8 +236,8 @@ int32_t lq_prefill(const lq_config* cfg, void* state, const float* S0, int32_t n
  * the arXiv 2609.38166 abstract ("Abstract (arXiv)" section, mlsanity.com
  * paper page) keeps for the whole window, with the Compensator Tokens added
  * back -- or, with include_buffer != 0, that state advanced through the
- * buffered tokens: the abstract's fixed low-bit state together with the
- * high-precision buffered updates, i.e. the state after the last decode step.
+ * buffered tokens, i.e. what the last decode step read its output from (the
+ * window-start state plus the exactly kept tokens since).
  * For inspection and checkpoint conversion.
  */
 int32_t lq_dequant_state(const lq_config* cfg, const void* state, float* S_out,
@@ -246,7 +247,7 @@ int32_t lq_dequant_state(const lq_config* cfg, const void* state, float* S_out,
  * The FP32-state comparison step: S (fp32, in place) advanced by one token
  * and o = S_t q, with the same inputs and layouts as lq_decode_step.  This is
  * the FP32 baseline the pages measure against (bedrocknews.com review: the
- * baseline is FP32 inference of the same models).
+ * comparison runs the same models with a 32-bit float state).
  */
 int32_t lq_fp32_decode_step(const lq_config* cfg, float* S, const float* q, const float* k,
                             const float* v, const float* beta, const float* gate, float* o,

@@ -3,8 +3,8 @@
 // decode_q8_kernel: one token of the windowed 8-bit scheme (INT8 codes, or
 // E4M3 8-bit floats: the review says INT8, the abstract only "8-bit").  The arXiv
 // 2609.38166 abstract ("Abstract (arXiv)" section, mlsanity.com paper page):
-// within a window, outputs are computed from the fixed low-bit state together
-// with high-precision buffered updates.  The bedrocknews.com review: the cost
+// a token inside a window takes its output from the 8-bit state, unchanged
+// since the window began, and the window's full-precision tokens.  The bedrocknews.com review: the cost
 // is recomputing the buffered tokens' contributions, traded for far less
 // state traffic.  Per unit (sequence x value head), with the window-start
 // state S_hat = Diag(sigma) Q Diag(s) + sum_c v_c k_c^T and buffered tokens
@@ -36,7 +36,7 @@
 // no MFMA.
 //
 // decode_fp32_kernel: the FP32-state step the pages compare against (the
-// bedrocknews.com review: the baseline is FP32 inference).  The row form
+// bedrocknews.com review: the comparison keeps a 32-bit float state).  The row form
 // x = g * S[i,:];  S[i,:] = x + beta (v_i - x.k) k;  o_i = x.q + beta (v_i - x.k)(k.q)
 // reads and writes each 512-byte row once.
 

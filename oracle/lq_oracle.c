@@ -175,8 +175,8 @@ static int8_t code_round(int fmt, double x) {
  * and, when o is given, o = S q with the updated S (READING: output after the
  * update, so a token sees its own write).
  *
- * [ABS]: GDN and KDA compress the context into a fixed-size recurrent state
- * that is read and updated at every token.  The recurrence itself is not
+ * [ABS]: GDN and KDA hold everything seen so far in a recurrent state whose
+ * size does not grow with the context; every token reads and updates it.  The recurrence itself is not
  * printed on the pages; this is the gated delta rule of the works the pages
  * cite ("Gated Delta Networks: Improving Mamba2 with Delta Rule"; "Kimi
  * Linear"), in the orientation the invariants above fix.
@@ -467,8 +467,9 @@ int orc_dequant(int fmt, int n_units, int dk, int dv, int n_c, const int8_t* cod
 /* O3: output from the fixed low-bit state plus the buffered window.         */
 /* ------------------------------------------------------------------------ */
 /*
- * [ABS]: inside a window, outputs come from the fixed low-bit state together
- * with high-precision buffered updates.  [REV]: the price is recomputing the
+ * [ABS]: inside a window a token's output is formed from the 8-bit state,
+ * which stays unchanged until the window closes, plus the window's tokens
+ * kept at full precision.  [REV]: the price is recomputing the
  * contributions of the buffered tokens.
  *
  * With the window-start state S_hat and buffered tokens 1..n (the current
@@ -543,8 +544,8 @@ int orc_replay_output(int fmt, int n_units, int dk, int dv, int n_c, int gate_ki
 /* O2: the windowed scheme, definitional ("fake-quant") form, end to end.    */
 /* ------------------------------------------------------------------------ */
 /*
- * [ABS]: per-window quantization leaps over a window of tokens and quantizes
- * the state only once at its end.  [REV]: the state is quantized once at the
+ * [ABS]: the state runs unquantized through a whole window and is quantized
+ * a single time, when the window closes.  [REV]: the state is quantized once at the
  * window boundary instead of after every update.
  *
  * Start: (codes, sigma, s, comps) = Qz(S0) and S_hat = their dequantization.

@@ -3,9 +3,9 @@
 O3 (output from the fixed low-bit state plus the buffered window, by a reverse
 pass over the buffer) and O2 (the definitional windowed run) follow the arXiv
 2609.38166 abstract ("Abstract (arXiv)" section of the mlsanity.com paper
-page): within a window outputs come from the fixed low-bit state together with
-high-precision buffered updates, and the state is quantized only once at the
-window's end.  With quantization out of the picture the windowed form must
+page): a token inside a window reads the 8-bit state, unchanged since the
+window began, plus the window's full-precision tokens, and the state is
+requantized a single time, when the window closes.  With quantization out of the picture the windowed form must
 reproduce the plain recurrence; that, an exact closed-form sum, and the
 linearity of compensator tokens pin them.
 """
