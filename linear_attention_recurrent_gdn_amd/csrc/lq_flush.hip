@@ -210,27 +210,6 @@ __device__ __forceinline__ int reduce_columns(double (&v)[NV], int m) {
     }
 }
 
-// The value that lane m of row group g (lanes 16g .. 16g + 15) holds, in lane
-// m of every row group (g uniform): v_permlane32_swap replicates the half
-// that holds g, v_permlane16_swap then the row of that half.
-__device__ __forceinline__ double group_bcast(double x, int g) {
-    const uint64_t b = __builtin_bit_cast(uint64_t, x);
-    int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
-    {
-        const auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-        const auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-        lo = (g & 2) ? (int)pl[1] : (int)pl[0];
-        hi = (g & 2) ? (int)ph[1] : (int)ph[0];
-    }
-    {
-        const auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-        const auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-        lo = (g & 1) ? (int)pl[1] : (int)pl[0];
-        hi = (g & 1) ? (int)ph[1] : (int)ph[0];
-    }
-    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
-
 // Wavefront maximum of a double, in every lane: DPP inside each 16-lane row,
 // then the row swaps.  fmax returns one of its inputs, so the result equals
 // some lane's value exactly.
@@ -908,16 +887,15 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
                 gam = lds_gs[1];
             }
             // every wavefront: A = T Kf^T (prefill: also Aq = T Qf^T, register r:
-            // token 4r + q, row n) on the matrix pipe.  The keys of block b + 1
-            // are requested before the products of block b; the scheduling
-            // barriers keep that order.
+            // token 4r + q, row n) on the matrix pipe, one accumulator each (the
+            // pipe forwards a dependent accumulator to the next product).  The
+            // keys of block b + 1 are requested before the products of block b;
+            // the scheduling barriers keep that order.
             v4d Aq4 = {0.0, 0.0, 0.0, 0.0};
             v4d A4;
             {
                 const double(*kf)[KP] = kf_of(c & 1);
-                v4d acc[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = v4d{0.0, 0.0, 0.0, 0.0};
+                v4d acc = {0.0, 0.0, 0.0, 0.0};
                 double kc[2][4], qc[4];
                 auto load_keys = [&](int b, double* kd) {
 #pragma unroll
@@ -934,25 +912,15 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
 #pragma unroll
                         for (int r = 0; r < 4; ++r) qc[r] = lds_qf[m][16 * b + 4 * q + r];
                     }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc = mfma(kc[cur][r], T[b][r], acc);
                     if constexpr (PF) {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[0] = mfma(kc[cur][r], T[b][r], acc[0]);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[2] = mfma(qc[r], T[b][r], acc[2]);
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[r] = mfma(kc[cur][r], T[b][r], acc[r]);
+                        for (int r = 0; r < 4; ++r) Aq4 = mfma(qc[r], T[b][r], Aq4);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                if constexpr (PF) {
-                    // one accumulator each for keys and queries (registers are
-                    // short here; the matrix pipe forwards a dependent accumulator)
-                    Aq4 = acc[2];
-                    A4 = acc[0];
-                } else {
-                    A4 = (acc[0] + acc[1]) + (acc[2] + acc[3]);  // register r: A[token 4r + q][row n]
-                }
+                A4 = acc;  // register r: A[token 4r + q][row n]
             }
             // R = (v' - A) Diag(beta): register r -> token 4r + q, row n
             v4d R4;
@@ -987,12 +955,11 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             if (more) __syncthreads();  // chunk c's staged data, keys aside, is read
             stage(c + 1, more, solve_m);
             // C = M R (per row): register r -> token 4r + q, row n
-            v4d C4a = {0.0, 0.0, 0.0, 0.0}, C4b = {0.0, 0.0, 0.0, 0.0};
-            C4a = mfma(lds_M[m][q], R4[0], C4a);
-            C4b = mfma(lds_M[m][4 + q], R4[1], C4b);
-            C4a = mfma(lds_M[m][8 + q], R4[2], C4a);
-            C4b = mfma(lds_M[m][12 + q], R4[3], C4b);
-            const v4d C4 = C4a + C4b;
+            v4d C4 = {0.0, 0.0, 0.0, 0.0};
+            C4 = mfma(lds_M[m][q], R4[0], C4);
+            C4 = mfma(lds_M[m][4 + q], R4[1], C4);
+            C4 = mfma(lds_M[m][8 + q], R4[2], C4);
+            C4 = mfma(lds_M[m][12 + q], R4[3], C4);
             // prefill outputs of the chunk's tokens: o_e = T qf_e + sum_{e' <= e} C_e' (kb_e' . qf_e)
             const bool outs = PF && a.po != nullptr;
             if constexpr (PF) {
@@ -1253,32 +1220,30 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             const bool e4m3 = a.dm.code_format == LQ_CODE_E4M3;
             const float sg = (float)(mx / (e4m3 ? 448.0 : 127.0));
             if (q == 0) a.blob.sigma[(size_t)u * D + n] = sg;
+            // an all-zero row (sigma 0) gets 1/sigma = 0, so every x below is 0
+            // and takes code 0
             const double isg = sg != 0.0f ? 1.0 / (double)sg : 0.0;
-            // an all-zero row (sigma 0) takes code 0 by a select, not a branch
-            const bool live = sg != 0.0f;
             uint32_t* crow = reinterpret_cast<uint32_t*>(a.blob.codes + ((size_t)u * D + n) * D + 4 * q);
             if (e4m3) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     uint32_t packed = 0u;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint32_t code = e4m3_code(T[b][r] * isg);
-                        packed |= (live ? code : 0u) << (8 * r);
-                    }
+                    for (int r = 0; r < 4; ++r) packed |= e4m3_code(T[b][r] * isg) << (8 * r);
                     crow[4 * b] = packed;
                 }
             } else {
 #pragma unroll
+                // |x| <= 127 (1 + 2^-23) here, so rint gives a code in [-127, 127]
+                // (the integer clamp only guards a non-finite state); the four
+                // low bytes are packed by byte permutes
                 for (int b = 0; b < NB; ++b) {
-                    uint32_t packed = 0u;
+                    int k[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const double x = T[b][r] * isg;
-                        const uint32_t code = (uint32_t)(int)fmin(fmax(rint(x), -127.0), 127.0) & 0xFFu;
-                        packed |= (live ? code : 0u) << (8 * r);
-                    }
-                    crow[4 * b] = packed;
+                    for (int r = 0; r < 4; ++r) k[r] = min(max((int)rint(T[b][r] * isg), -127), 127);
+                    const uint32_t lo = __builtin_amdgcn_perm((uint32_t)k[1], (uint32_t)k[0], 0x0c0c0400u);
+                    const uint32_t hi = __builtin_amdgcn_perm((uint32_t)k[3], (uint32_t)k[2], 0x0c0c0400u);
+                    crow[4 * b] = lo | (hi << 16);
                 }
             }
         }

@@ -253,6 +253,72 @@ def test_results_do_not_depend_on_batch_position():
     assert torch.equal(outs["solo"][1], outs["batch"][1])
 
 
+def _degenerate_start(U, d, seed):
+    """Start states that take the quantizer's edge paths: unit 0 zero; unit 1
+    random with its first d/2 rows and two columns zero; unit 2 rank one with
+    zeros in both factors; unit 3 nonzero only on one row and one column (two
+    compensator lines take everything, the residual is zero)."""
+    rng = np.random.default_rng(seed)
+    S = np.zeros((U, d, d), np.float32)
+    S[1] = rng.standard_normal((d, d))
+    S[1, : d // 2] = 0.0
+    S[1, :, [3, d - 5]] = 0.0
+    a, b = rng.standard_normal(d), rng.standard_normal(d)
+    a[::3] = 0.0
+    b[1::4] = 0.0
+    S[2] = np.outer(a, b)
+    S[3, 7, :] = rng.standard_normal(d)
+    S[3, :, 11] = rng.standard_normal(d)
+    return S
+
+
+@pytest.mark.parametrize("fmt", ["int8", "e4m3"])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_degenerate_states(d, gate, fmt):
+    # zero units, zero rows and columns, a rank-one state and a state the two
+    # compensator lines empty: at init and after a window of tokens that do
+    # not write (beta = 0, so zero rows stay zero), the codes, scales,
+    # smoothing and lines match the oracle's; a zero row has sigma 0 and code
+    # 0 throughout; outputs match the plain recurrence; no flag is raised
+    base = "gdn_decode" if gate == "scalar" else "kda_decode"
+    wl = small(base, name=f"degenerate_{gate}_{d}_{fmt}", n_seq=1, n_v_heads=4, n_k_heads=4, d=d,
+               window=4, n_comp=2, prefill=0, outlier_rows=0, outlier_cols=0, code_format=fmt)
+    cfg = _cfg(wl)
+    U = wl.n_units
+    S0 = _degenerate_start(U, d, seed=d + (gate == "channel"))
+    st = lq.new_state(cfg)
+    views = lq.state_views(cfg, st)
+    lq.lq_state_init(cfg, st, torch.from_numpy(S0).cuda())
+    torch.cuda.synchronize()
+    rep = parity.Report(wl.name)
+    units = np.arange(U)
+    gb = parity.blob_host(views, units, fmt)
+    parity.check_quantizer(S0.astype(np.float64), gb, wl.n_comp, rep, "init")
+    S_hat = orc.dequant(gb)
+    o = torch.empty((wl.n_seq, wl.n_v_heads, d), device="cuda")
+    for t in range(wl.window):
+        tk = I.token(wl, t)
+        tk["beta"] = np.zeros_like(tk["beta"])
+        dev = {k: torch.from_numpy(v).cuda() for k, v in tk.items()}
+        lq.lq_decode_step(cfg, st, dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], o)
+        pu = I.tokens_per_unit(wl, {k: v[None] for k, v in tk.items()})
+        S_hat, o_ref = orc.recurrence(S_hat, pu["q"], pu["k"], pu["v"], pu["beta"], pu["gate"])
+        o_gpu = o.view(U, d).cpu().numpy()
+        scale = max(float(np.abs(o_ref).max()), 1e-30)
+        np.testing.assert_allclose(o_gpu, o_ref[0], rtol=0, atol=1e-5 * scale, err_msg=f"token {t}")
+    lq.lq_window_flush(cfg, st, None)
+    torch.cuda.synchronize()
+    gb = parity.blob_host(views, units, fmt)
+    parity.check_quantizer(S_hat, gb, wl.n_comp, rep, "flush")
+    zero_rows = np.abs(S_hat).max(axis=2) == 0.0
+    assert zero_rows[0].all() and zero_rows[1, : d // 2].all()
+    assert (gb.sigma[zero_rows] == 0.0).all()
+    assert (gb.codes[zero_rows] == 0).all()
+    assert int(views["fill"].max()) == 0
+    assert lq.lq_read_status(cfg, st) == 0
+
+
 def test_repeatable_bitwise():
     wl = small("kda_decode", name="repeat", n_seq=2, n_v_heads=3, n_k_heads=3, window=8, n_comp=3,
                prefill=0)
