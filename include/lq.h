@@ -165,9 +165,9 @@ int32_t lq_state_init(const lq_config* cfg, void* state, const float* S0, hipStr
  * window-start state advanced through the buffered tokens (the current one
  * included): per the abstract, a token inside a window reads the 8-bit state
  * held since the window began plus the exactly kept tokens since.  The INT8
- * codes, scales, smoothing and compensators are read, never written.  A unit whose window is already
- * full (lq_window_flush was not called) gets o = NaN and sets
- * LQ_DEV_WINDOW_OVERFLOW.
+ * codes, scales, smoothing and compensators are read, never written.  A unit
+ * whose window is already full (lq_window_flush was not called) gets o = NaN
+ * and sets LQ_DEV_WINDOW_OVERFLOW.
  */
 int32_t lq_decode_step(const lq_config* cfg, void* state, const float* q, const float* k,
                        const float* v, const float* beta, const float* gate, float* o,
