@@ -6,6 +6,12 @@ One step = one decode token for every (sequence, head) unit of every layer
 of every layer whose units filled their window on that token.  Inputs are
 synthetic, seeded, and resident in HBM before the timed region starts.
 
+Boundary beside the decode.  With several layers, a layer's boundary call
+depends only on that layer's decode of the token, and only that layer's next
+decode depends on it; it runs on a second stream (--flush-cus: its persistent
+grid limited to 96 of the 256 CUs by default) while the next layers decode on
+the rest, and the layer's next decode waits for it through an event.
+
 Steady state.  Windows are staggered so that any run of steps carries its
 share of boundary work and sees every fill position of the window: with
 several layers, layer l starts its windows floor(l W / L) tokens later than
@@ -41,6 +47,7 @@ Prints one JSON line:
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -81,6 +88,10 @@ def parse_args(argv=None):
                     help="independent copies of every state, each token run on every copy in turn: with "
                          "enough copies the working set exceeds the 256 MB last-level cache, so every launch "
                          "reads its state from HBM (throughput counts the units of all copies)")
+    ap.add_argument("--flush-cus", type=int, default=-1,
+                    help="multi-layer workloads: run each layer's boundary call on a second stream, on this many "
+                         "CUs (lq_config.flush_cus), beside the next layers' decode steps; 0 runs it on the "
+                         "decode stream after the token's last layer; -1 (default) picks 96 of 256 (measured best of 64-160)")
     return ap.parse_args(argv)
 
 
@@ -449,6 +460,16 @@ def main(argv=None):
     buffer_format = {"fp32": lq.LQ_BUFFER_FP32, "fp16": lq.LQ_BUFFER_FP16}[args.buffer]
     cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind, code_format,
                     buffer_format)
+    # Boundary beside the decode (multi-layer stacks): a layer's boundary call
+    # depends only on that layer's decode of the token, and only that layer's
+    # decode of the next token depends on it, so it runs on a second stream
+    # (default priority) with its persistent grid limited to part of the CUs
+    # while the following layers decode on the rest.
+    n_cus_total = torch.cuda.get_device_properties(dev).multi_processor_count
+    flush_cus = args.flush_cus if args.flush_cus >= 0 else min(96, n_cus_total)
+    overlap = L > 1 and 0 < flush_cus
+    fstream = torch.cuda.Stream(dev) if overlap else None
+    cfg_side = dataclasses.replace(cfg, flush_cus=flush_cus) if overlap else cfg
     t_setup = time.perf_counter()
 
     # ---- start states: FP32 prefill through the FP32-state kernel (input synthesis)
@@ -482,21 +503,44 @@ def main(argv=None):
     force_dev = torch.zeros(wl.n_seq, dtype=torch.uint8, device=dev)
     acct = {"decode_bytes": 0.0, "flush_bytes": 0.0, "flush_calls": 0, "flushed_units": 0, "decode_launches": 0}
 
-    def q8_step(t, setup_token=None):
+    pending = [None] * L  # event of a layer's boundary call not yet waited for
+
+    def join_flushes():
         for layer in range(L):
+            if pending[layer] is not None:
+                stream.wait_event(pending[layer])
+                pending[layer] = None
+
+    def q8_step(t, setup_token=None):
+        side = overlap and setup_token is None
+        due_now = {layer for layer in range(L) if (sched.fill[layer] + 1 >= W).any()} if side else set()
+        for layer in range(L):
+            if pending[layer] is not None:
+                stream.wait_event(pending[layer])
+                pending[layer] = None
             tk = tok(layer, t)
             fills = sched.fill[layer]
             acct["decode_bytes"] += R * H * float(sum(decode_bytes(wl, int(j)) for j in fills))
             acct["decode_launches"] += R
             for st in blobs[layer]:
                 lq.lq_decode_step(cfg, st, tk["q"], tk["k"], tk["v"], tk["beta"], tk["gate"], o)
+            if layer in due_now:
+                ev = torch.cuda.Event()
+                ev.record(stream)
+                fstream.wait_event(ev)
+                for st in blobs[layer]:
+                    lq.lq_window_flush(cfg_side, st, None, stream=fstream)
+                done = torch.cuda.Event()
+                done.record(fstream)
+                pending[layer] = done
         for layer, forced, n_due in sched.step(setup_token):
-            fm = None
-            if forced is not None:
-                force_dev.copy_(torch.from_numpy(forced.astype(np.uint8)))
-                fm = force_dev
-            for st in blobs[layer]:
-                lq.lq_window_flush(cfg, st, fm)
+            if layer not in due_now:
+                fm = None
+                if forced is not None:
+                    force_dev.copy_(torch.from_numpy(forced.astype(np.uint8)))
+                    fm = force_dev
+                for st in blobs[layer]:
+                    lq.lq_window_flush(cfg, st, fm)
             acct["flush_calls"] += R
             acct["flushed_units"] += R * H * n_due
             acct["flush_bytes"] += R * H * n_due * flush_bytes(wl, W)
@@ -507,6 +551,7 @@ def main(argv=None):
     assert (sched.fill == sched.offsets).all()
     for t in range(W, W + warmup):
         q8_step(t)
+    join_flushes()
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -517,7 +562,7 @@ def main(argv=None):
     seg_ms = []
     for r in range(n_seg):
         a = t0 + r * K
-        seg_ms.append(timed_graph(torch, stream, lambda: [q8_step(t) for t in range(a, a + K)]))
+        seg_ms.append(timed_graph(torch, stream, lambda: ([q8_step(t) for t in range(a, a + K)], join_flushes())))
     ms_seg = float(np.median(seg_ms))
     flags = [lq.lq_read_status(cfg, st) for bl in blobs for st in bl]
     if any(flags):
@@ -555,7 +600,13 @@ def main(argv=None):
                    + ("per sequence (the workload's offsets)" if wl.stagger else
                       f"across layers (layer l offset floor(l*{W}/{L}))" if L > 1 else
                       f"over {stagger_groups(wl)} sequence groups")
-                   + ", so the timed steps carry their share of boundary requantization"),
+                   + ", so the timed steps carry their share of boundary requantization"
+                   + (f"; each layer's boundary call on a second stream with its grid on {flush_cus} of "
+                      f"{n_cus_total} CUs, beside the next layers' decode steps (that layer's next decode waits "
+                      f"for it; every segment ends when its last boundary call has)" if overlap else
+                      "; boundary calls on the decode stream")),
+        "boundary_stream": ({"flush_cus": flush_cus, "of": n_cus_total, "overlapped": True} if overlap else
+                            {"overlapped": False}),
         "timed_steps": {
             "decode_launches": acct["decode_launches"],
             "flush_calls": acct["flush_calls"],
@@ -644,6 +695,9 @@ def main(argv=None):
         # the boundary work per step if its time scaled with the units flushed
         "flush_model_ms_per_step": (acct["flushed_units"] / steps_timed) / U * fl_s * 1e3,
     }
+    # with the boundary beside the decode: the part of (decode launches +
+    # boundary model) that the step no longer pays
+    checks["boundary_hidden_ms_per_step"] = (dec_floor_ms + checks["flush_model_ms_per_step"]) - ms_seg / K
     if fp32 is not None:
         int8_b = result["timed_steps"]["alg_bytes_per_step"]
         g = d if wl.gate == "channel" else 1

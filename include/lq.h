@@ -97,7 +97,7 @@ typedef struct ihipStream_t* hipStream_t;
  * 1 <= window <= 256; 0 <= n_comp <= 16; n_seq, n_v_heads, n_k_heads >= 1;
  * n_v_heads % n_k_heads == 0; gate_kind in {LQ_GATE_SCALAR, LQ_GATE_CHANNEL};
  * code_format in {LQ_CODE_INT8, LQ_CODE_E4M3};
- * buffer_format in {LQ_BUFFER_FP32, LQ_BUFFER_FP16};
+ * buffer_format in {LQ_BUFFER_FP32, LQ_BUFFER_FP16}; flush_cus >= 0;
  * the unit count n_seq * n_v_heads below 2^31.
  */
 typedef struct lq_config {
@@ -116,6 +116,16 @@ typedef struct lq_config {
                               enter the window rounded to binary16 (half the buffer
                               bytes); the rounded token is then the token everywhere:
                               its own output, later replays, the window-end state */
+    int32_t flush_cus; /* CUs' worth of workgroups in the persistent grid of the
+                          window-boundary kernel (lq_window_flush and its
+                          allocation-free form, lq_state_init, lq_prefill,
+                          lq_dequant_state), which walks the units: at d = 128 a
+                          workgroup fills a CU, so the kernel occupies at most this
+                          many CUs wherever they are.  0: every CU of the
+                          device.  A caller that runs
+                          a layer's boundary on a second stream beside the next
+                          layers' decode steps gives it part of the device; values
+                          above the device's CU count mean every CU */
 } lq_config;
 
 /*

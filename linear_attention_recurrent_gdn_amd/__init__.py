@@ -49,7 +49,7 @@ class LQError(RuntimeError):
 class _CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_seq", "n_v_heads", "n_k_heads", "d_k", "d_v", "window", "n_comp", "gate_kind",
-                 "code_format", "buffer_format")]
+                 "code_format", "buffer_format", "flush_cus")]
 
 
 _LAYOUT_FIELDS = ("total_bytes", "status", "fill", "codes", "sigma", "smooth", "comp_idx",
@@ -73,6 +73,7 @@ class Config:
     gate_kind: int = LQ_GATE_SCALAR
     code_format: int = LQ_CODE_INT8
     buffer_format: int = LQ_BUFFER_FP32
+    flush_cus: int = 0
 
     @property
     def n_units(self) -> int:

@@ -1327,17 +1327,21 @@ __global__ __launch_bounds__(1024) void due_scan_kernel(MatArgs a) {
 
 __global__ void clear_status_kernel(uint32_t* status) { *status = 0u; }
 
-// Workgroups of `kernel` that the device holds at once: the size of a
-// persistent grid, asked of the runtime at every launch (the library keeps no
-// state between calls); 0 when the runtime cannot say (the caller then falls
-// back to a fixed size).
+// Workgroups of `kernel` that the CUs available to it hold at once: the size
+// of a persistent grid, asked of the runtime at every launch (the library
+// keeps no state between calls).  The CUs are the device's, at most max_cus
+// of them when max_cus > 0 (the caller's share for a boundary that runs
+// beside other kernels; the grid stays within it wherever the dispatcher
+// places it, because the d = 128 workgroup needs a whole CU).  0 when the
+// runtime cannot say (the caller then falls back to a fixed size).
 template <typename K>
-int resident_blocks(K kernel, int block) {
+int resident_blocks(K kernel, int block, int max_cus) {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block, 0) != hipSuccess) return 0;
-    return cus * (per > 0 ? per : 1);
+    const int n = (max_cus > 0 && max_cus < cus) ? max_cus : cus;
+    return n * (per > 0 ? per : 1);
 }
 
 hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, hipStream_t st) {
@@ -1358,7 +1362,7 @@ hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, 
         if (e != hipSuccess) return e;
     }
     auto grid_for = [&](auto kernel) {
-        int g = resident_blocks(kernel, block_threads);
+        int g = resident_blocks(kernel, block_threads, a.dm.max_cus);
         if (g <= 0) g = 2048;
         return dim3(a.dm.n_units < g ? a.dm.n_units : g);
     };

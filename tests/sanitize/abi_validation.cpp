@@ -97,6 +97,8 @@ int main() {
     x = base(); x.gate_kind = 2; EXPECT(lq_state_bytes(&x, &nb) == LQ_EINVAL);
     x = base(); x.code_format = -1; EXPECT(lq_state_bytes(&x, &nb) == LQ_EINVAL);
     x = base(); x.buffer_format = 9; EXPECT(lq_state_bytes(&x, &nb) == LQ_EINVAL);
+    x = base(); x.flush_cus = -1; EXPECT(lq_state_bytes(&x, &nb) == LQ_EINVAL);
+    x = base(); x.flush_cus = 100000; EXPECT(lq_state_bytes(&x, &nb) == LQ_OK);
     x = base(); x.n_seq = 0; EXPECT(lq_state_bytes(&x, &nb) == LQ_EINVAL);
     x = base(); x.n_seq = 1 << 30; x.n_v_heads = 4; x.n_k_heads = 4; EXPECT(lq_state_bytes(&x, &nb) == LQ_EUNSUPPORTED);
     x = base(); x.n_seq = (1 << 20); x.n_v_heads = 2047; x.n_k_heads = 1;  // just under 2^31 units

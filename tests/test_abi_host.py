@@ -78,6 +78,7 @@ def test_state_bytes_matches_int8_footprint(lib):
     (dict(gate_kind=7), lq.LQ_EINVAL),
     (dict(code_format=2), lq.LQ_EINVAL),
     (dict(buffer_format=2), lq.LQ_EINVAL),
+    (dict(flush_cus=-1), lq.LQ_EINVAL),
     (dict(window=0), lq.LQ_EINVAL),
     (dict(n_comp=-1), lq.LQ_EINVAL),
     (dict(d_k=96, d_v=96), lq.LQ_EUNSUPPORTED),
