@@ -92,6 +92,9 @@ def parse_args(argv=None):
                     help="multi-layer workloads: run each layer's boundary call on a second stream, on this many "
                          "CUs (lq_config.flush_cus), beside the next layers' decode steps; 0 runs it on the "
                          "decode stream after the token's last layer; -1 (default) picks 96 of 256 (measured best of 64-160)")
+    ap.add_argument("--stagger-layout", default="blocks", choices=("blocks", "interleaved"),
+                    help="one-layer workloads: which sequences share a window offset (consecutive ones, "
+                         "fills falling along the unit index; or sequence s in group s mod G)")
     return ap.parse_args(argv)
 
 
@@ -179,17 +182,27 @@ def stagger_groups(wl) -> int:
     return 1
 
 
-def window_offsets(wl, n_layers):
-    """Fill count [layer, sequence] after the set-up phase (the window offsets)."""
+def window_offsets(wl, n_layers, layout="blocks"):
+    """Fill count [layer, sequence] after the set-up phase (the window offsets).
+
+    One layer: G groups of sequences at offsets W/G apart (G = W for a workload
+    defined with per-sequence offsets, the serving step).  `layout` says which
+    sequences share an offset: "blocks", consecutive sequences, with the
+    offsets falling along the sequence index (so along the unit index, and
+    the decode launch's dispatch order, fills fall too, with one wrap), or
+    "interleaved", sequence s in group s mod G."""
     import numpy as np
 
     W, S = wl.window, wl.n_seq
-    if wl.stagger:  # the workload's own per-sequence offsets
-        return np.tile(np.arange(S) % W, (n_layers, 1))
-    if n_layers > 1:  # layer l starts its windows floor(l W / L) tokens later
+    if n_layers > 1 and not wl.stagger:  # layer l starts its windows floor(l W / L) tokens later
         return np.repeat(((np.arange(n_layers) * W) // n_layers)[:, None], S, axis=1)
-    G = stagger_groups(wl)
-    return ((np.arange(S) % G) * (W // G))[None, :]
+    G = W if wl.stagger else stagger_groups(wl)
+    s = np.arange(S)
+    if layout == "blocks" and S % G == 0:
+        off = (G - 1 - s // (S // G)) * (W // G)
+    else:
+        off = (s % G) * (W // G)
+    return np.tile(off, (n_layers, 1))
 
 
 class Schedule:
@@ -200,11 +213,11 @@ class Schedule:
     after token W - 1 - offset, so it ends the phase `offset` tokens into a
     window; later steps flush only full windows."""
 
-    def __init__(self, wl, n_layers):
+    def __init__(self, wl, n_layers, layout="blocks"):
         import numpy as np
 
         self.W = wl.window
-        self.offsets = window_offsets(wl, n_layers)
+        self.offsets = window_offsets(wl, n_layers, layout)
         self.fill = np.zeros((n_layers, wl.n_seq), np.int64)
         self.force_at = np.where(self.offsets == 0, -1, self.W - 1 - self.offsets)
 
@@ -499,7 +512,7 @@ def main(argv=None):
     tok = lambda layer, t: pool[layer][t % n_pool]
     torch.cuda.synchronize()
 
-    sched = Schedule(wl, L)
+    sched = Schedule(wl, L, args.stagger_layout)
     force_dev = torch.zeros(wl.n_seq, dtype=torch.uint8, device=dev)
     acct = {"decode_bytes": 0.0, "flush_bytes": 0.0, "flush_calls": 0, "flushed_units": 0, "decode_launches": 0}
 
@@ -597,9 +610,10 @@ def main(argv=None):
         "timing": (f"{n_seg} consecutive segments of {K} steps after {W} set-up and {warmup} warm-up steps; "
                    f"each segment one HIP graph replayed once between HIP events; median segment "
                    f"({', '.join(f'{x:.3f}' for x in seg_ms)} ms); windows staggered "
-                   + ("per sequence (the workload's offsets)" if wl.stagger else
+                   + (f"per sequence (the workload's offsets, {W} groups, layout {args.stagger_layout})"
+                      if wl.stagger else
                       f"across layers (layer l offset floor(l*{W}/{L}))" if L > 1 else
-                      f"over {stagger_groups(wl)} sequence groups")
+                      f"over {stagger_groups(wl)} sequence groups (layout {args.stagger_layout})")
                    + ", so the timed steps carry their share of boundary requantization"
                    + (f"; each layer's boundary call on a second stream with its grid on {flush_cus} of "
                       f"{n_cus_total} CUs, beside the next layers' decode steps (that layer's next decode waits "
