@@ -88,3 +88,31 @@ def test_stagger_groups_leave_a_unit_per_cu():
         wl = I.WORKLOADS[name]
         G = bench.stagger_groups(wl)
         assert G > 1 and wl.n_units // G >= 256 and wl.window % G == 0
+
+
+@pytest.mark.parametrize("name", ["gdn_decode", "kda_decode", "gdn_serving"])
+def test_stagger_layouts_same_offsets_different_sequences(name):
+    # both layouts give every offset to the same number of sequences; "blocks"
+    # gives it to a run of consecutive sequences, the offsets falling along
+    # the sequence index (so the fills do along the dispatch order, with one
+    # wrap), "interleaved" to sequences s = g mod G
+    import numpy as np
+
+    wl = I.WORKLOADS[name]
+    blocks = bench.window_offsets(wl, 1, "blocks")[0]
+    inter = bench.window_offsets(wl, 1, "interleaved")[0]
+    assert sorted(blocks.tolist()) == sorted(inter.tolist())
+    G = wl.window if wl.stagger else bench.stagger_groups(wl)
+    run = wl.n_seq // G
+    assert (np.diff(blocks) <= 0).all()
+    assert all(len(set(blocks[i:i + run].tolist())) == 1 for i in range(0, wl.n_seq, run))
+    assert inter[0] == 0 and inter[1] == wl.window // G
+
+
+def test_stack_offsets_ignore_layout():
+    import numpy as np
+
+    wl = I.WORKLOADS["hybrid_stack"]
+    a = bench.window_offsets(wl, wl.layers, "blocks")
+    b = bench.window_offsets(wl, wl.layers, "interleaved")
+    assert (a == b).all() and (a[:, 0] == (np.arange(wl.layers) * wl.window) // wl.layers).all()
