@@ -121,11 +121,12 @@ typedef struct lq_config {
                           allocation-free form, lq_state_init, lq_prefill,
                           lq_dequant_state), which walks the units: at d = 128 a
                           workgroup fills a CU, so the kernel occupies at most this
-                          many CUs wherever they are.  0: every CU of the
-                          device.  A caller that runs
-                          a layer's boundary on a second stream beside the next
-                          layers' decode steps gives it part of the device; values
-                          above the device's CU count mean every CU */
+                          many CUs wherever they are.  0, or a value above the
+                          device's CU count: every CU.  A caller that runs a
+                          layer's boundary on a second stream beside the next
+                          layers' decode steps gives it part of the device.  The
+                          results do not depend on it (each unit is computed the
+                          same way wherever it runs) */
 } lq_config;
 
 /*
