@@ -31,6 +31,14 @@ Three commands:
       the matrix-core counters, the busy fraction of the matrix pipes and the
       FP64 rate the instruction count implies.
 
+  overlap  --trace FILE --out FILE --command "..."
+      Reads a kernel_trace.csv of the stack benchmark (boundary calls on a
+      second stream beside the next layers' decode steps) and writes: the
+      boundary dispatches that ran beside decode launches (count, grid in
+      workgroups, mean duration) against those that ran alone, and, between
+      the first and the last of the former, the decode launches that ran beside
+      a boundary against those that did not (count, mean duration).
+
   hbm
       Practical memory bandwidth of this device for plain streaming kernels:
       the stream_read yardstick (probe/stream_read.hip: 16-byte loads,
@@ -328,6 +336,64 @@ def stats(csv_path: str, cmd: str, out: str, trace_csv: str = None, tail_kernel:
     print(text)
 
 
+def overlap(trace_csv: str, cmd: str, out: str) -> str:
+    """Boundary dispatches beside decode launches, and decode launches beside
+    a boundary, from one kernel trace (times in us)."""
+    dec, flu = [], []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            span = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+            if DECODE_KERNEL in name:
+                dec.append(span)
+            elif "materialize_kernel<" in name and name.split("<")[1].split(",")[2].strip() == "1":
+                wg = int(r["Workgroup_Size_X"])
+                flu.append(span + (int(r["Grid_Size_X"]) // max(wg, 1),))
+    dec.sort()
+    flu.sort()
+    starts = [s for s, _ in dec]
+
+    import bisect
+
+    def beside(a, b):  # decode launches overlapping [a, b)
+        i = bisect.bisect_left(starts, a) - 1
+        i = max(i, 0)
+        out_ = []
+        while i < len(dec) and dec[i][0] < b:
+            if dec[i][1] > a:
+                out_.append(i)
+            i += 1
+        return out_
+
+    with_dec, alone = [], []
+    overlapped_dec = set()
+    for s, e, g in flu:
+        idx = beside(s, e)
+        (with_dec if idx else alone).append((s, e, g))
+        overlapped_dec.update(idx)
+    mean = lambda xs: sum(xs) / len(xs) if xs else float("nan")
+    lines = ["# window-boundary kernel beside the decode (kernel trace)", f"# command: {cmd}", "#"]
+    lines.append(f"# boundary dispatches beside decode launches: {len(with_dec)}, grid "
+                 f"{sorted(set(g for _, _, g in with_dec))} workgroups, mean "
+                 f"{mean([(e - s) / 1e3 for s, e, _ in with_dec]):.1f} us")
+    lines.append(f"# boundary dispatches alone: {len(alone)}, grid {sorted(set(g for _, _, g in alone))} "
+                 f"workgroups, mean {mean([(e - s) / 1e3 for s, e, _ in alone]):.1f} us")
+    if with_dec:
+        a, b = with_dec[0][0], with_dec[-1][1]
+        region = [i for i in range(len(dec)) if a <= dec[i][0] < b]
+        bd = [(dec[i][1] - dec[i][0]) / 1e3 for i in region if i in overlapped_dec]
+        al = [(dec[i][1] - dec[i][0]) / 1e3 for i in region if i not in overlapped_dec]
+        lines.append(f"# decode launches in that span: {len(region)}; beside a boundary {len(bd)}, mean "
+                     f"{mean(bd):.2f} us; alone {len(al)}, mean {mean(al):.2f} us")
+        lines.append("# (the two groups mix window fills in different proportions: compare launches of the "
+                     "same layer and fill for the slowdown itself)")
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    print(text)
+    return text
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -353,6 +419,10 @@ def main(argv=None):
     fl = sub.add_parser("flush")
     fl.add_argument("--workload", default="gdn_decode")
     fl.add_argument("--launches", type=int, default=3)
+    ov = sub.add_parser("overlap")
+    ov.add_argument("--trace", required=True)
+    ov.add_argument("--out", required=True)
+    ov.add_argument("--command", default="")
     m = sub.add_parser("mfma")
     m.add_argument("--workload", default="gdn_decode")
     m.add_argument("--dir", required=True)
@@ -385,6 +455,8 @@ def main(argv=None):
         print(json.dumps(traffic(args.workload, args.fetch, args.write, args.out, args.command), indent=1))
     elif args.cmd == "flush":
         run_flush(args.workload, args.launches)
+    elif args.cmd == "overlap":
+        overlap(args.trace, args.command, args.out)
     elif args.cmd == "mfma":
         print(json.dumps(mfma(args.workload, args.dir, args.out, args.command), indent=1))
     else:
