@@ -319,6 +319,58 @@ def test_degenerate_states(d, gate, fmt):
     assert lq.lq_read_status(cfg, st) == 0
 
 
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_extreme_gates(d, gate):
+    # gates of 0, 1e-20 and 1e-30 (two of them in one 16-token chunk, whose
+    # product underflows FP32 and folds into the boundary's FP64 state), and
+    # channel gates with whole channels at 0 or 1e-25: the decode outputs
+    # follow the plain recurrence from the window-start state, and the
+    # boundary's codes, scales and lines match the oracle's on the state the
+    # recurrence reaches (the boundary floors each gate at 2^-45, the oracle
+    # does not: the difference is below 2^-45 of the state)
+    base = "gdn_decode" if gate == "scalar" else "kda_decode"
+    wl = small(base, name=f"extreme_gates_{gate}_{d}", n_seq=2, n_v_heads=2, n_k_heads=2, d=d,
+               window=20, n_comp=2, prefill=0, outlier_rows=0, outlier_cols=0)
+    cfg = _cfg(wl)
+    U = wl.n_units
+    rng = np.random.default_rng(17 + d)
+    S0 = rng.standard_normal((U, d, d)).astype(np.float32)
+    st = lq.new_state(cfg)
+    views = lq.state_views(cfg, st)
+    lq.lq_state_init(cfg, st, torch.from_numpy(S0).cuda())
+    torch.cuda.synchronize()
+    rep = parity.Report(wl.name)
+    units = np.arange(U)
+    S_hat = orc.dequant(parity.blob_host(views, units, "int8"))
+    o = torch.empty((wl.n_seq, wl.n_v_heads, d), device="cuda")
+    for t in range(wl.window):
+        tk = I.token(wl, t)
+        g = tk["gate"]
+        if gate == "scalar":
+            special = {3: 1e-20, 9: 0.0, 13: 1e-30, 14: 1e-30}
+            if t in special:
+                g[...] = special[t]
+        else:
+            if t in (4, 5):
+                g[..., : d // 4] = 0.0
+            if t in (10, 11, 12):
+                g[..., d // 2: d // 2 + 8] = 1e-25
+        dev = {k: torch.from_numpy(v).cuda() for k, v in tk.items()}
+        lq.lq_decode_step(cfg, st, dev["q"], dev["k"], dev["v"], dev["beta"], dev["gate"], o)
+        pu = I.tokens_per_unit(wl, {k: v[None] for k, v in tk.items()})
+        S_hat, o_ref = orc.recurrence(S_hat, pu["q"], pu["k"], pu["v"], pu["beta"], pu["gate"])
+        o_gpu = o.view(U, d).cpu().numpy()
+        scale = max(float(np.abs(o_ref).max()), 1e-30)
+        np.testing.assert_allclose(o_gpu, o_ref[0], rtol=0, atol=1e-5 * scale, err_msg=f"token {t}")
+    lq.lq_window_flush(cfg, st, None)
+    torch.cuda.synchronize()
+    gb = parity.blob_host(views, units, "int8")
+    parity.check_quantizer(S_hat, gb, wl.n_comp, rep, "flush")
+    assert int(views["fill"].max()) == 0
+    assert lq.lq_read_status(cfg, st) == 0
+
+
 def test_repeatable_bitwise():
     wl = small("kda_decode", name="repeat", n_seq=2, n_v_heads=3, n_k_heads=3, window=8, n_comp=3,
                prefill=0)
