@@ -74,8 +74,9 @@ def parse_args(argv=None):
     ap.add_argument("--n-comp", type=int, default=None, help="override the workload's compensator count (0..16)")
     ap.add_argument("--format", default="int8", choices=("int8", "e4m3"),
                     help="8-bit code format of the stored state")
-    ap.add_argument("--buffer", default="fp32", choices=("fp32", "fp16"),
-                    help="precision of the window buffer's k and v")
+    ap.add_argument("--buffer", default="fp32", choices=("fp32", "fp16", "nform"),
+                    help="window buffer: k and v in fp32 or binary16, or the chain-free form (fp32 k and n; "
+                         "scalar gate, d = 128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-fp32", action="store_true", help="skip the FP32-state comparison loop")
@@ -104,6 +105,8 @@ def parse_args(argv=None):
 
 def entry_bytes(wl) -> int:
     g = wl.d if wl.gate == "channel" else 1
+    if wl.buffer_format == "nform":  # k, the vector n and the gate (beta is inside n)
+        return 4 * (wl.d // wl.group + wl.d) + 4 * g
     e = 2 if wl.buffer_format == "fp16" else 4  # k and v elements
     return e * (wl.d // wl.group + wl.d) + 4 * (1 + g)
 
@@ -262,8 +265,9 @@ def cpu_baseline(wl, target_s, fmt="int8", buffer="fp32", single_thread_s=4.0):
         S0, st = sample(units)
         t0 = time.perf_counter()
         for _ in range(reps):
+            # the chain-free buffer computes the fp32 buffer's result
             orc.windowed_run(S0, st["q"], st["k"], st["v"], st["beta"], st["gate"], wl.window, wl.n_comp,
-                             fmt=fmt, buffer=buffer)
+                             fmt=fmt, buffer="fp32" if buffer == "nform" else buffer)
         return time.perf_counter() - t0
 
     threads = orc.num_threads()
@@ -470,7 +474,7 @@ def main(argv=None):
     torch.cuda.set_stream(stream)
     gen = torch.Generator(dev).manual_seed(1000 + wl.seed)
     code_format = {"int8": lq.LQ_CODE_INT8, "e4m3": lq.LQ_CODE_E4M3}[args.format]
-    buffer_format = {"fp32": lq.LQ_BUFFER_FP32, "fp16": lq.LQ_BUFFER_FP16}[args.buffer]
+    buffer_format = {"fp32": lq.LQ_BUFFER_FP32, "fp16": lq.LQ_BUFFER_FP16, "nform": lq.LQ_BUFFER_NFORM}[args.buffer]
     cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind, code_format,
                     buffer_format)
     # Boundary beside the decode (multi-layer stacks): a layer's boundary call

@@ -86,6 +86,9 @@ typedef struct ihipStream_t* hipStream_t;
 /* window-buffer formats (the buffered tokens' k and v) */
 #define LQ_BUFFER_FP32 0 /* as given */
 #define LQ_BUFFER_FP16 1 /* IEEE binary16, nearest-even, magnitudes above 65504 stored as 65504 */
+#define LQ_BUFFER_NFORM 2 /* scalar gate, d = 128: each entry keeps k, the gate and, in place of v
+                             and beta, the WY-form vector n (fp32), so the decode has no
+                             sequential pass over the window and the boundary is one product */
 
 /* sticky device flags (lq_read_status) */
 #define LQ_DEV_WINDOW_OVERFLOW 0x1u /* lq_decode_step found a full window: that unit's o is NaN, nothing appended */
@@ -97,7 +100,8 @@ typedef struct ihipStream_t* hipStream_t;
  * 1 <= window <= 256; 0 <= n_comp <= 16; n_seq, n_v_heads, n_k_heads >= 1;
  * n_v_heads % n_k_heads == 0; gate_kind in {LQ_GATE_SCALAR, LQ_GATE_CHANNEL};
  * code_format in {LQ_CODE_INT8, LQ_CODE_E4M3};
- * buffer_format in {LQ_BUFFER_FP32, LQ_BUFFER_FP16}; flush_cus >= 0;
+ * buffer_format in {LQ_BUFFER_FP32, LQ_BUFFER_FP16, LQ_BUFFER_NFORM} (NFORM with
+ * gate_kind LQ_GATE_SCALAR and d_k = d_v = 128 only); flush_cus >= 0;
  * the unit count n_seq * n_v_heads below 2^31.
  */
 typedef struct lq_config {
@@ -142,8 +146,8 @@ typedef struct lq_config {
  *   comp_vec  fp32  [units][n_comp][max(d_k,d_v)]  row slot: the row (d_k);
  *                                      column slot: the column (d_v)
  *   buf_k     fp32 or fp16 [n_seq][n_k_heads][window][d_k]  (shared by a key head's value heads)
- *   buf_v     fp32 or fp16 [units][window][d_v]
- *   buf_beta  fp32  [units][window]
+ *   buf_v     fp32 or fp16 [units][window][d_v]  (NFORM: the vectors n, fp32)
+ *   buf_beta  fp32  [units][window]  (NFORM: not used; beta is inside n)
  *   buf_gate  fp32  [units][window] (scalar) or [units][window][d_k] (channel)
  *   work      int32 [1 + units]        scratch of lq_window_flush: count, then the
  *                                      units whose window is due

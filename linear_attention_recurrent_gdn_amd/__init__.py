@@ -31,6 +31,7 @@ LQ_CODE_INT8 = 0
 LQ_CODE_E4M3 = 1
 LQ_BUFFER_FP32 = 0
 LQ_BUFFER_FP16 = 1
+LQ_BUFFER_NFORM = 2
 LQ_DEV_WINDOW_OVERFLOW = 0x1
 LQ_DEV_NONFINITE_INPUT = 0x2
 LQ_DEV_BUFFER_SATURATED = 0x4

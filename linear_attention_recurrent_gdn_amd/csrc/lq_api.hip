@@ -18,11 +18,15 @@ int32_t check_config(const lq_config* c) {
     if (c->n_v_heads % c->n_k_heads != 0) return LQ_EINVAL;
     if (c->gate_kind != LQ_GATE_SCALAR && c->gate_kind != LQ_GATE_CHANNEL) return LQ_EINVAL;
     if (c->code_format != LQ_CODE_INT8 && c->code_format != LQ_CODE_E4M3) return LQ_EINVAL;
-    if (c->buffer_format != LQ_BUFFER_FP32 && c->buffer_format != LQ_BUFFER_FP16) return LQ_EINVAL;
+    if (c->buffer_format != LQ_BUFFER_FP32 && c->buffer_format != LQ_BUFFER_FP16 &&
+        c->buffer_format != LQ_BUFFER_NFORM)
+        return LQ_EINVAL;
     if (c->flush_cus < 0) return LQ_EINVAL;
     if ((int64_t)c->n_seq * c->n_v_heads >= ((int64_t)1 << 31)) return LQ_EUNSUPPORTED;
     if (c->d_k != c->d_v || (c->d_k != 64 && c->d_k != 128)) return LQ_EUNSUPPORTED;
     if (c->window > 256 || c->n_comp > 16) return LQ_EUNSUPPORTED;
+    if (c->buffer_format == LQ_BUFFER_NFORM && (c->gate_kind != LQ_GATE_SCALAR || c->d_k != 128))
+        return LQ_EUNSUPPORTED;
     return LQ_OK;
 }
 

@@ -561,6 +561,268 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     }
 }
 
+
+// The chain-free form of the window buffer (LQ_BUFFER_NFORM, scalar gate).
+// Within a window the gated delta rule's state is, by the WY form of a
+// product of (I - beta k k^T) factors (the compact-WY representation that
+// the works the pages cite use for chunked training),
+//     S_t = g_t S_hat + sum_{i <= t} (g_t / g_i) n_i k_i^T,
+//     n_t = beta_t (v_t - g_t S_hat k_t - sum_{i < t} (g_t / g_i) n_i (k_i . k_t)),
+// with g_t the product of the window's gates up to token t.  A buffer entry
+// keeps k_i (per key head, as in the token form), n_i in place of v_i, and
+// the token's gate; beta is inside n_i.  The ratios g_t / g_i are 2 to the
+// sum of log2 of the gates of the tokens after i, a gate floored at 2^-126
+// (a gate of 0 makes the earlier ratios underflow to 0): the sums are taken
+// newest entry first, so each one is a short sum of the gates that matter,
+// not a difference of two long ones.  The output o_t = S_t q_t needs the dot products of every buffered
+// key with k_t and with q_t, which are independent of each other: the four
+// wavefronts of the workgroup take every fourth entry, with no dependent
+// chain across entries.
+template <int D, int FMT>
+__global__ __launch_bounds__(256) void decode_nform_kernel(DecodeArgs a) {
+    constexpr int EPL = D / kWave;    // vector elements per lane
+    constexpr int RW = D / 4;         // tile rows per wave
+    constexpr int LPR = D / 16;       // lanes per code row
+    constexpr int RPL = kWave / LPR;  // code rows per wave-wide 16-byte load
+    constexpr int NLW = RW / RPL;     // 16-byte tile loads per lane
+    constexpr int P = 4;              // entries requested ahead, per wavefront
+    constexpr int NCP = 8;            // compensator slots held in registers
+    constexpr float kLogFloor = -126.f;
+
+    __shared__ float lds_x[2][D];        // s * k_t, s * q_t
+    __shared__ float lds_add[2][D];      // compensator terms of S_hat k_t, S_hat q_t per row
+    __shared__ float lds_part[4][2][D];  // per wavefront: sum over its entries of ratio (k_i . x) n_i
+    __shared__ float lds_scal[2];        // g_t, k_t . q_t
+
+    if ((int)blockIdx.x >= a.dm.n_units) return;
+    const int u = unit_of_block(blockIdx.x, a.dm);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = lane_id();
+    const int W = a.dm.window;
+    const int nc = a.dm.n_comp;
+    const int s = u / a.dm.n_v_heads;
+    const int h = u - s * a.dm.n_v_heads;
+    const int kh = h / a.dm.group;
+    const size_t kvec = ((size_t)s * a.dm.n_k_heads + kh);
+
+    const int cg = lane % LPR;
+    const int row0 = wave * RW;
+    const uint4* tile = reinterpret_cast<const uint4*>(a.blob.codes + ((size_t)u * D + row0) * D);
+    const int my_row = row0 + min(cg, NLW - 1) * RPL + lane / LPR;
+    uint4 tw[NLW];
+#pragma unroll
+    for (int t = 0; t < NLW; ++t) tw[t] = tile[t * kWave + lane];
+    const float sg_row = a.blob.sigma[(size_t)u * D + my_row];
+    const float v_row = a.v[(size_t)u * D + my_row];
+
+    // every wavefront: the current token's k and q (its dot products need them)
+    const Vec<EPL> kt = load_vec<EPL>(a.k + kvec * D + lane * EPL);
+    const Vec<EPL> qt = load_vec<EPL>(a.q + kvec * D + lane * EPL);
+    const float beta = a.beta[u];
+    const float alpha = a.gate[u];
+    float* bg = a.blob.buf_gate + (size_t)u * W;  // gates of the window's entries
+    const int j_ld = a.blob.fill[u];
+    const int j = __builtin_amdgcn_readfirstlane(j_ld);
+    const bool over = j >= W;
+    const int jr = over ? 0 : j;
+    // log2 of the entries' gates, newest first: lane l of register w holds
+    // entry jr - 1 - (l + 64 w) (0 past the oldest); its ratio exponent is the
+    // sum over the newer entries (an exclusive prefix sum across the lanes,
+    // earlier registers carried) plus the current token's
+    const float lt = fmaxf(__builtin_log2f(alpha), kLogFloor);
+    float rexp[4];
+    float carry = lt;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int idx = jr - 1 - (lane + w * kWave);
+        const float g = bg[max(idx, 0)];
+        const float lg = idx >= 0 ? fmaxf(__builtin_log2f(g), kLogFloor) : 0.f;
+        const float ex = wave_prefix_sum_excl(lg);
+        rexp[w] = carry + ex;
+        carry += lane_value(ex, kWave - 1) + lane_value(lg, kWave - 1);
+    }
+    const float gt = __builtin_exp2f(carry);  // g_t: every buffered gate and the current one
+    auto entry_ratio = [&](int i) {  // g_t / g_i for buffered entry i (uniform)
+        const int r = jr - 1 - i;
+        const int w = r >> 6;
+        const float x = w == 0 ? rexp[0] : w == 1 ? rexp[1] : w == 2 ? rexp[2] : rexp[3];
+        return __builtin_exp2f(lane_value(x, r & 63));
+    };
+
+    // entries i = wave, wave + 4, ... (< jr), through buffer resources; slots
+    // past the end load through a zero-size resource (zeros, no memory access)
+    const size_t kb0 = kvec * (size_t)W * D;
+    const size_t vb0 = (size_t)u * W * D;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (char*)a.blob.buf_k + kb0 * 4, (short)0, W * D * 4, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
+        (char*)a.blob.buf_v + vb0 * 4, (short)0, W * D * 4, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rnone =
+        __builtin_amdgcn_make_buffer_rsrc((char*)a.blob.buf_k, (short)0, 0, kBufferFlags);
+    const int voff = lane * EPL * 4;
+    Vec<EPL> ek[P], en[P];
+    auto load_entry = [&](int i, int p) {
+        const bool live = i < jr;  // uniform
+        const int ie = live ? i : 0;
+        ek[p] = buf_load_f32<EPL>(live ? rk : rnone, voff, ie * D * 4);
+        en[p] = buf_load_f32<EPL>(live ? rn : rnone, voff, ie * D * 4);
+    };
+#pragma unroll
+    for (int p = 0; p < P; ++p) load_entry(wave + 4 * p, p);
+
+    // compensator lines (wavefront 0)
+    int cidx = 0;
+    Vec<EPL> cvec[NCP];
+    Vec<EPL> sm;
+    if (wave == 0) {
+        sm = load_vec<EPL>(a.blob.smooth + (size_t)u * D + lane * EPL);
+        cidx = a.blob.comp_idx[(size_t)u * nc + min(lane, max(nc - 1, 0))];
+#pragma unroll
+        for (int c = 0; c < NCP; ++c)
+            cvec[c] = load_vec<EPL>(a.blob.comp_vec + ((size_t)u * nc + min(c, max(nc - 1, 0))) * D + lane * EPL);
+    }
+
+    // the entries: A1 = sum ratio_i (k_i . k_t) n_i, A2 = sum ratio_i (k_i . q_t) n_i
+    Vec<EPL> A1, A2;
+    for (int e = 0; e < EPL; ++e) A1.e[e] = A2.e[e] = 0.f;
+    for (int s0 = 0; wave + 4 * s0 < jr; s0 += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int i = wave + 4 * (s0 + p);
+            if (i < jr) {  // uniform
+                float pr[2] = {0.f, 0.f};
+                for (int e = 0; e < EPL; ++e) {
+                    pr[0] = __builtin_fmaf(ek[p].e[e], kt.e[e], pr[0]);
+                    pr[1] = __builtin_fmaf(ek[p].e[e], qt.e[e], pr[1]);
+                }
+                wave_sum_all_n<2>(pr);
+                const float ratio = entry_ratio(i);
+                const float w1 = ratio * pr[0], w2 = ratio * pr[1];
+                for (int e = 0; e < EPL; ++e) {
+                    A1.e[e] = __builtin_fmaf(w1, en[p].e[e], A1.e[e]);
+                    A2.e[e] = __builtin_fmaf(w2, en[p].e[e], A2.e[e]);
+                }
+            }
+            load_entry(i + 4 * P, p);
+        }
+    }
+    for (int e = 0; e < EPL; ++e) {
+        lds_part[wave][0][lane * EPL + e] = A1.e[e];
+        lds_part[wave][1][lane * EPL + e] = A2.e[e];
+    }
+
+    if (wave == 0) {
+        // check the token, then S_hat's compensator terms for x = k_t and q_t
+        bool ok = finite(beta) && finite(alpha);
+        for (int e = 0; e < EPL; ++e) ok = ok && finite(qt.e[e]) && finite(kt.e[e]);
+        if (__any(!ok) && lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_NONFINITE_INPUT);
+        Vec<EPL> c1, c2;
+        for (int e = 0; e < EPL; ++e) c1.e[e] = c2.e[e] = 0.f;
+        auto comp = [&](int idx, const Vec<EPL>& w) {
+            if (idx < D) {
+                float pr[2] = {0.f, 0.f};
+                for (int e = 0; e < EPL; ++e) {
+                    pr[0] = __builtin_fmaf(w.e[e], kt.e[e], pr[0]);
+                    pr[1] = __builtin_fmaf(w.e[e], qt.e[e], pr[1]);
+                }
+                wave_sum_all_n<2>(pr);
+                for (int e = 0; e < EPL; ++e) {
+                    c1.e[e] += (lane * EPL + e == idx) ? pr[0] : 0.f;
+                    c2.e[e] += (lane * EPL + e == idx) ? pr[1] : 0.f;
+                }
+            } else {
+                const int col = idx - D;
+                float x1 = lane_value(kt.e[0], col / EPL), x2 = lane_value(qt.e[0], col / EPL);
+                if constexpr (EPL == 2) {
+                    const float y1 = lane_value(kt.e[1], col / EPL), y2 = lane_value(qt.e[1], col / EPL);
+                    x1 = (col & 1) ? y1 : x1;
+                    x2 = (col & 1) ? y2 : x2;
+                }
+                for (int e = 0; e < EPL; ++e) {
+                    c1.e[e] = __builtin_fmaf(w.e[e], x1, c1.e[e]);
+                    c2.e[e] = __builtin_fmaf(w.e[e], x2, c2.e[e]);
+                }
+            }
+        };
+#pragma unroll
+        for (int c = 0; c < NCP; ++c)
+            if (c < nc) comp(__builtin_amdgcn_readlane(cidx, c), cvec[c]);
+        for (int c = NCP; c < nc; ++c)
+            comp(__builtin_amdgcn_readlane(cidx, c),
+                 load_vec<EPL>(a.blob.comp_vec + ((size_t)u * nc + c) * D + lane * EPL));
+        float kq = 0.f;
+        for (int e = 0; e < EPL; ++e) {
+            lds_x[0][lane * EPL + e] = sm.e[e] * kt.e[e];
+            lds_x[1][lane * EPL + e] = sm.e[e] * qt.e[e];
+            lds_add[0][lane * EPL + e] = c1.e[e];
+            lds_add[1][lane * EPL + e] = c2.e[e];
+            kq = __builtin_fmaf(kt.e[e], qt.e[e], kq);
+        }
+        kq = wave_sum_all(kq);
+        if (lane == 0) lds_scal[1] = kq;
+        // append k_t and L_t (the n entry is written per row below)
+        if (!over) {
+            if (h % a.dm.group == 0) store_vec(reinterpret_cast<float*>(a.blob.buf_k) + kb0 + (size_t)j * D + lane * EPL, kt);
+            if (lane == 0) bg[j] = alpha;
+        }
+    }
+    lds_barrier();
+
+    // every wave: its rows of Q (s * k_t) and Q (s * q_t)
+    float xs1[16], xs2[16];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float4 a1 = *reinterpret_cast<const float4*>(&lds_x[0][cg * 16 + 4 * t]);
+        const float4 a2 = *reinterpret_cast<const float4*>(&lds_x[1][cg * 16 + 4 * t]);
+        xs1[4 * t + 0] = a1.x; xs1[4 * t + 1] = a1.y; xs1[4 * t + 2] = a1.z; xs1[4 * t + 3] = a1.w;
+        xs2[4 * t + 0] = a2.x; xs2[4 * t + 1] = a2.y; xs2[4 * t + 2] = a2.z; xs2[4 * t + 3] = a2.w;
+    }
+    float mine1 = 0.f, mine2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < NLW; ++t) {
+        float cf[16];
+        codes_to_float<FMT>(tw[t], cf);
+        float p1 = 0.f, p2 = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            p1 = __builtin_fmaf(cf[c], xs1[c], p1);
+            p2 = __builtin_fmaf(cf[c], xs2[c], p2);
+        }
+        if constexpr (LPR == 8) {
+            p1 = sum8(p1);
+            p2 = sum8(p2);
+        } else {
+            p1 = sum4(p1);
+            p2 = sum4(p2);
+        }
+        if (t == cg) {
+            mine1 = p1;
+            mine2 = p2;
+        }
+    }
+    if (cg < NLW) {
+        const float kq = lds_scal[1];
+        const float y1 = __builtin_fmaf(sg_row, mine1, lds_add[0][my_row]);
+        const float y2 = __builtin_fmaf(sg_row, mine2, lds_add[1][my_row]);
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            s1 += lds_part[w][0][my_row];
+            s2 += lds_part[w][1][my_row];
+        }
+        // n_t = beta (v - g_t S_hat k_t - sum ratio n_i (k_i . k_t));
+        // o = g_t S_hat q_t + sum_{i < t} ratio n_i (k_i . q_t) + n_t (k_t . q_t)
+        const float nt = beta * (v_row - __builtin_fmaf(gt, y1, s1));
+        const float ov = over ? __builtin_nanf("") : __builtin_fmaf(nt, kq, __builtin_fmaf(gt, y2, s2));
+        a.o[(size_t)u * D + my_row] = ov;
+        if (!over) reinterpret_cast<float*>(a.blob.buf_v)[vb0 + (size_t)j * D + my_row] = nt;
+    }
+    if (wave == 0 && lane == 0) {
+        if (over) atomicOr(a.blob.status, (uint32_t)LQ_DEV_WINDOW_OVERFLOW);
+        else a.blob.fill[u] = j + 1;
+    }
+}
+
 template <int D, bool KDA>
 __global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
     constexpr int LPR = D / 8;        // lanes per state row, 8 floats per lane
@@ -698,6 +960,14 @@ void launch_decode_q8_b(const DecodeArgs& a, int d, int gate_kind, hipStream_t s
 }
 
 hipError_t launch_decode_q8(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
+    if (a.dm.buffer_format == LQ_BUFFER_NFORM) {  // scalar gate only (checked by the caller)
+        const dim3 grid(a.dm.n_units), block(256);
+        const bool e4m3 = a.dm.code_format == LQ_CODE_E4M3;
+        (void)d;  // d = 128 only (checked by the caller)
+        if (e4m3) hipLaunchKernelGGL((decode_nform_kernel<128, LQ_CODE_E4M3>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_nform_kernel<128, LQ_CODE_INT8>), grid, block, 0, st, a);
+        return hipGetLastError();
+    }
     if (a.dm.buffer_format == LQ_BUFFER_FP16) launch_decode_q8_b<true>(a, d, gate_kind, st);
     else launch_decode_q8_b<false>(a, d, gate_kind, st);
     return hipGetLastError();

@@ -360,11 +360,46 @@ __device__ __forceinline__ float4 fetch_q(const float* bq, size_t stride, int i0
 
 }  // namespace
 
+
+// x from the lane the DPP control names; 1.0 where that lane lies outside
+// the row (or the wavefront) or the row is masked off.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64_or1(double x) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0x3FF00000, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Exclusive prefix product over the lanes of the wavefront (lane 0 gets 1):
+// shifts of 1, 2, 4, 8 lanes inside each 16-lane row, the row ends carried
+// with row_bcast, then the result moved up one lane.
+__device__ __forceinline__ double wave_prefix_prod_excl(double x) {
+    x *= dpp_f64_or1<0x111>(x);  // row_shr:1
+    x *= dpp_f64_or1<0x112>(x);  // row_shr:2
+    x *= dpp_f64_or1<0x114>(x);  // row_shr:4
+    x *= dpp_f64_or1<0x118>(x);  // row_shr:8
+    x *= dpp_f64_or1<0x142, 0xA>(x);  // row_bcast:15
+    x *= dpp_f64_or1<0x143, 0xC>(x);  // row_bcast:31
+    return dpp_f64_or1<0x138>(x);  // wave_shr:1
+}
+
+__device__ __forceinline__ double lane_value_f64(double x, int l) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // H16: the window buffer holds binary16 keys and values (a flush or dequant
-// that replays it; fp32 otherwise)
-template <int D, bool KDA, int MODE, bool H16>
+// that replays it; fp32 otherwise).  NF: the buffer is in the chain-free form
+// (entries k_i, gate alpha_i and n_i; scalar gate): the window-end state is
+// S = g S_hat + sum_i (g / g_i) n_i k_i^T, one product instead of the replay.
+template <int D, bool KDA, int MODE, bool H16, bool NF = false>
 __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) {
     static_assert(!H16 || MODE == kModeFlush || MODE == kModeDequant, "binary16 applies to the window buffer");
+    static_assert(!NF || (!KDA && !H16 && (MODE == kModeFlush || MODE == kModeDequant)),
+                  "the chain-free buffer: scalar gate, fp32, boundary and dequantization");
     constexpr int NW = D / 16;          // wavefronts = 16-row groups
     constexpr int NT = kWave * NW;      // threads
     constexpr int NB = D / 16;          // 16-column blocks
@@ -496,7 +531,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
     auto chunk0_fetch = [&](int uu) {
         const int nr = replay_count(__builtin_amdgcn_readfirstlane(hfill));
         nr_next = nr;
-        if (nr > 0) {
+        if (!NF && nr > 0) {
             const void *bk, *bv;
             const float *bb, *bg;
             unit_buffers(uu, bk, bv, bb, bg);
@@ -657,6 +692,74 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             }
         }
 
+        // ---------------- B (chain-free buffer): S = g S_hat + sum_i (g / g_i) n_i k_i^T
+        if constexpr (NF) {
+            if (n_replay > 0) {
+                // g / g_i for every entry (exclusive suffix products of the
+                // gates, floored at 2^-126 as in the decode, FP64), into LDS;
+                // g into gam
+                double* lds_ratio = &lds_part[0][0];
+                static_assert(sizeof(lds_part) >= 256 * sizeof(double), "room for a window of ratios");
+                if (wave == 0) {
+                    double carry = 1.0;
+#pragma unroll 1
+                    for (int w = 0; w * kWave < n_replay; ++w) {  // uniform
+                        const int idx = n_replay - 1 - (lane + w * kWave);
+                        const double g = idx >= 0 ? fmax((double)bg[max(idx, 0)], 0x1p-126) : 1.0;
+                        const double ex = wave_prefix_prod_excl(g);
+                        if (idx >= 0) lds_ratio[idx] = carry * ex;
+                        carry *= lane_value_f64(ex, kWave - 1) * lane_value_f64(g, kWave - 1);
+                    }
+                    if (lane == 0) lds_gs[1] = carry;
+                }
+                __syncthreads();
+                gam = lds_gs[1];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) T[b] *= gam;
+                const int colm = 4 * (m & 3) + (m >> 2);  // column of block b held by result row m
+                const float* bkf = reinterpret_cast<const float*>(bk);
+                const float* bvf = reinterpret_cast<const float*>(bv);
+#pragma unroll 1
+                for (int c = 0; c * EB < n_replay; ++c) {  // uniform
+                    const int i0 = c * EB;
+                    const int ne = (n_replay - i0) < EB ? (n_replay - i0) : EB;
+                    const int par = c & 1;
+                    {
+                        // the chunk's keys into LDS as FP64 (zero past the last entry)
+                        int t = threadIdx.x;
+                        asm volatile("" : "+v"(t));
+                        const int x = 4 * t;
+                        const int e = x / D, col = x % D;
+                        float4 kx = make_float4(0.f, 0.f, 0.f, 0.f);
+                        if (e < ne) kx = *reinterpret_cast<const float4*>(bkf + (size_t)(i0 + e) * D + col);
+                        double* kd = &lds_kf[par][e][col];
+                        kd[0] = (double)kx.x;
+                        kd[1] = (double)kx.y;
+                        kd[2] = (double)kx.z;
+                        kd[3] = (double)kx.w;
+                    }
+                    // this lane's n for tokens 4r + q of the chunk, times g / g_i
+                    double nb[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int e = 4 * r + q;
+                        nb[r] = e < ne ? (double)bvf[(size_t)(i0 + e) * D + n] * lds_ratio[i0 + e] : 0.0;
+                    }
+                    __syncthreads();
+                    const double(*kf)[KP] = (const double(*)[KP])lds_kf[par];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        double kv[NB];
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) kv[b] = kf[4 * r + q][16 * b + colm];
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) T[b] = mfma(kv[b], nb[r], T[b]);
+                    }
+                }
+                gam = 1.0;  // g is in T
+                __syncthreads();  // the ratios' LDS is the quantizer's
+            }
+        } else {
         // ---------------- B: forward replay of the buffered tokens (or the prompt), 16 per chunk
         //
         // Software-pipelined over chunks.  Chunk c+1 is staged while chunk c
@@ -1007,6 +1110,7 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
             if (more) gram_issue(c + 1);
             t_update(more);
         }
+        }  // chain-free or token buffer
         // the next unit's head, requested while this one finishes (from the codes)
         if (kFromCodes && MODE != kModeDequant && ahead) {
             u_next = work_unit(k + 1);
@@ -1367,12 +1471,18 @@ hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, 
         return dim3(a.dm.n_units < g ? a.dm.n_units : g);
     };
     const bool h16 = a.dm.buffer_format == LQ_BUFFER_FP16;
+    const bool nf = a.dm.buffer_format == LQ_BUFFER_NFORM;
 #define LQ_MAT(D_, K_, M_, H_)                                                                  \
     hipLaunchKernelGGL((materialize_kernel<D_, K_, M_, H_>), grid_for(materialize_kernel<D_, K_, M_, H_>), \
                        block, 0, st, a)
+#define LQ_MAT_NF(D_, M_)                                                                        \
+    hipLaunchKernelGGL((materialize_kernel<D_, false, M_, false, true>),                         \
+                       grid_for(materialize_kernel<D_, false, M_, false, true>), block, 0, st, a)
 #define LQ_MAT_MODE(D_, K_)                                                            \
     do {                                                                               \
         if (mode == kModeInit) LQ_MAT(D_, K_, kModeInit, false);                       \
+        else if (nf && !K_ && D_ == 128 && mode == kModeFlush) LQ_MAT_NF(128, kModeFlush);     \
+        else if (nf && !K_ && D_ == 128 && mode == kModeDequant) LQ_MAT_NF(128, kModeDequant); \
         else if (mode == kModePrefill) LQ_MAT(D_, K_, kModePrefill, false);            \
         else if (mode == kModeFlush && h16) LQ_MAT(D_, K_, kModeFlush, true);          \
         else if (mode == kModeFlush) LQ_MAT(D_, K_, kModeFlush, false);                \
@@ -1387,6 +1497,7 @@ hipError_t launch_materialize(const MatArgs& a, int mode, int d, int gate_kind, 
         else LQ_MAT_MODE(64, false);
     }
 #undef LQ_MAT_MODE
+#undef LQ_MAT_NF
 #undef LQ_MAT
     return hipGetLastError();
 }

@@ -219,6 +219,47 @@ __device__ __forceinline__ float wave_sum_all(float x) {
     return __builtin_bit_cast(float, (int)p32[0]) + __builtin_bit_cast(float, (int)p32[1]);
 }
 
+// N independent sums over the whole wavefront, each left in every lane: the
+// stages of wave_sum_all applied to all N values in turn, so the N chains
+// overlap and cost about the latency of one.
+template <int N>
+__device__ __forceinline__ void wave_sum_all_n(float (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f32<kDppQuadXor1>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f32<kDppQuadXor2>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f32<kDppRowHalfMirror>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f32<kDppRowMirror>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int b = __builtin_bit_cast(int, x[i]);
+        const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+        x[i] = __builtin_bit_cast(float, (int)p[0]) + __builtin_bit_cast(float, (int)p[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int b = __builtin_bit_cast(int, x[i]);
+        const auto p = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+        x[i] = __builtin_bit_cast(float, (int)p[0]) + __builtin_bit_cast(float, (int)p[1]);
+    }
+}
+
+// Exclusive prefix sum over the lanes of the wavefront (lane 0 gets 0):
+// shifts of 1, 2, 4 and 8 lanes inside each 16-lane row, the row ends
+// carried with row_bcast, then the whole result moved up one lane.  Each
+// partial sum covers a run of lanes starting at lane 0 of the scan.
+__device__ __forceinline__ float wave_prefix_sum_excl(float x) {
+    x += dpp_f32<0x111>(x);  // row_shr:1
+    x += dpp_f32<0x112>(x);  // row_shr:2
+    x += dpp_f32<0x114>(x);  // row_shr:4
+    x += dpp_f32<0x118>(x);  // row_shr:8
+    x += dpp_f32<kDppRowBcast15, 0xA>(x);
+    x += dpp_f32<kDppRowBcast31, 0xC>(x);
+    return dpp_f32<0x138>(x);  // wave_shr:1
+}
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences global

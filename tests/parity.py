@@ -63,7 +63,7 @@ def unit_rel_l2(a, b) -> np.ndarray:
 
 def config_of(wl: I.Workload) -> lq.Config:
     fmt = {"int8": lq.LQ_CODE_INT8, "e4m3": lq.LQ_CODE_E4M3}[wl.code_format]
-    buf = {"fp32": lq.LQ_BUFFER_FP32, "fp16": lq.LQ_BUFFER_FP16}[wl.buffer_format]
+    buf = {"fp32": lq.LQ_BUFFER_FP32, "fp16": lq.LQ_BUFFER_FP16, "nform": lq.LQ_BUFFER_NFORM}[wl.buffer_format]
     return lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, wl.d, wl.d, wl.window, wl.n_comp,
                      wl.gate_kind, fmt, buf)
 
@@ -235,11 +235,14 @@ def run(wl: I.Workload, n_tokens: Optional[int] = None, checked: Optional[Sequen
         if wl.buffer_format == "fp16":
             # the token enters the window as the binary16 buffer holds it
             pu["k"], pu["v"] = orc.fp16_round(pu["k"]), orc.fp16_round(pu["v"])
-        # the appended entry holds exactly the (rounded) k and v
+        # the appended entry holds exactly the (rounded) k and v (the chain-free
+        # form keeps its own vector n in place of v: the outputs, the state it
+        # dequantizes to and the boundary's codes check it)
         j_chk = fill[checked]
-        bv_chk = views["buf_v"].index_select(0, chk_dev).float().cpu().numpy()
-        assert np.array_equal(bv_chk[np.arange(len(checked)), j_chk], pu["v"][0][checked]), \
-            f"{wl.name}: token {t}: buffered v differs from the appended token"
+        if wl.buffer_format != "nform":
+            bv_chk = views["buf_v"].index_select(0, chk_dev).float().cpu().numpy()
+            assert np.array_equal(bv_chk[np.arange(len(checked)), j_chk], pu["v"][0][checked]), \
+                f"{wl.name}: token {t}: buffered v differs from the appended token"
         kh_of = (checked % wl.n_v_heads) // wl.group
         bk_all = views["buf_k"]
         bk_chk = bk_all[torch.as_tensor(checked // wl.n_v_heads, device=device),

@@ -25,7 +25,8 @@ def sample_units(wl, n=24, seed=7):
 
 @pytest.mark.parametrize("name,fmt", [("tiny_gdn", "int8"), ("gdn_decode", "int8"), ("kda_decode", "int8"),
                                       ("gdn_serving", "int8"), ("gdn_decode", "e4m3"), ("kda_decode", "e4m3"),
-                                      ("gdn_decode", "int8+fp16"), ("kda_decode", "int8+fp16")])
+                                      ("gdn_decode", "int8+fp16"), ("kda_decode", "int8+fp16"),
+                                      ("gdn_decode", "int8+nform"), ("gdn_serving", "int8+nform")])
 def test_fullsize_parity(name, fmt):
     code, _, buf = fmt.partition("+")
     wl = I.WORKLOADS[name].scaled(code_format=code, buffer_format=buf or "fp32")

@@ -77,6 +77,24 @@ CASES = {
                        prefill=24, decode=40, window=16, n_comp=2), dict(dequant_every=17)),
     "kda_gqa_xcd": (small("kda_decode", name="kda_gqa_xcd", n_seq=2, n_v_heads=8, n_k_heads=4,
                           prefill=24, decode=40, window=16, n_comp=3), dict(dequant_every=19)),
+    # the chain-free buffer (scalar gate, d = 128): outlier lines over several
+    # windows, GQA with a ragged last window, forced partial flushes, E4M3
+    # codes, the largest window (four registers of entries), W = 1
+    "gdn_small_nf": (small("gdn_decode", name="gdn_small_nf", n_seq=3, n_v_heads=5, n_k_heads=5,
+                           prefill=96, decode=150, buffer_format="nform"), dict(dequant_every=37)),
+    "gqa_nf": (small("gdn_decode", name="gqa_nf", n_seq=3, n_v_heads=4, n_k_heads=2, prefill=40,
+                     decode=45, window=16, n_comp=3, outlier_rows=0, outlier_cols=0,
+                     buffer_format="nform"), dict(dequant_every=13)),
+    "stagger_nf": (small("gdn_serving", name="stagger_nf", n_seq=8, n_v_heads=2, n_k_heads=2,
+                         prefill=32, decode=50, window=16, buffer_format="nform"), dict(dequant_every=11)),
+    "gdn_nf_e4m3": (small("gdn_decode", name="gdn_nf_e4m3", n_seq=2, n_v_heads=3, n_k_heads=3,
+                          prefill=64, decode=100, code_format="e4m3", buffer_format="nform"),
+                    dict(dequant_every=29)),
+    "max_nf": (small("gdn_decode", name="max_nf", n_seq=1, n_v_heads=3, n_k_heads=3, prefill=64,
+                     decode=300, window=256, n_comp=16, buffer_format="nform"), dict(dequant_every=110)),
+    "w1_nf": (small("gdn_decode", name="w1_nf", n_seq=2, n_v_heads=3, n_k_heads=3, prefill=20,
+                    decode=12, window=1, n_comp=0, outlier_rows=0, outlier_cols=0,
+                    buffer_format="nform"), dict()),
     # zero start state (no prefill) with the channel gate at d=128
     "kda_zero_start": (small("kda_decode", name="kda_zero_start", n_seq=1, n_v_heads=2,
                              n_k_heads=2, prefill=0, decode=20, window=8, n_comp=4), dict()),
@@ -319,19 +337,22 @@ def test_degenerate_states(d, gate, fmt):
     assert lq.lq_read_status(cfg, st) == 0
 
 
-@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("gate,buf", [("scalar", "fp32"), ("channel", "fp32"), ("scalar", "nform")])
 @pytest.mark.parametrize("d", [64, 128])
-def test_extreme_gates(d, gate):
+def test_extreme_gates(d, gate, buf):
     # gates of 0, 1e-20 and 1e-30 (two of them in one 16-token chunk, whose
     # product underflows FP32 and folds into the boundary's FP64 state), and
     # channel gates with whole channels at 0 or 1e-25: the decode outputs
     # follow the plain recurrence from the window-start state, and the
     # boundary's codes, scales and lines match the oracle's on the state the
     # recurrence reaches (the boundary floors each gate at 2^-45, the oracle
-    # does not: the difference is below 2^-45 of the state)
+    # does not: the difference is below 2^-45 of the state); with the
+    # chain-free buffer the gates enter as floored logarithms and ratios
+    if buf == "nform" and d != 128:
+        pytest.skip("the chain-free buffer is built for d = 128")
     base = "gdn_decode" if gate == "scalar" else "kda_decode"
-    wl = small(base, name=f"extreme_gates_{gate}_{d}", n_seq=2, n_v_heads=2, n_k_heads=2, d=d,
-               window=20, n_comp=2, prefill=0, outlier_rows=0, outlier_cols=0)
+    wl = small(base, name=f"extreme_gates_{gate}_{d}_{buf}", n_seq=2, n_v_heads=2, n_k_heads=2, d=d,
+               window=20, n_comp=2, prefill=0, outlier_rows=0, outlier_cols=0, buffer_format=buf)
     cfg = _cfg(wl)
     U = wl.n_units
     rng = np.random.default_rng(17 + d)
