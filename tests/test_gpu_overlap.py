@@ -27,9 +27,10 @@ def _blob_equal(cfg, a, b, what):
         assert torch.equal(va[key], vb[key]), (what, key)
 
 
-@pytest.mark.parametrize("name,cus", [("gdn_decode", 5), ("gdn_decode", 96), ("kda_decode", 13)])
-def test_flush_on_fewer_cus_is_bitwise_equal(name, cus):
-    wl = I.WORKLOADS[name].scaled(name=f"{name}_cus", window=8, prefill=0, n_seq=16)
+@pytest.mark.parametrize("name,cus,buf", [("gdn_decode", 5, "fp32"), ("gdn_decode", 96, "fp32"),
+                                          ("kda_decode", 13, "fp32"), ("gdn_decode", 7, "nform")])
+def test_flush_on_fewer_cus_is_bitwise_equal(name, cus, buf):
+    wl = I.WORKLOADS[name].scaled(name=f"{name}_cus", window=8, prefill=0, n_seq=16, buffer_format=buf)
     cfg = parity.config_of(wl)
     few = dataclasses.replace(cfg, flush_cus=cus)
     U, d = wl.n_units, wl.d

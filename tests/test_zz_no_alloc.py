@@ -66,3 +66,15 @@ def test_noalloc_rejects_more_units_than_its_scratch():
     with pytest.raises(lq.LQError) as e:
         lq.lq_window_flush_noalloc(cfg, dummy.data_ptr(), None)
     assert e.value.code == lq.LQ_ESCRATCH
+
+
+def test_noalloc_flush_matches_flush_chain_free_buffer():
+    # the chain-free buffer's boundary kernel through the same scratch array:
+    # a full window for most units, a forced partial one, then a smaller call
+    big = I.WORKLOADS["gdn_decode"].scaled(name="noalloc_nf", window=8, prefill=0, buffer_format="nform")
+    fill = _flush_both(big, 8, [5, 17], seed=3)
+    assert (fill == 0).all()
+    small = I.WORKLOADS["gdn_decode"].scaled(name="noalloc_nf_small", n_seq=3, n_v_heads=2, n_k_heads=1,
+                                             window=12, n_comp=2, prefill=0, buffer_format="nform")
+    fill = _flush_both(small, 7, [0, 2], seed=4)
+    assert fill.tolist() == [0, 0, 7, 7, 0, 0]
