@@ -93,6 +93,11 @@ def parse_args(argv=None):
                     help="multi-layer workloads: run each layer's boundary call on a second stream, on this many "
                          "CUs (lq_config.flush_cus), beside the next layers' decode steps; 0 runs it on the "
                          "decode stream after the token's last layer; -1 (default) picks 96 of 256 (measured best of 64-160)")
+    ap.add_argument("--load-policy", default="residency", choices=("residency", "auto", "stream", "cached"),
+                    help="lq_config.load_policy of the decode steps: streaming (non-temporal) state reads, "
+                         "automatic (launches of more than 2,048 units), or ordinary; 'residency' (default) "
+                         "streams when the states of every layer and copy exceed twice the 256 MB "
+                         "last-level cache, as a caller that knows its working set would, else automatic")
     ap.add_argument("--stagger-layout", default="blocks", choices=("blocks", "interleaved"),
                     help="one-layer workloads: which sequences share a window offset (consecutive ones, "
                          "fills falling along the unit index; or sequence s in group s mod G)")
@@ -477,6 +482,13 @@ def main(argv=None):
     buffer_format = {"fp32": lq.LQ_BUFFER_FP32, "fp16": lq.LQ_BUFFER_FP16, "nform": lq.LQ_BUFFER_NFORM}[args.buffer]
     cfg = lq.Config(wl.n_seq, wl.n_v_heads, wl.n_k_heads, d, d, W, wl.n_comp, wl.gate_kind, code_format,
                     buffer_format)
+    if args.load_policy == "residency":
+        in_hbm = L * R * lq.lq_state_bytes(cfg) > 2 * LLC_BYTES
+        load_policy = lq.LQ_LOADS_STREAM if in_hbm else lq.LQ_LOADS_AUTO
+    else:
+        load_policy = {"auto": lq.LQ_LOADS_AUTO, "stream": lq.LQ_LOADS_STREAM,
+                       "cached": lq.LQ_LOADS_CACHED}[args.load_policy]
+    cfg = dataclasses.replace(cfg, load_policy=load_policy)
     # Boundary beside the decode (multi-layer stacks): a layer's boundary call
     # depends only on that layer's decode of the token, and only that layer's
     # decode of the next token depends on it, so it runs on a second stream
@@ -608,6 +620,8 @@ def main(argv=None):
             "code_format": args.format, "buffer_format": args.buffer,
             "prefill": wl.prefill, "units": units_step, "state_copies": R,
             "state_bytes": ws_bytes,
+            "load_policy": {lq.LQ_LOADS_AUTO: "auto", lq.LQ_LOADS_STREAM: "stream",
+                            lq.LQ_LOADS_CACHED: "cached"}[cfg.load_policy],
             "residency": ("hbm" if ws_bytes > 2 * LLC_BYTES else
                           "cache (the states fit the 256 MB last-level cache; --replicas pushes them to HBM)"),
         },

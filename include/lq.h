@@ -90,6 +90,16 @@ typedef struct ihipStream_t* hipStream_t;
                              and beta, the WY-form vector n (fp32), so the decode has no
                              sequential pass over the window and the boundary is one product */
 
+/* how a decode step reads each unit's state and window (lq_config.load_policy):
+   the bytes a step reads from a unit (its 8-bit tile, scales, compensator lines and
+   buffered values) are read once per step, so streaming (non-temporal) loads keep
+   them from displacing data that is read again (the keys that the value heads of
+   one key head share, the lines the step writes); a state that stays in the
+   last-level cache between steps is read faster with ordinary loads */
+#define LQ_LOADS_AUTO 0   /* streaming loads in decode launches of more than 2,048 units */
+#define LQ_LOADS_STREAM 1 /* always (a caller whose states do not stay in the cache) */
+#define LQ_LOADS_CACHED 2 /* never */
+
 /* sticky device flags (lq_read_status) */
 #define LQ_DEV_WINDOW_OVERFLOW 0x1u /* lq_decode_step found a full window: that unit's o is NaN, nothing appended */
 #define LQ_DEV_NONFINITE_INPUT 0x2u /* an input (decode token, prompt token, start state S0) was NaN or Inf */
@@ -102,6 +112,7 @@ typedef struct ihipStream_t* hipStream_t;
  * code_format in {LQ_CODE_INT8, LQ_CODE_E4M3};
  * buffer_format in {LQ_BUFFER_FP32, LQ_BUFFER_FP16, LQ_BUFFER_NFORM} (NFORM with
  * gate_kind LQ_GATE_SCALAR and d_k = d_v = 128 only); flush_cus >= 0;
+ * load_policy in {LQ_LOADS_AUTO, LQ_LOADS_STREAM, LQ_LOADS_CACHED};
  * the unit count n_seq * n_v_heads below 2^31.
  */
 typedef struct lq_config {
@@ -131,6 +142,9 @@ typedef struct lq_config {
                           layers' decode steps gives it part of the device.  The
                           results do not depend on it (each unit is computed the
                           same way wherever it runs) */
+    int32_t load_policy; /* LQ_LOADS_*: the cache policy of lq_decode_step's state and
+                            window reads; performance only, the results are the same
+                            bit for bit */
 } lq_config;
 
 /*

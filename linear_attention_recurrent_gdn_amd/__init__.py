@@ -32,6 +32,9 @@ LQ_CODE_E4M3 = 1
 LQ_BUFFER_FP32 = 0
 LQ_BUFFER_FP16 = 1
 LQ_BUFFER_NFORM = 2
+LQ_LOADS_AUTO = 0
+LQ_LOADS_STREAM = 1
+LQ_LOADS_CACHED = 2
 LQ_DEV_WINDOW_OVERFLOW = 0x1
 LQ_DEV_NONFINITE_INPUT = 0x2
 LQ_DEV_BUFFER_SATURATED = 0x4
@@ -50,7 +53,7 @@ class LQError(RuntimeError):
 class _CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_seq", "n_v_heads", "n_k_heads", "d_k", "d_v", "window", "n_comp", "gate_kind",
-                 "code_format", "buffer_format", "flush_cus")]
+                 "code_format", "buffer_format", "flush_cus", "load_policy")]
 
 
 _LAYOUT_FIELDS = ("total_bytes", "status", "fill", "codes", "sigma", "smooth", "comp_idx",
@@ -75,6 +78,7 @@ class Config:
     code_format: int = LQ_CODE_INT8
     buffer_format: int = LQ_BUFFER_FP32
     flush_cus: int = 0
+    load_policy: int = LQ_LOADS_AUTO
 
     @property
     def n_units(self) -> int:

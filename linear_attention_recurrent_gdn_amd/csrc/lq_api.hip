@@ -22,6 +22,8 @@ int32_t check_config(const lq_config* c) {
         c->buffer_format != LQ_BUFFER_NFORM)
         return LQ_EINVAL;
     if (c->flush_cus < 0) return LQ_EINVAL;
+    if (c->load_policy != LQ_LOADS_AUTO && c->load_policy != LQ_LOADS_STREAM && c->load_policy != LQ_LOADS_CACHED)
+        return LQ_EINVAL;
     if ((int64_t)c->n_seq * c->n_v_heads >= ((int64_t)1 << 31)) return LQ_EUNSUPPORTED;
     if (c->d_k != c->d_v || (c->d_k != 64 && c->d_k != 128)) return LQ_EUNSUPPORTED;
     if (c->window > 256 || c->n_comp > 16) return LQ_EUNSUPPORTED;
@@ -43,6 +45,7 @@ Dims dims_of(const lq_config* c) {
     d.code_format = c->code_format;
     d.buffer_format = c->buffer_format;
     d.max_cus = c->flush_cus;
+    d.load_policy = c->load_policy;
     return d;
 }
 

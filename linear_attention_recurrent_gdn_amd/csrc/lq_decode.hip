@@ -48,6 +48,7 @@ namespace lq {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int EPL>
 struct Vec {
@@ -65,6 +66,34 @@ __device__ __forceinline__ Vec<EPL> load_vec(const float* p) {
         r.e[0] = p[0];
     }
     return r;
+}
+
+// The same, as streaming (non-temporal) loads where STREAM: for data that a
+// launch reads exactly once (a unit's 8-bit tile, scales, compensator lines,
+// buffered values), so that it does not displace in the caches what is read
+// again (the keys that the value heads of one key head share, the lines that
+// the stores write).  A state small enough to stay in the last-level cache
+// from one token to the next (1,024 units of d = 128 on their own) is read
+// faster with ordinary loads: lq_config.load_policy chooses.
+template <int EPL, bool STREAM>
+__device__ __forceinline__ Vec<EPL> load_vec_as(const float* p) {
+    if constexpr (!STREAM) return load_vec<EPL>(p);
+    Vec<EPL> r;
+    if constexpr (EPL == 2) {
+        const f32x2 t = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+        r.e[0] = t[0];
+        r.e[1] = t[1];
+    } else {
+        r.e[0] = __builtin_nontemporal_load(p);
+    }
+    return r;
+}
+
+template <bool STREAM>
+__device__ __forceinline__ uint4 load_tile_as(const uint4* p) {
+    if constexpr (!STREAM) return *p;
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
 }
 
 template <int EPL>
@@ -179,27 +208,30 @@ struct RingEntry<EPL, GE, true> {
 };
 
 constexpr int kBufferFlags = 0x00020000;  // raw 32-bit buffer resource word 3 (gfx9 family)
+// cache-policy operand of a buffer load: 0 ordinary, kStream the non-temporal
+// (streaming) bit of gfx950's buffer instructions
+constexpr int kStream = 2;
 
 // EPL consecutive fp32 (or packed binary16 when H16) of a buffer resource at
 // a per-lane byte offset plus a uniform (scalar) byte offset.
-template <int EPL>
+template <int EPL, int POL = 0>
 __device__ __forceinline__ Vec<EPL> buf_load_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     Vec<EPL> x;
     if constexpr (EPL == 2) {
         // the builtin returns a two-element vector of its own (GCC vector) type
-        const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POL);
         x.e[0] = __builtin_bit_cast(float, (unsigned int)w[0]);
         x.e[1] = __builtin_bit_cast(float, (unsigned int)w[1]);
     } else {
-        x.e[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+        x.e[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, POL));
     }
     return x;
 }
 
-template <int EPL>
+template <int EPL, int POL = 0>
 __device__ __forceinline__ uint32_t buf_load_halves(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    if constexpr (EPL == 2) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-    else return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    if constexpr (EPL == 2) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, POL);
+    else return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, POL);
 }
 
 // beta and scalar gate of the whole window as loaded, NWB per lane (token i
@@ -250,7 +282,7 @@ __device__ __forceinline__ void codes_to_float(const uint4& w4, float (&cf)[16])
 // launch on the hybrid stack; the 4-byte writes stay ordinary stores, as
 // non-temporal they cost more).  The other form (one round of workgroups)
 // keeps the codes converted early and eight slots in registers.
-template <int D, bool KDA, int P, int NWB, int FMT, bool H16, bool LARGE>
+template <int D, bool KDA, int P, int NWB, int FMT, bool H16, bool LARGE, bool STREAM>
 __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     constexpr int EPL = D / kWave;   // state elements per lane in the chain wave
     constexpr int GE = KDA ? EPL : 1;
@@ -301,7 +333,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
 
     if (wave != 0) {
 #pragma unroll
-        for (int t = 0; t < NLW; ++t) tw[t] = tile[t * kWave + lane];
+        for (int t = 0; t < NLW; ++t) tw[t] = load_tile_as<STREAM>(&tile[t * kWave + lane]);
         sg_row = a.blob.sigma[(size_t)u * D + my_row];
         j = __builtin_amdgcn_readfirstlane(j_ld);
         // the codes to floats while wavefront 0 runs the reverse pass, so
@@ -342,14 +374,14 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
             win.a[w] = KDA ? 0.f : bg[min(lane + w * kWave, W - 1)];
         }
 #pragma unroll
-        for (int t = 0; t < NLW; ++t) tw[t] = tile[t * kWave + lane];
+        for (int t = 0; t < NLW; ++t) tw[t] = load_tile_as<STREAM>(&tile[t * kWave + lane]);
         sg_row = a.blob.sigma[(size_t)u * D + my_row];
-        const Vec<EPL> sm = load_vec<EPL>(a.blob.smooth + (size_t)u * D + lane * EPL);
+        const Vec<EPL> sm = load_vec_as<EPL, STREAM>(a.blob.smooth + (size_t)u * D + lane * EPL);
         const int cidx = a.blob.comp_idx[(size_t)u * nc + min(lane, max(nc - 1, 0))];
         Vec<EPL> cvec[NCP];
 #pragma unroll
         for (int c = 0; c < NCP; ++c)
-            cvec[c] = load_vec<EPL>(a.blob.comp_vec + ((size_t)u * nc + min(c, max(nc - 1, 0))) * D + lane * EPL);
+            cvec[c] = load_vec_as<EPL, STREAM>(a.blob.comp_vec + ((size_t)u * nc + min(c, max(nc - 1, 0))) * D + lane * EPL);
 
         j = __builtin_amdgcn_readfirstlane(j_ld);
         const bool over = j >= W;
@@ -371,15 +403,20 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         const __amdgpu_buffer_rsrc_t rnone =
             __builtin_amdgcn_make_buffer_rsrc((char*)a.blob.buf_k, (short)0, 0, kBufferFlags);
         const int voff = lane * EPL * ESZ;
+        // values are read once per launch and streamed; so are the keys with
+        // the channel gate, whose entries carry a gate vector as well (with a
+        // scalar gate, streamed keys and gates were slower: measured)
+        constexpr int KPOL = (STREAM && KDA) ? kStream : 0;
+        constexpr int VPOL = STREAM ? kStream : 0;
         auto load_entry = [&](int i, RingEntry<EPL, GE, H16>& en) {
             const bool live = i >= 0;  // uniform
             const int ie = live ? i : 0;
             if constexpr (H16) {
-                en.k = buf_load_halves<EPL>(live ? rk : rnone, voff, ie * D * ESZ);
-                en.v = buf_load_halves<EPL>(live ? rv : rnone, voff, ie * D * ESZ);
+                en.k = buf_load_halves<EPL, KPOL>(live ? rk : rnone, voff, ie * D * ESZ);
+                en.v = buf_load_halves<EPL, VPOL>(live ? rv : rnone, voff, ie * D * ESZ);
             } else {
-                en.k = buf_load_f32<EPL>(live ? rk : rnone, voff, ie * D * ESZ);
-                en.v = buf_load_f32<EPL>(live ? rv : rnone, voff, ie * D * ESZ);
+                en.k = buf_load_f32<EPL, KPOL>(live ? rk : rnone, voff, ie * D * ESZ);
+                en.v = buf_load_f32<EPL, VPOL>(live ? rv : rnone, voff, ie * D * ESZ);
             }
             if constexpr (KDA) en.g = buf_load_f32<GE>(live ? rg : rnone, lane * EPL * 4, ie * D * 4);
         };
@@ -430,6 +467,10 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
         // reverse pass over the window, newest token first.  With a scalar
         // gate the running gate product sc stays off the dependent chain:
         // r_true = sc * r, so r -= (beta (k.r)) k and acc += beta sc (k.r) v.
+        // the reverse pass is the workgroup's dependent chain: it takes issue
+        // priority over the other wavefronts on its SIMD (other workgroups'
+        // tile products and prologues) until its results are in LDS
+        __builtin_amdgcn_s_setprio(3);
         Vec<EPL> r = qv;
         Vec<EPL> acc;
         for (int e = 0; e < EPL; ++e) acc.e[e] = 0.f;
@@ -509,7 +550,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
             if (c < nc) comp(__builtin_amdgcn_readlane(cidx, c), cvec[c]);
         for (int c = NCP; c < nc; ++c)
             comp(__builtin_amdgcn_readlane(cidx, c),
-                 load_vec<EPL>(a.blob.comp_vec + ((size_t)u * nc + c) * D + lane * EPL));
+                 load_vec_as<EPL, STREAM>(a.blob.comp_vec + ((size_t)u * nc + c) * D + lane * EPL));
 
         for (int e = 0; e < EPL; ++e) {
             lds_x[lane * EPL + e] = sm.e[e] * r.e[e];
@@ -519,6 +560,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
 #pragma unroll
             for (int t = 0; t < NLW; ++t) codes_to_float<FMT>(tw[t], cf[t]);
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     lds_barrier();
 
@@ -578,7 +620,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
 // key with k_t and with q_t, which are independent of each other: the four
 // wavefronts of the workgroup take every fourth entry, with no dependent
 // chain across entries.
-template <int D, int FMT>
+template <int D, int FMT, bool STREAM>
 __global__ __launch_bounds__(256) void decode_nform_kernel(DecodeArgs a) {
     constexpr int EPL = D / kWave;    // vector elements per lane
     constexpr int RW = D / 4;         // tile rows per wave
@@ -611,7 +653,7 @@ __global__ __launch_bounds__(256) void decode_nform_kernel(DecodeArgs a) {
     const int my_row = row0 + min(cg, NLW - 1) * RPL + lane / LPR;
     uint4 tw[NLW];
 #pragma unroll
-    for (int t = 0; t < NLW; ++t) tw[t] = tile[t * kWave + lane];
+    for (int t = 0; t < NLW; ++t) tw[t] = load_tile_as<STREAM>(&tile[t * kWave + lane]);
     const float sg_row = a.blob.sigma[(size_t)u * D + my_row];
     const float v_row = a.v[(size_t)u * D + my_row];
 
@@ -665,7 +707,7 @@ __global__ __launch_bounds__(256) void decode_nform_kernel(DecodeArgs a) {
         const bool live = i < jr;  // uniform
         const int ie = live ? i : 0;
         ek[p] = buf_load_f32<EPL>(live ? rk : rnone, voff, ie * D * 4);
-        en[p] = buf_load_f32<EPL>(live ? rn : rnone, voff, ie * D * 4);
+        en[p] = buf_load_f32<EPL, STREAM ? kStream : 0>(live ? rn : rnone, voff, ie * D * 4);
     };
 #pragma unroll
     for (int p = 0; p < P; ++p) load_entry(wave + 4 * p, p);
@@ -675,11 +717,11 @@ __global__ __launch_bounds__(256) void decode_nform_kernel(DecodeArgs a) {
     Vec<EPL> cvec[NCP];
     Vec<EPL> sm;
     if (wave == 0) {
-        sm = load_vec<EPL>(a.blob.smooth + (size_t)u * D + lane * EPL);
+        sm = load_vec_as<EPL, STREAM>(a.blob.smooth + (size_t)u * D + lane * EPL);
         cidx = a.blob.comp_idx[(size_t)u * nc + min(lane, max(nc - 1, 0))];
 #pragma unroll
         for (int c = 0; c < NCP; ++c)
-            cvec[c] = load_vec<EPL>(a.blob.comp_vec + ((size_t)u * nc + min(c, max(nc - 1, 0))) * D + lane * EPL);
+            cvec[c] = load_vec_as<EPL, STREAM>(a.blob.comp_vec + ((size_t)u * nc + min(c, max(nc - 1, 0))) * D + lane * EPL);
     }
 
     // the entries: A1 = sum ratio_i (k_i . k_t) n_i, A2 = sum ratio_i (k_i . q_t) n_i
@@ -749,7 +791,7 @@ __global__ __launch_bounds__(256) void decode_nform_kernel(DecodeArgs a) {
             if (c < nc) comp(__builtin_amdgcn_readlane(cidx, c), cvec[c]);
         for (int c = NCP; c < nc; ++c)
             comp(__builtin_amdgcn_readlane(cidx, c),
-                 load_vec<EPL>(a.blob.comp_vec + ((size_t)u * nc + c) * D + lane * EPL));
+                 load_vec_as<EPL, STREAM>(a.blob.comp_vec + ((size_t)u * nc + c) * D + lane * EPL));
         float kq = 0.f;
         for (int e = 0; e < EPL; ++e) {
             lds_x[0][lane * EPL + e] = sm.e[e] * kt.e[e];
@@ -923,34 +965,49 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
 #define LQ_LARGE_UNITS_MIN 2048
 #endif
 
-template <int NWB, int FMT, bool H16, bool LARGE>
+// streaming loads for this launch (lq_config.load_policy; automatic: the
+// large form)
+static bool stream_loads(const Dims& dm) {
+    if (dm.load_policy == LQ_LOADS_STREAM) return true;
+    if (dm.load_policy == LQ_LOADS_CACHED) return false;
+    return dm.n_units > LQ_LARGE_UNITS_MIN;
+}
+
+template <int NWB, int FMT, bool H16, bool LARGE, bool STREAM>
 void launch_decode_q8_w(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
     const dim3 grid(a.dm.n_units), block(256);
     if (d == 128) {
         constexpr int PK = H16 ? LQ_RING_KDA_H16 : LQ_RING_KDA;
         constexpr int PG = H16 ? LQ_RING_GDN_H16 : LQ_RING_GDN;
         if (gate_kind == LQ_GATE_CHANNEL)
-            hipLaunchKernelGGL((decode_q8_kernel<128, true, PK, NWB, FMT, H16, LARGE>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<128, true, PK, NWB, FMT, H16, LARGE, STREAM>), grid, block, 0, st, a);
         else
-            hipLaunchKernelGGL((decode_q8_kernel<128, false, PG, NWB, FMT, H16, LARGE>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<128, false, PG, NWB, FMT, H16, LARGE, STREAM>), grid, block, 0, st, a);
     } else {
         if (gate_kind == LQ_GATE_CHANNEL)
-            hipLaunchKernelGGL((decode_q8_kernel<64, true, 16, NWB, FMT, H16, LARGE>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<64, true, 16, NWB, FMT, H16, LARGE, STREAM>), grid, block, 0, st, a);
         else
-            hipLaunchKernelGGL((decode_q8_kernel<64, false, 16, NWB, FMT, H16, LARGE>), grid, block, 0, st, a);
+            hipLaunchKernelGGL((decode_q8_kernel<64, false, 16, NWB, FMT, H16, LARGE, STREAM>), grid, block, 0, st, a);
+    }
+}
+
+template <int NWB, int FMT, bool H16>
+void launch_decode_q8_s(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
+    const bool large = a.dm.n_units > LQ_LARGE_UNITS_MIN;
+    const bool stream = stream_loads(a.dm);
+    if (large) {
+        if (stream) launch_decode_q8_w<NWB, FMT, H16, true, true>(a, d, gate_kind, st);
+        else launch_decode_q8_w<NWB, FMT, H16, true, false>(a, d, gate_kind, st);
+    } else {
+        if (stream) launch_decode_q8_w<NWB, FMT, H16, false, true>(a, d, gate_kind, st);
+        else launch_decode_q8_w<NWB, FMT, H16, false, false>(a, d, gate_kind, st);
     }
 }
 
 template <int FMT, bool H16>
 void launch_decode_q8_f(const DecodeArgs& a, int d, int gate_kind, hipStream_t st) {
-    const bool large = a.dm.n_units > LQ_LARGE_UNITS_MIN;
-    if (a.dm.window <= 2 * kWave) {
-        if (large) launch_decode_q8_w<2, FMT, H16, true>(a, d, gate_kind, st);
-        else launch_decode_q8_w<2, FMT, H16, false>(a, d, gate_kind, st);
-    } else {
-        if (large) launch_decode_q8_w<4, FMT, H16, true>(a, d, gate_kind, st);
-        else launch_decode_q8_w<4, FMT, H16, false>(a, d, gate_kind, st);
-    }
+    if (a.dm.window <= 2 * kWave) launch_decode_q8_s<2, FMT, H16>(a, d, gate_kind, st);
+    else launch_decode_q8_s<4, FMT, H16>(a, d, gate_kind, st);
 }
 
 template <bool H16>
@@ -964,8 +1021,14 @@ hipError_t launch_decode_q8(const DecodeArgs& a, int d, int gate_kind, hipStream
         const dim3 grid(a.dm.n_units), block(256);
         const bool e4m3 = a.dm.code_format == LQ_CODE_E4M3;
         (void)d;  // d = 128 only (checked by the caller)
-        if (e4m3) hipLaunchKernelGGL((decode_nform_kernel<128, LQ_CODE_E4M3>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((decode_nform_kernel<128, LQ_CODE_INT8>), grid, block, 0, st, a);
+        const bool stream = stream_loads(a.dm);
+        if (e4m3) {
+            if (stream) hipLaunchKernelGGL((decode_nform_kernel<128, LQ_CODE_E4M3, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((decode_nform_kernel<128, LQ_CODE_E4M3, false>), grid, block, 0, st, a);
+        } else {
+            if (stream) hipLaunchKernelGGL((decode_nform_kernel<128, LQ_CODE_INT8, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((decode_nform_kernel<128, LQ_CODE_INT8, false>), grid, block, 0, st, a);
+        }
         return hipGetLastError();
     }
     if (a.dm.buffer_format == LQ_BUFFER_FP16) launch_decode_q8_b<true>(a, d, gate_kind, st);

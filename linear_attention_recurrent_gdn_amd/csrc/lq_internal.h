@@ -89,6 +89,7 @@ struct Dims {
     int code_format;    // LQ_CODE_INT8 or LQ_CODE_E4M3
     int buffer_format;  // LQ_BUFFER_FP32 or LQ_BUFFER_FP16 (k and v of the window buffer)
     int max_cus;        // CUs the persistent (materialize) grid may occupy; 0: all
+    int load_policy;    // LQ_LOADS_*: streaming loads in the decode step
 };
 
 struct DecodeArgs {

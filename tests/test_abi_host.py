@@ -78,6 +78,8 @@ def test_state_bytes_matches_int8_footprint(lib):
     (dict(gate_kind=7), lq.LQ_EINVAL),
     (dict(code_format=2), lq.LQ_EINVAL),
     (dict(flush_cus=-1), lq.LQ_EINVAL),
+    (dict(load_policy=3), lq.LQ_EINVAL),
+    (dict(load_policy=-1), lq.LQ_EINVAL),
     (dict(buffer_format=3), lq.LQ_EINVAL),
     (dict(buffer_format=lq.LQ_BUFFER_NFORM, gate_kind=lq.LQ_GATE_CHANNEL), lq.LQ_EUNSUPPORTED),
     (dict(buffer_format=lq.LQ_BUFFER_NFORM, d_k=64, d_v=64), lq.LQ_EUNSUPPORTED),
