@@ -281,7 +281,9 @@ __device__ __forceinline__ void codes_to_float(const uint4& w4, float (&cf)[16])
 // appended entry, the outputs) as non-temporal stores (about 1 us less per
 // launch on the hybrid stack; the 4-byte writes stay ordinary stores, as
 // non-temporal they cost more).  The other form (one round of workgroups)
-// keeps the codes converted early and eight slots in registers.
+// keeps the codes converted early and eight slots in registers.  STREAM
+// (lq_config.load_policy) reads the unit's once-read bytes with streaming
+// loads, and makes the 512-byte writes non-temporal in either form.
 template <int D, bool KDA, int P, int NWB, int FMT, bool H16, bool LARGE, bool STREAM>
 __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     constexpr int EPL = D / kWave;   // state elements per lane in the chain wave
@@ -319,6 +321,9 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     // binary16 buffer: there the extra registers cost a wavefront per SIMD of
     // occupancy, more than the conversion saves.
     constexpr bool kEarlyCodes = !H16 && !LARGE;
+    // the 512-byte writes (the appended entry, the outputs) as non-temporal
+    // stores: in the large form, and wherever the loads stream
+    constexpr bool NTST = LARGE || STREAM;
     float cf[NLW][16];
     float sg_row;
 
@@ -439,8 +444,8 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
             if (__any(sat) && lane == 0) atomicOr(a.blob.status, (uint32_t)LQ_DEV_BUFFER_SATURATED);
         }
         if (!over) {
-            if (h % a.dm.group == 0) store_buf<EPL, H16, LARGE>(a.blob.buf_k, kb0 + (size_t)j * D + lane * EPL, cur.k);
-            store_buf<EPL, H16, LARGE>(a.blob.buf_v, vb0 + (size_t)j * D + lane * EPL, cur.v);
+            if (h % a.dm.group == 0) store_buf<EPL, H16, NTST>(a.blob.buf_k, kb0 + (size_t)j * D + lane * EPL, cur.k);
+            store_buf<EPL, H16, NTST>(a.blob.buf_v, vb0 + (size_t)j * D + lane * EPL, cur.v);
         }
         // beta and scalar gate of every buffered slot into LDS, then the ring's
         // first entries take theirs (uniform reads; later refills read ahead)
@@ -594,7 +599,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     if (cg < NLW)
     {
         const float ov = over ? __builtin_nanf("") : __builtin_fmaf(sg_row, mine, lds_add[my_row]);
-        if constexpr (LARGE) __builtin_nontemporal_store(ov, a.o + (size_t)u * D + my_row);
+        if constexpr (NTST) __builtin_nontemporal_store(ov, a.o + (size_t)u * D + my_row);
         else a.o[(size_t)u * D + my_row] = ov;
     }
     if (wave == 0 && lane == 0) {
