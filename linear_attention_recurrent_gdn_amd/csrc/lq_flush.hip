@@ -210,15 +210,17 @@ __device__ __forceinline__ int reduce_columns(double (&v)[NV], int m) {
     }
 }
 
-// Wavefront maximum of a double, in every lane: DPP inside each 16-lane row,
-// then the row swaps.  fmax returns one of its inputs, so the result equals
-// some lane's value exactly.
-__device__ __forceinline__ double wave_max(double x) {
-    x = fmax(x, dpp_f64<kDppQuadXor1>(x));
-    x = fmax(x, dpp_f64<kDppQuadXor2>(x));
-    x = fmax(x, dpp_f64<kDppRowHalfMirror>(x));
-    x = fmax(x, dpp_f64<kDppRowMirror>(x));
-    return across_rows<true>(x);
+// Wavefront maximum of a 32-bit unsigned value, in every lane (DPP inside
+// each 16-lane row, then the row swaps).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppQuadXor1, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppQuadXor2, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppRowHalfMirror, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppRowMirror, 0xF, 0xF, false));
+    const auto p16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max((uint32_t)p16[0], (uint32_t)p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max((uint32_t)p32[0], (uint32_t)p32[1]);
 }
 
 // E4M3 byte of x (FP64): the nearest value of the 8-bit float format with
@@ -1193,36 +1195,63 @@ __global__ __launch_bounds__(kWave * D / 16) void materialize_kernel(MatArgs a) 
         }
         // ---------------- C2: top-n_comp selection (wavefront 0)
         if (wave == 0) {
-            // Each round takes every lane's best untaken candidate (the lower
-            // index on equal scores), the wavefront maximum of those, and the
-            // first lane that offers it: its candidates precede those of later
-            // lanes, so equal scores go to the lower candidate index.  Scores
-            // are >= 0; a NaN score (non-finite input) ranks below every real
-            // one, and a taken candidate becomes -1, which never wins.
-            double val[CPL];
+            // Candidates are ranked by a 64-bit key: 2 + the bits of the score
+            // (scores are >= 0, and the bit patterns of non-negative doubles
+            // order as their values), 1 for a NaN score (non-finite input:
+            // below every real one), 0 once taken.  Each lane sorts its own
+            // candidates once (key descending, the lower index first on equal
+            // keys); a round takes the wavefront maximum of the lanes' first
+            // keys (high words, then the low words of the lanes that tie) and
+            // the first lane offering it, whose candidates precede those of
+            // later lanes: equal scores go to the lower candidate index.  The
+            // winning lane then drops its first candidate.
+            uint64_t key[CPL];
+            int idx[CPL];
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
-                const double sc = lds_score[lane * CPL + i];
-                val[i] = __builtin_isnan(sc) ? -0.5 : sc;
+                const double sc = lds_score[lane * CPL + i] + 0.0;  // (a -0.0 as +0.0)
+                key[i] = __builtin_isnan(sc) ? 1ull : 2ull + __builtin_bit_cast(uint64_t, sc);
+                idx[i] = i;
+            }
+            auto order = [&](int x, int y) {  // positions x < y: y first if it ranks higher
+                const bool sw = key[y] > key[x] || (key[y] == key[x] && idx[y] < idx[x]);
+                const uint64_t kx = key[x], ky = key[y];
+                const int ix = idx[x], iy = idx[y];
+                key[x] = sw ? ky : kx;
+                key[y] = sw ? kx : ky;
+                idx[x] = sw ? iy : ix;
+                idx[y] = sw ? ix : iy;
+            };
+            static_assert(CPL == 2 || CPL == 4, "two or four candidates per lane");
+            if constexpr (CPL == 4) {
+                order(0, 1);
+                order(2, 3);
+                order(0, 2);
+                order(1, 3);
+                order(1, 2);
+            } else {
+                order(0, 1);
             }
             int mine = 0;  // lane r: the candidate chosen in round r
             for (int r = 0; r < nc; ++r) {
-                double bv_ = -1.0;
-                int bi_ = 0;
-#pragma unroll
-                for (int i = 0; i < CPL; ++i)
-                    if (val[i] > bv_) {
-                        bv_ = val[i];
-                        bi_ = i;
-                    }
-                const double top = wave_max(bv_);
-                const uint64_t hit = __ballot(bv_ == top);
-                const int L = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
-                const int pick = __builtin_amdgcn_readlane(bi_, L);
+                const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
+                const uint32_t mh = wave_max_u32(hi);
+                uint64_t win = __ballot(hi == mh);
+                if (__builtin_popcountll(win) > 1) {  // uniform: the high words tie
+                    const uint32_t ml = wave_max_u32(hi == mh ? lo : 0u);
+                    win = __ballot(hi == mh && lo == ml);
+                }
+                const int L = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(win));
+                const int pick = __builtin_amdgcn_readlane(idx[0], L);
                 const int best = L * CPL + pick;
+                if (lane == L) {
 #pragma unroll
-                for (int i = 0; i < CPL; ++i)
-                    if (lane == L && i == pick) val[i] = -1.0;
+                    for (int i = 0; i + 1 < CPL; ++i) {
+                        key[i] = key[i + 1];
+                        idx[i] = idx[i + 1];
+                    }
+                    key[CPL - 1] = 0ull;
+                }
                 if (lane == r) mine = best;
                 if (lane == 0) lds_chosen[r] = best;
             }
