@@ -92,7 +92,8 @@ def parse_args(argv=None):
     ap.add_argument("--flush-cus", type=int, default=-1,
                     help="multi-layer workloads: run each layer's boundary call on a second stream, on this many "
                          "CUs (lq_config.flush_cus), beside the next layers' decode steps; 0 runs it on the "
-                         "decode stream after the token's last layer; -1 (default) picks 96 of 256 (measured best of 64-160)")
+                         "decode stream after the token's last layer; -1 (default) picks 96 of 256, 128 with the binary16 "
+                         "buffer (measured best of 64-160)")
     ap.add_argument("--load-policy", default="residency", choices=("residency", "auto", "stream", "cached"),
                     help="lq_config.load_policy of the decode steps: streaming (non-temporal) state reads, "
                          "automatic (launches of more than 2,048 units), or ordinary; 'residency' (default) "
@@ -495,7 +496,10 @@ def main(argv=None):
     # (default priority) with its persistent grid limited to part of the CUs
     # while the following layers decode on the rest.
     n_cus_total = torch.cuda.get_device_properties(dev).multi_processor_count
-    flush_cus = args.flush_cus if args.flush_cus >= 0 else min(96, n_cus_total)
+    # measured best grids (sweeps of 64-160 CUs): 96 with the fp32 buffer, 128 with
+    # the binary16 one, whose shorter decode launches leave the boundary less time
+    default_cus = 128 if args.buffer == "fp16" else 96
+    flush_cus = args.flush_cus if args.flush_cus >= 0 else min(default_cus, n_cus_total)
     overlap = L > 1 and 0 < flush_cus
     fstream = torch.cuda.Stream(dev) if overlap else None
     cfg_side = dataclasses.replace(cfg, flush_cus=flush_cus) if overlap else cfg

@@ -955,6 +955,11 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(Fp32DecodeArgs a) {
 #endif
 // the small form with streaming loads (states read from HBM at 1,024 units:
 // 12.1 -> 11.9 us per launch against 6 entries, 12.8 with 4)
+// the large form with the binary16 buffer and streaming loads (hybrid stack:
+// 2.59 -> 2.52 ms per step with the boundary beside the decode)
+#ifndef LQ_RING_GDN_H16_LARGE
+#define LQ_RING_GDN_H16_LARGE 8
+#endif
 #ifndef LQ_RING_GDN_SMALL_STREAM
 #define LQ_RING_GDN_SMALL_STREAM 8
 #endif
@@ -988,7 +993,8 @@ void launch_decode_q8_w(const DecodeArgs& a, int d, int gate_kind, hipStream_t s
     const dim3 grid(a.dm.n_units), block(256);
     if (d == 128) {
         constexpr int PK = H16 ? LQ_RING_KDA_H16 : LQ_RING_KDA;
-        constexpr int PG = H16 ? LQ_RING_GDN_H16 : (!LARGE && STREAM) ? LQ_RING_GDN_SMALL_STREAM : LQ_RING_GDN;
+        constexpr int PG = H16 ? (LARGE ? LQ_RING_GDN_H16_LARGE : LQ_RING_GDN_H16)
+                               : (!LARGE && STREAM) ? LQ_RING_GDN_SMALL_STREAM : LQ_RING_GDN;
         if (gate_kind == LQ_GATE_CHANNEL)
             hipLaunchKernelGGL((decode_q8_kernel<128, true, PK, NWB, FMT, H16, LARGE, STREAM>), grid, block, 0, st, a);
         else
